@@ -1,0 +1,284 @@
+"""Reference oracle for Newton-Schulz orthogonalisation (fp64 CPU).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline use it.  It shares no code with the HIP library.
+
+Every routine follows the written description in
+"Dion3: Full-Stack Orthogonal Updates" (Amsel et al.):
+
+* ``standard_ns``   -- §2.2, Algorithm 1 (standard Newton-Schulz).
+* ``gram_ns``       -- §4, Algorithm 2 (naive Gram Newton-Schulz) and §4.2,
+                       Algorithm 3 (stabilised Gram Newton-Schulz, with the
+                       reformulated quadratic of Appendix B.2.3), with the
+                       restart generalised to any set of iterations
+                       (Appendix B.2: restart every few iterations).
+* ``theorem2_q``    -- §4, Theorem 2 (scalar r/q/z recurrence).
+* ``composed_poly`` -- §2.2: the composed odd polynomial p_T o ... o p_1.
+* ``spectral_map``  -- §2.2: NS acts on the SVD as U (p_T o...o p_1)(S) V^T.
+* ``polar``         -- §2.1, Definition 1: polar(X) = U V^T.
+* ``dion3_rows``    -- §6, Algorithm 4: orthogonalise the selected rows M[S,:]
+                       as one k x m matrix and write them back.
+* ``flops_*``       -- §2.2 and §4.1 FLOP models, §4.2 restart surcharge.
+
+Arithmetic is float64 numpy (BLAS matmul) for float inputs.  For inputs of
+dtype ``object`` holding ``fractions.Fraction`` the very same code runs in
+exact rational arithmetic; the Frobenius norm then must be rational (the
+square root is taken exactly), which is how the tests pin the algebra
+bit-exactly.  The pages run these iterations in half precision; the oracle
+deliberately does not emulate any rounding.
+
+Reading of the pages taken here (each also listed in the design notes):
+* normalisation is X / (||X||_F + eps) with eps = 1e-7 added to the norm;
+* "restart after iteration s" means: before computing Z_{s+1}, replace X by
+  Q_s X, re-form R from it and reset Q to I (X is not renormalised);
+* the coefficient triple of iteration t is (a_t, b_t, c_t) with
+  p_t(x) = a_t x + b_t x^3 + c_t x^5 and h_t(y) = a_t + b_t y + c_t y^2.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import Iterable, Sequence
+
+import numpy as np
+
+EPS = 1e-7
+
+__all__ = [
+    "EPS", "frobenius_normalize", "standard_ns", "gram_ns", "theorem2_q",
+    "composed_poly", "spectral_map", "polar", "dion3_rows", "flops_standard",
+    "flops_gram", "gram_ns_trace",
+]
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+def _is_exact(x: np.ndarray) -> bool:
+    return x.dtype == object
+
+
+def _exact_sqrt(v: Fraction) -> Fraction:
+    """Square root of a non-negative rational that must be a perfect square."""
+    v = Fraction(v)
+    if v < 0:
+        raise ValueError("negative")
+    p, q = v.numerator, v.denominator
+    rp, rq = math.isqrt(p), math.isqrt(q)
+    if rp * rp != p or rq * rq != q:
+        raise ValueError(f"{v} is not the square of a rational")
+    return Fraction(rp, rq)
+
+
+def _eye(n: int, like: np.ndarray) -> np.ndarray:
+    if _is_exact(like):
+        e = np.empty((n, n), dtype=object)
+        for i in range(n):
+            for j in range(n):
+                e[i, j] = Fraction(int(i == j))
+        return e
+    return np.eye(n, dtype=np.float64)
+
+
+def _as_work(X) -> np.ndarray:
+    X = np.asarray(X)
+    if X.dtype == object:
+        return np.vectorize(Fraction, otypes=[object])(X)
+    return X.astype(np.float64)
+
+
+def _coef(c, exact: bool):
+    return Fraction(c) if exact else float(c)
+
+
+def _coeff_list(coeffs, exact: bool):
+    out = []
+    for row in coeffs:
+        a, b, c = row
+        out.append((_coef(a, exact), _coef(b, exact), _coef(c, exact)))
+    if not out:
+        raise ValueError("need at least one iteration")
+    return out
+
+
+# --------------------------------------------------------------------------
+# normalisation (Algorithms 1-3, first step)
+# --------------------------------------------------------------------------
+def frobenius_normalize(X, eps=EPS) -> np.ndarray:
+    """X / (||X||_F + eps): puts every singular value in [0, 1)."""
+    X = _as_work(X)
+    if _is_exact(X):
+        s = sum((v * v for v in X.ravel()), Fraction(0))
+        return X / (_exact_sqrt(s) + Fraction(eps))
+    return X / (np.sqrt(np.sum(X * X)) + eps)
+
+
+# --------------------------------------------------------------------------
+# Algorithm 1: standard Newton-Schulz
+# --------------------------------------------------------------------------
+def standard_ns(X, coeffs, eps=EPS) -> np.ndarray:
+    """Standard Newton-Schulz (Dion3 §2.2, Algorithm 1).
+
+    Each iteration forms the n x n matrix A = X X^T, the quadratic
+    B = b A + c A^2 and updates X <- a X + B X, which maps every singular
+    value x to p_t(x) = a x + b x^3 + c x^5.
+    """
+    X = _as_work(X)
+    n, m = X.shape
+    if n > m:
+        raise ValueError("Algorithm 1 assumes n <= m")
+    exact = _is_exact(X)
+    Y = frobenius_normalize(X, eps)
+    for a, b, c in _coeff_list(coeffs, exact):
+        A = Y @ Y.T
+        B = b * A + c * (A @ A)
+        Y = a * Y + B @ Y
+    return Y
+
+
+# --------------------------------------------------------------------------
+# Algorithms 2 and 3: Gram Newton-Schulz
+# --------------------------------------------------------------------------
+def gram_ns_trace(X, coeffs, restarts: Iterable[int] = (2,),
+                  algebra: str = "stabilized", eps=EPS):
+    """Gram Newton-Schulz, returning the output and every intermediate.
+
+    algebra="stabilized": Dion3 §4.2 Algorithm 3 / Appendix B.2.3.  The
+        quadratic is Z_t = b R + c R^2 and a_t enters each product through
+        an explicit a * (.) term:  Q_t = Q Z + a Q,  RZ = R Z + a R,
+        R_t = Z RZ + a RZ.
+    algebra="naive":      Dion3 §4 Algorithm 2.  Z_t = a I + b R + c R^2,
+        Q_t = Q Z, R_t = Z R Z.
+
+    ``restarts`` holds the iterations s after which the method restarts
+    (Dion3 §4.2; Appendix B.2): at the start of iteration s+1 the input is
+    replaced by Q_s X, R is re-formed as X X^T and Q is reset to I.  The
+    pages' default is a single restart after iteration 2.  An empty set gives
+    the un-restarted iteration.
+
+    Returns (output, trace) where trace is a list of dicts with the values of
+    R, Z, Q after each iteration (and the restarted X when one happens).
+    """
+    X = _as_work(X)
+    n, m = X.shape
+    if n > m:
+        raise ValueError("Gram Newton-Schulz assumes n <= m")
+    exact = _is_exact(X)
+    cl = _coeff_list(coeffs, exact)
+    T = len(cl)
+    rs = sorted(set(int(s) for s in restarts))
+    for s in rs:
+        if not 1 <= s <= T - 1:
+            raise ValueError(f"restart after iteration {s} is outside [1, T-1]")
+    if algebra not in ("stabilized", "naive"):
+        raise ValueError(algebra)
+
+    Y = frobenius_normalize(X, eps)
+    R = Y @ Y.T                      # Gram matrix R_0
+    Q = _eye(n, Y)                   # Q_0 = I
+    trace = []
+    for t in range(1, T + 1):
+        a, b, c = cl[t - 1]
+        step = {"t": t}
+        if (t - 1) in rs:            # restart after iteration t-1
+            Y = Q @ Y
+            R = Y @ Y.T
+            Q = _eye(n, Y)
+            step["restart_X"] = Y
+        if algebra == "stabilized":
+            Z = b * R + c * (R @ R)
+            Q = Q @ Z + a * Q
+            RZ = R @ Z + a * R
+            R = Z @ RZ + a * RZ
+        else:
+            Z = a * _eye(n, Y) + b * R + c * (R @ R)
+            Q = Q @ Z
+            R = Z @ R @ Z
+        step.update(R=R, Z=Z, Q=Q)
+        trace.append(step)
+    return Q @ Y, trace
+
+
+def gram_ns(X, coeffs, restarts: Iterable[int] = (2,),
+            algebra: str = "stabilized", eps=EPS) -> np.ndarray:
+    """Gram Newton-Schulz output Q_T X (see :func:`gram_ns_trace`)."""
+    return gram_ns_trace(X, coeffs, restarts, algebra, eps)[0]
+
+
+# --------------------------------------------------------------------------
+# Theorem 2 and the spectral picture
+# --------------------------------------------------------------------------
+def composed_poly(coeffs, x):
+    """(p_T o ... o p_1)(x) with p_t(x) = a_t x + b_t x^3 + c_t x^5 (§2.2)."""
+    exact = isinstance(x, Fraction) or (isinstance(x, np.ndarray) and x.dtype == object)
+    y = x
+    for a, b, c in _coeff_list(coeffs, exact):
+        y = a * y + b * y ** 3 + c * y ** 5
+    return y
+
+
+def theorem2_q(coeffs, x):
+    """q_T from Theorem 2: r_0 = x^2, q_0 = 1, z_t = h_t(r_{t-1}),
+    r_t = r_{t-1} z_t^2, q_t = q_{t-1} z_t, with h_t(y) = a + b y + c y^2.
+    The theorem states (p_T o ... o p_1)(x) = q_T x."""
+    exact = isinstance(x, Fraction) or (isinstance(x, np.ndarray) and x.dtype == object)
+    r = x * x
+    q = Fraction(1) if exact else 1.0
+    for a, b, c in _coeff_list(coeffs, exact):
+        z = a + b * r + c * r * r
+        r = r * z * z
+        q = q * z
+    return q
+
+
+def spectral_map(X, coeffs, eps=EPS) -> np.ndarray:
+    """U diag(phi(s)) V^T for the thin SVD of X/(||X||_F+eps), phi the
+    composed polynomial: the exact result of T Newton-Schulz steps (§2.2)."""
+    Y = frobenius_normalize(np.asarray(X, dtype=np.float64), eps)
+    U, s, Vt = np.linalg.svd(Y, full_matrices=False)
+    return (U * composed_poly(coeffs, s)) @ Vt
+
+
+def polar(X) -> np.ndarray:
+    """polar(X) = U V^T for the thin SVD X = U S V^T (Dion3 Definition 1)."""
+    U, _, Vt = np.linalg.svd(np.asarray(X, dtype=np.float64), full_matrices=False)
+    return U @ Vt
+
+
+# --------------------------------------------------------------------------
+# Dion3 fractional rows (Algorithm 4, orthogonalisation of M[S,:])
+# --------------------------------------------------------------------------
+def dion3_rows(X, out_init, rows: Sequence[int], coeffs, restarts=(2,),
+               algebra="stabilized", eps=EPS) -> np.ndarray:
+    """Orthogonalise rows ``rows`` of X as one k x m matrix (normalised by its
+    own Frobenius norm) with Gram Newton-Schulz and write the result to the
+    same rows of a copy of ``out_init``; all other rows are left as given."""
+    X = np.asarray(X)
+    rows = [int(r) for r in rows]
+    if len(set(rows)) != len(rows):
+        raise ValueError("row indices must be distinct")
+    out = np.array(out_init, dtype=np.float64, copy=True)
+    out[rows, :] = gram_ns(X[rows, :], coeffs, restarts, algebra, eps)
+    return out
+
+
+# --------------------------------------------------------------------------
+# FLOP models (2 FLOPs per multiply-add)
+# --------------------------------------------------------------------------
+def flops_standard(n: int, m: int, T: int, symmetric: bool) -> float:
+    """Standard NS: per iteration X X^T (2mn^2), A^2 (2n^3), B X (2mn^2)
+    (§2.2); the symmetric kernels halve the two symmetric products (§2.3)."""
+    if symmetric:
+        return T * (3.0 * m * n * n + n ** 3)
+    return T * (4.0 * m * n * n + 2.0 * n ** 3)
+
+
+def flops_gram(n: int, m: int, T: int, n_restarts: int) -> float:
+    """Gram NS with symmetric kernels (§4.1): four n^3 products per iteration,
+    mn^2 for the Gram matrix, 2mn^2 for the final Q X, minus the free Q_1 and
+    the skipped R_T (3n^3); each restart adds Q X (2mn^2) and a Gram matrix
+    (mn^2) and again makes one Q update free and one R update skippable
+    (3n^3), i.e. +3(alpha-1) n^3 (§4.2)."""
+    base = T * 4.0 * n ** 3 + 3.0 * m * n * n - 3.0 * n ** 3
+    return base + n_restarts * (3.0 * m * n * n - 3.0 * n ** 3)
