@@ -1,0 +1,240 @@
+"""ctypes binding of libgns.so (the C ABI in include/gns.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the stream.
+The binding fails loudly when the library has not been built; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgns.so")
+
+GNS_F32, GNS_BF16, GNS_F16 = 0, 1, 2
+GNS_OPT_NAIVE_ALGEBRA = 0x1
+GNS_OPT_TILE_128 = 0x10
+GNS_OPT_TILE_256 = 0x20
+MAX_ITERS = 64
+
+_DT = {torch.float32: GNS_F32, torch.bfloat16: GNS_BF16, torch.float16: GNS_F16}
+_STATUS = {
+    0: "GNS_OK", 1: "GNS_E_NULL", 2: "GNS_E_SHAPE", 3: "GNS_E_DTYPE", 4: "GNS_E_COEFF",
+    5: "GNS_E_RESTART", 6: "GNS_E_ROWIDX", 7: "GNS_E_ALIAS", 8: "GNS_E_WORKSPACE",
+    9: "GNS_E_HIP", 10: "GNS_E_FLAGS",
+}
+
+#: every symbol include/gns.h declares
+EXPORTS = [
+    "gns_abi_version", "gns_status_str", "gns_gram_workspace_bytes",
+    "gns_standard_workspace_bytes", "gns_gram_batched", "gns_standard_batched",
+    "gns_check_row_idx", "gns_timing_enable", "gns_timing_read", "gns_timing_reset",
+]
+
+
+class GnsError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+        self.name = _STATUS.get(code, str(code))
+
+
+class LaunchRecord(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("kernel", ctypes.c_char_p), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("ms", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgns.so (raises if it is missing: build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m gram_newton_schulz_amd.build or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.gns_abi_version.restype = ctypes.c_int
+    L.gns_status_str.restype = ctypes.c_char_p
+    L.gns_status_str.argtypes = [ctypes.c_int]
+    for f in (L.gns_gram_workspace_bytes, L.gns_standard_workspace_bytes):
+        f.restype = sz
+        f.argtypes = [ctypes.c_int, i64, i64, i64]
+    L.gns_gram_batched.restype = ctypes.c_int
+    L.gns_gram_batched.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                   vp, i64, ctypes.c_uint, vp, sz, vp]
+    L.gns_standard_batched.restype = ctypes.c_int
+    L.gns_standard_batched.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_double), ctypes.c_int,
+                                       vp, i64, ctypes.c_uint, vp, sz, vp]
+    L.gns_check_row_idx.restype = ctypes.c_int
+    L.gns_check_row_idx.argtypes = [vp, i64, i64, i64, vp, vp]
+    L.gns_timing_enable.argtypes = [ctypes.c_int]
+    L.gns_timing_enable.restype = None
+    L.gns_timing_reset.restype = None
+    L.gns_timing_read.restype = ctypes.c_int
+    L.gns_timing_read.argtypes = [ctypes.POINTER(LaunchRecord), ctypes.c_int]
+    _lib = L
+    return L
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise GnsError(code, lib().gns_status_str(code).decode())
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    if dt not in _DT:
+        raise GnsError(3, f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+def _coeff_array(coeffs) -> "ctypes.Array":
+    flat = []
+    for row in coeffs:
+        a, b, c = row
+        flat += [float(a), float(b), float(c)]
+    return (ctypes.c_double * max(len(flat), 1))(*flat), len(flat) // 3
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gram_workspace_bytes(compute_dtype, batch: int, rows: int, m: int) -> int:
+    return int(lib().gns_gram_workspace_bytes(_dtype_code(compute_dtype), batch, rows, m))
+
+
+def standard_workspace_bytes(compute_dtype, batch: int, rows: int, m: int) -> int:
+    return int(lib().gns_standard_workspace_bytes(_dtype_code(compute_dtype), batch, rows, m))
+
+
+def _tile_opts(tile: Optional[int]) -> int:
+    if tile is None:
+        return 0
+    if tile == 128:
+        return GNS_OPT_TILE_128
+    if tile == 256:
+        return GNS_OPT_TILE_256
+    raise GnsError(10, f"tile must be 128 or 256, got {tile}")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] = (2,), *,
+                    row_idx: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    compute_dtype=None, naive_algebra: bool = False, tile: Optional[int] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gram Newton-Schulz of every matrix in X ([batch, n, m] or [n, m]) via
+    gns_gram_batched.  ``row_idx`` ([batch, k] int64, device) selects the
+    rows to orthogonalise; the other rows of ``out`` are left as they are
+    (``out`` defaults to a copy of X in that case)."""
+    squeeze = X.dim() == 2
+    Xb = X.unsqueeze(0) if squeeze else X
+    if Xb.dim() != 3 or not Xb.is_contiguous():
+        raise GnsError(2, "X must be a contiguous [batch, n, m] tensor")
+    B, n, m = Xb.shape
+    cdt = _dtype_code(Xb.dtype if compute_dtype is None else compute_dtype)
+    k = 0
+    if row_idx is not None:
+        ri = row_idx.unsqueeze(0) if row_idx.dim() == 1 else row_idx
+        if ri.dtype != torch.int64 or not ri.is_contiguous() or ri.shape[0] != B:
+            raise GnsError(6, "row_idx must be a contiguous int64 [batch, k] tensor")
+        k = ri.shape[1]
+        row_idx = ri
+    if out is None:
+        out = Xb.clone() if row_idx is not None else torch.empty_like(Xb)
+    elif squeeze:
+        out = out.unsqueeze(0)
+    rows = k if row_idx is not None else n
+    ws = _workspace(gram_workspace_bytes(cdt, B, rows, m), Xb.device, workspace)
+    carr, T = _coeff_array(coeffs)
+    rs = list(restarts)
+    rarr = (ctypes.c_int * max(len(rs), 1))(*rs)
+    _check(lib().gns_gram_batched(
+        _ptr(Xb), _ptr(out), B, n, m, _dtype_code(Xb.dtype), cdt, carr, T, rarr, len(rs),
+        _ptr(row_idx), k, (GNS_OPT_NAIVE_ALGEBRA if naive_algebra else 0) | _tile_opts(tile),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out.squeeze(0) if squeeze else out
+
+
+def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
+                        row_idx: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, compute_dtype=None,
+                        tile: Optional[int] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Standard Newton-Schulz (Algorithm 1) via gns_standard_batched."""
+    squeeze = X.dim() == 2
+    Xb = X.unsqueeze(0) if squeeze else X
+    if Xb.dim() != 3 or not Xb.is_contiguous():
+        raise GnsError(2, "X must be a contiguous [batch, n, m] tensor")
+    B, n, m = Xb.shape
+    cdt = _dtype_code(Xb.dtype if compute_dtype is None else compute_dtype)
+    k = 0
+    if row_idx is not None:
+        ri = row_idx.unsqueeze(0) if row_idx.dim() == 1 else row_idx
+        if ri.dtype != torch.int64 or not ri.is_contiguous() or ri.shape[0] != B:
+            raise GnsError(6, "row_idx must be a contiguous int64 [batch, k] tensor")
+        k = ri.shape[1]
+        row_idx = ri
+    if out is None:
+        out = Xb.clone() if row_idx is not None else torch.empty_like(Xb)
+    elif squeeze:
+        out = out.unsqueeze(0)
+    rows = k if row_idx is not None else n
+    ws = _workspace(standard_workspace_bytes(cdt, B, rows, m), Xb.device, workspace)
+    carr, T = _coeff_array(coeffs)
+    _check(lib().gns_standard_batched(
+        _ptr(Xb), _ptr(out), B, n, m, _dtype_code(Xb.dtype), cdt, carr, T,
+        _ptr(row_idx), k, _tile_opts(tile), _ptr(ws), ws.numel(), _stream(stream)))
+    return out.squeeze(0) if squeeze else out
+
+
+def check_row_idx(row_idx: torch.Tensor, n: int, stream=None) -> int:
+    """0 = valid, 1 = index out of range, 2 = repeated index (synchronises)."""
+    ri = row_idx.unsqueeze(0) if row_idx.dim() == 1 else row_idx
+    res = torch.empty(1, dtype=torch.int32, device=ri.device)
+    _check(lib().gns_check_row_idx(_ptr(ri), ri.shape[0], ri.shape[1], n, _ptr(res), _stream(stream)))
+    return int(res.item())
+
+
+def timing_enable(on: bool = True) -> None:
+    lib().gns_timing_enable(1 if on else 0)
+
+
+def timing_reset() -> None:
+    lib().gns_timing_reset()
+
+
+def timing_read():
+    """List of (name, kernel, flops, bytes, ms) for every timed launch since the last reset."""
+    L = lib()
+    n = L.gns_timing_read(None, 0)
+    recs = (LaunchRecord * max(n, 1))()
+    n = L.gns_timing_read(recs, n)
+    return [(r.name.decode(), r.kernel.decode(), r.flops, r.bytes, r.ms) for r in recs[:n]]

@@ -1,0 +1,513 @@
+// Host side of the C ABI declared in include/gns.h: argument validation,
+// workspace carving and the launch sequence of Gram Newton-Schulz
+// ("Dion3: Full-Stack Orthogonal Updates", §4.2 Algorithm 3, with the
+// Algorithm 2 algebra as an option) and of standard Newton-Schulz (§2.2,
+// Algorithm 1).  Everything is enqueued on the caller's stream; nothing
+// allocates, nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/gns.h"
+#include "gns_kernels.h"
+
+namespace {
+
+using gns::GemmParams;
+
+constexpr double kEps = 1e-7;  // added to the Frobenius norm (Algorithms 1-3)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+bool valid_dtype(int dt) { return dt == GNS_F32 || dt == GNS_BF16 || dt == GNS_F16; }
+
+// --------------------------------------------------------------------------
+// problem plan: tile edge, padded sizes, workspace layout
+// --------------------------------------------------------------------------
+struct Plan {
+  int tile = 128;
+  int64_t rows = 0, m = 0, Np = 0, Mp = 0;
+  int parts = 1;
+  int esz = 2;
+  size_t off_partials = 0, off_xh = 0, off_xt0 = 0, off_xt1 = 0;
+  size_t off_sq[5] = {0, 0, 0, 0, 0};  // R, Z, RZ, Q0, Q1 (standard NS: A, B)
+  size_t bytes = 0;
+};
+
+int choose_tile(int cdt, int64_t batch, int64_t rows) {
+  if (cdt == GNS_F32) return 128;
+  // 256-edge tiles halve operand traffic per FLOP; use them when the
+  // symmetric products still give every CU a couple of workgroups.
+  const int64_t t256 = (rows + 255) / 256;
+  const int64_t work = t256 * (t256 + 1) / 2 * batch;
+  return work >= 512 ? 256 : 128;
+}
+
+int choose_parts(int64_t batch, int64_t rows) {
+  int64_t p = (2048 + batch - 1) / std::max<int64_t>(batch, 1);
+  p = std::min<int64_t>(p, 1024);
+  p = std::min<int64_t>(p, rows);
+  return static_cast<int>(std::max<int64_t>(p, 1));
+}
+
+// tile_request: 0 = choose, else 128 or 256.  Workspace sizes are quoted
+// for 256-padded buffers so that any tile choice fits.
+bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, int tile_request,
+               Plan *pl) {
+  if (!valid_dtype(cdt) || batch < 0 || rows < 1 || m < rows) return false;
+  pl->tile = tile_request ? tile_request : choose_tile(cdt, batch, rows);
+  pl->rows = rows;
+  pl->m = m;
+  pl->Np = round_up(rows, pl->tile);
+  pl->Mp = round_up(m, pl->tile);
+  // per-matrix element offsets stay within int range of the kernels' math
+  if (pl->Np * pl->Mp > (int64_t(1) << 31)) return false;
+  pl->parts = choose_parts(batch, rows);
+  pl->esz = gns::dtype_size(cdt);
+  size_t off = 0;
+  pl->off_partials = off;
+  off = align_up(off + sizeof(double) * batch * pl->parts, kAlign);
+  const size_t rect = static_cast<size_t>(batch) * pl->Np * pl->Mp * pl->esz;
+  const size_t sq = static_cast<size_t>(batch) * pl->Np * pl->Np * pl->esz;
+  pl->off_xh = off;
+  off = align_up(off + rect, kAlign);
+  pl->off_xt0 = off;
+  off = align_up(off + rect, kAlign);
+  pl->off_xt1 = off;
+  off = align_up(off + rect, kAlign);
+  for (int i = 0; i < n_square; ++i) {
+    pl->off_sq[i] = off;
+    off = align_up(off + sq, kAlign);
+  }
+  pl->bytes = off;
+  return true;
+}
+
+// --------------------------------------------------------------------------
+// optional per-launch timing (benchmarking aid)
+// --------------------------------------------------------------------------
+struct TimedLaunch {
+  const char *name;
+  const char *kernel;
+  double flops, bytes;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct LaunchScope {
+  hipStream_t s;
+  TimedLaunch rec{};
+  bool on = false;
+  LaunchScope(hipStream_t st, const char *name, const char *kernel, double flops, double bytes)
+      : s(st) {
+    if (!g_timing) return;
+    rec = TimedLaunch{name, kernel, flops, bytes, pooled_event(), pooled_event()};
+    if (rec.start && rec.stop && hipEventRecord(rec.start, s) == hipSuccess) on = true;
+  }
+  void done() {
+    if (!on) return;
+    if (hipEventRecord(rec.stop, s) == hipSuccess) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      g_launches.push_back(rec);
+    }
+  }
+};
+
+// --------------------------------------------------------------------------
+// launch helpers
+// --------------------------------------------------------------------------
+struct Ctx {
+  const Plan *pl;
+  int cdt;
+  int64_t batch;
+  unsigned char *ws;
+  hipStream_t s;
+  void *sq(int i) const { return ws + pl->off_sq[i]; }
+  int64_t sq_stride() const { return pl->Np * pl->Np; }
+  int64_t rect_stride() const { return pl->Np * pl->Mp; }
+};
+
+GemmParams base_params(const Ctx &c) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.batch = static_cast<int>(c.batch);
+  p.alpha = 1.0f;
+  p.n_real = static_cast<int>(c.pl->rows);
+  return p;
+}
+
+// C = alpha * A B + beta * D for n x n iterates (B symmetric), mirrored.
+gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float beta, const void *D,
+                void *C, void *C2, float diag1, float diag2, const char *what, double flops) {
+  GemmParams p = base_params(c);
+  const int64_t N = c.pl->Np;
+  const int nt = static_cast<int>(N / c.pl->tile);
+  p.A = A; p.lda = N; p.sA = c.sq_stride();
+  p.B = B; p.ldb = N; p.sB = c.sq_stride();
+  p.K = static_cast<int>(N);
+  p.tiles_m = p.tiles_n = nt;
+  p.tiles_per_mat = nt * (nt + 1) / 2;
+  p.alpha = alpha; p.beta = beta;
+  p.D = D; p.ldd = N; p.sD = c.sq_stride();
+  p.C = C; p.ldc = N; p.sC = c.sq_stride();
+  p.C2 = C2; p.sC2 = c.sq_stride();
+  p.diag1 = diag1; p.diag2 = diag2;
+  const double n = static_cast<double>(c.pl->rows);
+  const double bytes = c.batch * n * n * c.pl->esz * (3.0 + (D ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
+  LaunchScope ls(c.s, what, gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), flops * c.batch,
+                 bytes);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, gns::MODE_SYM, p, c.s);
+  ls.done();
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+// R = X X^T from the row-layout buffer.
+gns_status syrk(const Ctx &c, void *R) {
+  GemmParams p = base_params(c);
+  const int64_t N = c.pl->Np, M = c.pl->Mp;
+  const int nt = static_cast<int>(N / c.pl->tile);
+  const void *Xh = c.ws + c.pl->off_xh;
+  p.A = Xh; p.lda = M; p.sA = c.rect_stride();
+  p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
+  p.K = static_cast<int>(M);
+  p.tiles_m = p.tiles_n = nt;
+  p.tiles_per_mat = nt * (nt + 1) / 2;
+  p.C = R; p.ldc = N; p.sC = c.sq_stride();
+  const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
+  LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), n * n * m * c.batch,
+                 c.batch * (n * m + n * n) * c.pl->esz);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, gns::MODE_SYM, p, c.s);
+  ls.done();
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+// Y = S X (+ beta * X) with S an n x n iterate and X read through its
+// transposed copy XT_in.  Either writes the row layout in place plus the
+// transposed copy XT_out, or (final) the caller's output.
+gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, float beta,
+                 bool final, void *out, int io_dtype, int64_t n_total, const int64_t *row_idx,
+                 const char *what) {
+  GemmParams p = base_params(c);
+  const int64_t N = c.pl->Np, M = c.pl->Mp;
+  const int tm = static_cast<int>(N / c.pl->tile), tn = static_cast<int>(M / c.pl->tile);
+  void *Xh = c.ws + c.pl->off_xh;
+  p.A = S; p.lda = N; p.sA = c.sq_stride();
+  p.B = XT_in; p.ldb = N; p.sB = c.rect_stride();
+  p.K = static_cast<int>(N);
+  p.tiles_m = tm; p.tiles_n = tn;
+  p.tiles_per_mat = tm * tn;
+  p.beta = beta;
+  if (beta != 0.0f) { p.D = Xh; p.ldd = M; p.sD = c.rect_stride(); }
+  const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
+  double bytes = c.batch * (n * n + n * m) * c.pl->esz;
+  if (final) {
+    p.out = out; p.out_dtype = io_dtype; p.out_rows = n_total; p.out_cols = c.pl->m;
+    p.rows_eff = c.pl->rows; p.row_idx = row_idx;
+    bytes += c.batch * n * m * gns::dtype_size(io_dtype);
+  } else {
+    p.C = Xh; p.ldc = M; p.sC = c.rect_stride();
+    p.CT = XT_out; p.ldct = N; p.sCT = c.rect_stride();
+    bytes += 2.0 * c.batch * n * m * c.pl->esz;
+  }
+  if (beta != 0.0f) bytes += c.batch * n * m * c.pl->esz;
+  LaunchScope ls(c.s, what,
+                 gns::gemm_kernel_name(c.cdt, c.pl->tile, final ? gns::MODE_FINAL : gns::MODE_GEN),
+                 2.0 * n * n * m * c.batch, bytes);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, final ? gns::MODE_FINAL : gns::MODE_GEN, p, c.s);
+  ls.done();
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+// Norm + scale + cast + transpose of the (row-selected) input.
+gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const int64_t *row_idx) {
+  double *partials = reinterpret_cast<double *>(c.ws + c.pl->off_partials);
+  const double rows = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
+  {
+    LaunchScope ls(c.s, "norm_partial", "norm_partial", 2.0 * rows * m * c.batch,
+                   c.batch * rows * m * gns::dtype_size(io));
+    hipError_t e = gns::launch_norm_partial(io, X, c.batch, n_total, c.pl->m, c.pl->rows, row_idx,
+                                            c.pl->parts, partials, c.s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  {
+    LaunchScope ls(c.s, "scale_transpose", "scale_transpose", rows * m * c.batch,
+                   c.batch * rows * m * (gns::dtype_size(io) + 2.0 * c.pl->esz));
+    hipError_t e = gns::launch_scale_transpose(io, c.cdt, X, c.batch, n_total, c.pl->m, c.pl->rows,
+                                               row_idx, partials, c.pl->parts, kEps,
+                                               c.ws + c.pl->off_xh, c.ws + c.pl->off_xt0,
+                                               c.pl->Np, c.pl->Mp, c.s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  return GNS_OK;
+}
+
+gns_status parse_opts(unsigned opts, unsigned allowed, int *tile) {
+  allowed |= GNS_OPT_TILE_128 | GNS_OPT_TILE_256;
+  if (opts & ~allowed) return GNS_E_FLAGS;
+  if ((opts & GNS_OPT_TILE_128) && (opts & GNS_OPT_TILE_256)) return GNS_E_FLAGS;
+  *tile = (opts & GNS_OPT_TILE_128) ? 128 : (opts & GNS_OPT_TILE_256) ? 256 : 0;
+  return GNS_OK;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+gns_status common_checks(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                         gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
+                         const int64_t *row_idx, int64_t k, int64_t *rows) {
+  if (!valid_dtype(io) || !valid_dtype(cdt)) return GNS_E_DTYPE;
+  if (batch < 0 || n < 1 || m < 1) return GNS_E_SHAPE;
+  if (row_idx) {
+    if (k < 1 || k > n) return GNS_E_SHAPE;
+    *rows = k;
+  } else {
+    *rows = n;
+  }
+  if (*rows > m) return GNS_E_SHAPE;
+  if (!coeffs) return GNS_E_NULL;
+  if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
+  for (int i = 0; i < 3 * T; ++i)
+    if (!std::isfinite(coeffs[i])) return GNS_E_COEFF;
+  if (batch > 0 && (!X || !out)) return GNS_E_NULL;
+  if (batch > (int64_t(1) << 24)) return GNS_E_SHAPE;
+  return GNS_OK;
+}
+
+gns_status workspace_checks(const void *X, const void *out, int64_t batch, int64_t n, int64_t m,
+                            gns_dtype io, const Plan &pl, void *ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < pl.bytes || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return GNS_E_WORKSPACE;
+  const size_t io_bytes = static_cast<size_t>(batch) * n * m * gns::dtype_size(io);
+  if (ranges_overlap(ws, pl.bytes, X, io_bytes) || ranges_overlap(ws, pl.bytes, out, io_bytes))
+    return GNS_E_ALIAS;
+  return GNS_OK;
+}
+
+}  // namespace
+
+// ==========================================================================
+// exported ABI
+// ==========================================================================
+extern "C" {
+
+int gns_abi_version(void) { return GNS_ABI_VERSION; }
+
+const char *gns_status_str(gns_status s) {
+  switch (s) {
+    case GNS_OK: return "ok";
+    case GNS_E_NULL: return "required pointer is NULL";
+    case GNS_E_SHAPE: return "invalid shape";
+    case GNS_E_DTYPE: return "unsupported dtype";
+    case GNS_E_COEFF: return "invalid iteration count or coefficient";
+    case GNS_E_RESTART: return "restart iterations must be strictly increasing in [1, T-1]";
+    case GNS_E_ROWIDX: return "row index out of range or repeated";
+    case GNS_E_ALIAS: return "workspace overlaps X or out";
+    case GNS_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GNS_E_HIP: return "HIP launch failed";
+    case GNS_E_FLAGS: return "unknown option bits";
+  }
+  return "unknown status";
+}
+
+size_t gns_gram_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t rows, int64_t m) {
+  Plan pl;
+  if (batch <= 0 || !make_plan(cdt, batch, rows, m, 5, 256, &pl)) return 0;
+  return pl.bytes;
+}
+
+size_t gns_standard_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t rows, int64_t m) {
+  Plan pl;
+  if (batch <= 0 || !make_plan(cdt, batch, rows, m, 2, 256, &pl)) return 0;
+  return pl.bytes;
+}
+
+gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                            gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
+                            const int *restart_after, int n_restart, const int64_t *row_idx,
+                            int64_t k, unsigned opts, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  int64_t rows = 0;
+  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
+  if (st != GNS_OK) return st;
+  int tile_req = 0;
+  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA, &tile_req)) != GNS_OK) return st;
+  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
+  std::vector<char> restart_at(T + 2, 0);
+  for (int i = 0; i < n_restart; ++i) {
+    const int r = restart_after[i];
+    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
+    restart_at[r] = 1;
+  }
+  if (batch == 0) return GNS_OK;
+  Plan pl;
+  if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;
+  st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
+  if (st != GNS_OK) return st;
+
+  const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
+  Ctx c{&pl, static_cast<int>(cdt), batch, static_cast<unsigned char *>(workspace),
+        static_cast<hipStream_t>(stream)};
+  void *R = c.sq(0), *Z = c.sq(1), *RZ = c.sq(2);
+  void *Qb[2] = {c.sq(3), c.sq(4)};
+  void *XT[2] = {c.ws + pl.off_xt0, c.ws + pl.off_xt1};
+  int qcur = 0, xcur = 0;
+  bool q_is_identity = true;
+  const double nn = static_cast<double>(rows);
+  const double n3 = nn * nn * nn;
+
+  if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
+  if ((st = syrk(c, R)) != GNS_OK) return st;                        // R_0 = X X^T
+  for (int t = 1; t <= T; ++t) {
+    const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);
+    const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
+    const float cc = static_cast<float>(coeffs[3 * (t - 1) + 2]);
+    if (t > 1 && restart_at[t - 1]) {
+      // restart: X <- Q X (row layout in place, transposed copy swapped),
+      // R <- X X^T, Q <- I
+      st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], 0.0f, false, nullptr, io, n, nullptr, "restart_apply");
+      if (st != GNS_OK) return st;
+      xcur ^= 1;
+      if ((st = syrk(c, R)) != GNS_OK) return st;
+      q_is_identity = true;
+    }
+    const bool need_r = (t < T) && !restart_at[t];
+    if (!naive) {
+      // Z = b R + c R^2; with Q = I the Q update is Z + a I, written by the
+      // same kernel as a second output
+      if (q_is_identity) {
+        st = symm(c, R, R, cc, b, R, Z, Qb[qcur], 0.0f, a, "poly_q", n3);
+        q_is_identity = false;
+      } else {
+        st = symm(c, R, R, cc, b, R, Z, nullptr, 0.0f, 0.0f, "poly", n3);
+        if (st == GNS_OK) {
+          st = symm(c, Qb[qcur], Z, 1.0f, a, Qb[qcur], Qb[qcur ^ 1], nullptr, 0.0f, 0.0f, "q_update", n3);
+          qcur ^= 1;
+        }
+      }
+      if (st != GNS_OK) return st;
+      if (need_r) {
+        if ((st = symm(c, R, Z, 1.0f, a, R, RZ, nullptr, 0.0f, 0.0f, "rz", n3)) != GNS_OK) return st;
+        if ((st = symm(c, Z, RZ, 1.0f, a, RZ, R, nullptr, 0.0f, 0.0f, "r_update", n3)) != GNS_OK) return st;
+      }
+    } else {
+      // Algorithm 2 algebra: Z = a I + b R + c R^2, Q <- Q Z, R <- Z R Z
+      if (q_is_identity) {
+        st = symm(c, R, R, cc, b, R, Z, Qb[qcur], a, a, "poly_q", n3);
+        q_is_identity = false;
+      } else {
+        st = symm(c, R, R, cc, b, R, Z, nullptr, a, 0.0f, "poly", n3);
+        if (st == GNS_OK) {
+          st = symm(c, Qb[qcur], Z, 1.0f, 0.0f, nullptr, Qb[qcur ^ 1], nullptr, 0.0f, 0.0f, "q_update", n3);
+          qcur ^= 1;
+        }
+      }
+      if (st != GNS_OK) return st;
+      if (need_r) {
+        if ((st = symm(c, R, Z, 1.0f, 0.0f, nullptr, RZ, nullptr, 0.0f, 0.0f, "rz", n3)) != GNS_OK) return st;
+        if ((st = symm(c, Z, RZ, 1.0f, 0.0f, nullptr, R, nullptr, 0.0f, 0.0f, "r_update", n3)) != GNS_OK) return st;
+      }
+    }
+  }
+  // out = Q_T X
+  return apply(c, Qb[qcur], XT[xcur], nullptr, 0.0f, true, out, io, n, row_idx, "final_apply");
+}
+
+gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                                gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
+                                const int64_t *row_idx, int64_t k, unsigned opts, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  int64_t rows = 0;
+  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
+  if (st != GNS_OK) return st;
+  int tile_req = 0;
+  if ((st = parse_opts(opts, 0u, &tile_req)) != GNS_OK) return st;
+  if (batch == 0) return GNS_OK;
+  Plan pl;
+  if (!make_plan(cdt, batch, rows, m, 2, tile_req, &pl)) return GNS_E_SHAPE;
+  st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
+  if (st != GNS_OK) return st;
+  Ctx c{&pl, static_cast<int>(cdt), batch, static_cast<unsigned char *>(workspace),
+        static_cast<hipStream_t>(stream)};
+  void *A = c.sq(0), *B = c.sq(1);
+  void *XT[2] = {c.ws + pl.off_xt0, c.ws + pl.off_xt1};
+  int xcur = 0;
+  const double nn = static_cast<double>(rows);
+  if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
+  for (int t = 1; t <= T; ++t) {
+    const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);
+    const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
+    const float cc = static_cast<float>(coeffs[3 * (t - 1) + 2]);
+    if ((st = syrk(c, A)) != GNS_OK) return st;                                   // A = X X^T
+    st = symm(c, A, A, cc, b, A, B, nullptr, 0.0f, 0.0f, "std_poly", nn * nn * nn);  // B = bA + cA^2
+    if (st != GNS_OK) return st;
+    if (t < T) {
+      st = apply(c, B, XT[xcur], XT[xcur ^ 1], a, false, nullptr, io, n, nullptr, "std_apply");
+      xcur ^= 1;
+    } else {
+      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, n, row_idx, "std_final_apply");
+    }
+    if (st != GNS_OK) return st;
+  }
+  return GNS_OK;
+}
+
+gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
+                             int32_t *result, void *stream) {
+  if (!row_idx || !result) return GNS_E_NULL;
+  if (batch < 0 || k < 1 || n < 1 || k > n || n > 65536) return GNS_E_SHAPE;
+  if (batch == 0) return GNS_OK;
+  hipError_t e = gns::launch_check_rows(row_idx, batch, k, n, result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+void gns_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+}
+
+void gns_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto &l : g_launches) {
+    g_event_pool.push_back(l.start);
+    g_event_pool.push_back(l.stop);
+  }
+  g_launches.clear();
+}
+
+int gns_timing_read(gns_launch_record *records, int cap) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  const int n = static_cast<int>(g_launches.size());
+  for (int i = 0; i < n && i < cap && records; ++i) {
+    const TimedLaunch &l = g_launches[i];
+    float ms = -1.0f;
+    if (hipEventSynchronize(l.stop) == hipSuccess && hipEventElapsedTime(&ms, l.start, l.stop) != hipSuccess)
+      ms = -1.0f;
+    records[i] = gns_launch_record{l.name, l.kernel, l.flops, l.bytes, ms};
+  }
+  return n;
+}
+
+}  // extern "C"

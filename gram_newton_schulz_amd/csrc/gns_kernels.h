@@ -1,0 +1,67 @@
+// Internal interface between the host orchestration (gns_host.cpp) and the
+// device kernels (gns_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gns {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// Epilogue of the NT product kernel.
+enum GemmMode : int {
+  MODE_SYM = 0,   // symmetric result: upper tiles computed, mirrored, diagonal
+                  // tiles symmetrised so that the stored matrix is exactly
+                  // symmetric; optional second output C2 = C + diag2 * I
+  MODE_GEN = 1,   // general result in row layout, optional transposed copy
+  MODE_FINAL = 2  // general result converted into the caller's output
+};
+
+// C = alpha * (A . B^T) + beta * D over a batch, A and B row-major with the
+// contraction index contiguous.  All internal buffers are padded to whole
+// tiles and zero-filled there, so the kernel needs no bounds checks except
+// for the caller's output in MODE_FINAL.
+struct GemmParams {
+  const void *A; int64_t lda, sA;   // leading dim and batch stride (elements)
+  const void *B; int64_t ldb, sB;
+  int K;                            // contraction length, multiple of 128 bytes
+  int tiles_m, tiles_n;             // output tiles per matrix along rows / cols
+  int tiles_per_mat;                // sym: tiles_m*(tiles_m+1)/2
+  int batch;
+  float alpha, beta;
+  const void *D; int64_t ldd, sD;   // beta term (same layout as C); may be null
+  void *C; int64_t ldc, sC;
+  void *C2; int64_t sC2;            // MODE_SYM second output (ld = ldc); may be null
+  float diag1, diag2;               // MODE_SYM: added to C / C2 on the diagonal
+  int n_real;                       // diagonal entries i < n_real get diag1/diag2
+  void *CT; int64_t ldct, sCT;      // MODE_GEN transposed copy; may be null
+  // MODE_FINAL
+  void *out; int out_dtype;
+  int64_t out_rows;                 // rows of each caller matrix (n)
+  int64_t out_cols;                 // m
+  int64_t rows_eff;                 // rows actually computed (n or k)
+  const int64_t *row_idx;           // [batch][rows_eff] or null
+};
+
+// Launchers (return hipGetLastError() after the launch).
+hipError_t launch_gemm(int compute_dtype, int tile, int mode, const GemmParams &p,
+                       hipStream_t s);
+const char *gemm_kernel_name(int compute_dtype, int tile, int mode);
+
+hipError_t launch_norm_partial(int io_dtype, const void *X, int64_t batch, int64_t n,
+                               int64_t m, int64_t rows_eff, const int64_t *row_idx,
+                               int parts, double *partials, hipStream_t s);
+
+hipError_t launch_scale_transpose(int io_dtype, int compute_dtype, const void *X,
+                                  int64_t batch, int64_t n, int64_t m, int64_t rows_eff,
+                                  const int64_t *row_idx, const double *partials,
+                                  int parts, double eps, void *Xh, void *XT, int64_t Np,
+                                  int64_t Mp, hipStream_t s);
+
+hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
+                             int32_t *result, hipStream_t s);
+
+}  // namespace gns

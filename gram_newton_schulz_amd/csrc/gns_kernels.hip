@@ -1,0 +1,589 @@
+// Device kernels of the Gram Newton-Schulz library, written for CDNA4 (gfx950).
+//
+// * norm_partial     -- Frobenius norm, first stage: per-workgroup sums of
+//                       squares in fixed order (HBM-bound, vector loads).
+// * scale_transpose  -- X_hat = X / (||X||_F + eps) rounded once to the
+//                       compute dtype, written both row-major [n][m] and
+//                       transposed [m][n] (zero padded to whole tiles); the
+//                       second stage of the norm reduction runs in its prologue.
+// * gemm_nt          -- C = alpha * A B^T + beta * D on bf16/fp16 (32x32x16)
+//                       or fp32 (32x32x2) MFMA with fp32 accumulation.  A
+//                       256x256 (or 128x128) workgroup tile, four waves in a
+//                       2x2 grid, 64-element (128-byte) K steps staged through
+//                       double-buffered, XOR-swizzled LDS.  Symmetric results
+//                       compute only the upper tiles and mirror them ("Dion3:
+//                       Full-Stack Orthogonal Updates", §5 and App. C.1-C.2).
+//
+// Every product of the method is written as A B^T with both operands stored
+// row-major along the contraction index: X X^T directly; products of two
+// n x n iterates because every stored iterate is exactly symmetric (so its
+// rows are its columns); Q X through the transposed copy of X kept beside it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gns_kernels.h"
+
+namespace gns {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// element types
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+struct EBF16 {
+  using S = uint16_t;
+  static constexpr int code = DT_BF16;
+  __device__ static float ld(S v) { return bf16_to_f32(v); }
+  __device__ static S st(float f) { return f32_to_bf16(f); }
+};
+struct EF16 {
+  using S = uint16_t;
+  static constexpr int code = DT_F16;
+  __device__ static float ld(S v) { return f16_to_f32(v); }
+  __device__ static S st(float f) { return f32_to_f16(f); }
+};
+struct EF32 {
+  using S = float;
+  static constexpr int code = DT_F32;
+  __device__ static float ld(S v) { return v; }
+  __device__ static S st(float f) { return f; }
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One lane's share of a 16-deep slice of the contraction: 8 consecutive
+// elements (one 16-byte chunk for 16-bit types, two for fp32).  A and B
+// fragments use the same element -> k mapping, so the products pair up
+// correctly whatever k numbering the instruction uses internally.
+// `load` reads slice s of a 128-byte LDS row whose chunks are XOR-swizzled
+// by `sw`; lanes 32..63 (h = 1) take the second half of the slice.
+template <class E>
+struct Mma;
+
+template <>
+struct Mma<EBF16> {
+  typedef u32x4 Frag;
+  __device__ static __forceinline__ Frag load(const unsigned char *row, int s, int h, int sw) {
+    return *reinterpret_cast<const u32x4 *>(row + (((2 * s + h) ^ sw) << 4));
+  }
+  __device__ static __forceinline__ f32x16_t run(Frag a, Frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<EF16> {
+  typedef u32x4 Frag;
+  __device__ static __forceinline__ Frag load(const unsigned char *row, int s, int h, int sw) {
+    return *reinterpret_cast<const u32x4 *>(row + (((2 * s + h) ^ sw) << 4));
+  }
+  __device__ static __forceinline__ f32x16_t run(Frag a, Frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<EF32> {
+  struct Frag {
+    u32x4 lo, hi;
+  };
+  __device__ static __forceinline__ Frag load(const unsigned char *row, int s, int h, int sw) {
+    Frag f;
+    f.lo = *reinterpret_cast<const u32x4 *>(row + (((4 * s + 2 * h) ^ sw) << 4));
+    f.hi = *reinterpret_cast<const u32x4 *>(row + (((4 * s + 2 * h + 1) ^ sw) << 4));
+    return f;
+  }
+  __device__ static __forceinline__ f32x16_t run(Frag a, Frag b, f32x16_t c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.lo[e]), __uint_as_float(b.lo[e]), c, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.hi[e]), __uint_as_float(b.hi[e]), c, 0, 0, 0);
+    return c;
+  }
+};
+
+__device__ __forceinline__ void store_out(void *base, int64_t idx, int dt, float v) {
+  if (dt == DT_F32) {
+    static_cast<float *>(base)[idx] = v;
+  } else if (dt == DT_BF16) {
+    static_cast<uint16_t *>(base)[idx] = f32_to_bf16(v);
+  } else {
+    static_cast<uint16_t *>(base)[idx] = f32_to_f16(v);
+  }
+}
+
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: rows r and
+// r' within any aligned group of 8 (and the even / odd rows of any aligned
+// group of 16) land on different banks for the column-wise fragment reads.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// ---------------------------------------------------------------------------
+// NT product with fused epilogues
+// ---------------------------------------------------------------------------
+template <class E, int TILE, int MODE>
+__global__ void __launch_bounds__(256)
+gemm_nt(GemmParams p) {
+  using S = typename E::S;
+  constexpr int ESZ = sizeof(S);
+  constexpr int BKE = 128 / ESZ;          // contraction elements per K step
+  constexpr int SUB = BKE / 16;           // 16-deep slices per K step
+  constexpr int CPF = (8 * ESZ) / 16;     // 16-byte chunks per lane fragment
+  constexpr int WT = TILE / 2;            // wave tile edge
+  constexpr int NB = WT / 32;             // 32x32 blocks per wave edge
+  constexpr int LOADS = TILE / 32;        // 16-byte chunks per thread per operand
+  constexpr int OPB = TILE * 128;         // bytes of one operand buffer
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * OPB];
+
+  // Workgroup -> tile.  Consecutive tiles share an operand panel; the
+  // hardware deals workgroups round-robin over the 8 XCDs, so regroup ids to
+  // keep runs of consecutive tiles on one XCD (one L2).
+  const int G = gridDim.x;
+  const int w = blockIdx.x;
+  const int G8 = G & ~7;
+  const int lw = (w < G8) ? ((w & 7) * (G8 >> 3) + (w >> 3)) : w;
+  const int mat = lw / p.tiles_per_mat;
+  const int t = lw - mat * p.tiles_per_mat;
+  int ti, tj;
+  if (MODE == MODE_SYM) {
+    int bj = static_cast<int>((sqrtf(8.0f * static_cast<float>(t) + 1.0f) - 1.0f) * 0.5f);
+    while ((bj + 1) * (bj + 2) / 2 <= t) ++bj;
+    while (bj * (bj + 1) / 2 > t) --bj;
+    tj = bj;
+    ti = t - bj * (bj + 1) / 2;
+  } else {
+    ti = t % p.tiles_m;
+    tj = t / p.tiles_m;
+  }
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = (wave >> 1) * WT;
+  const int wc = (wave & 1) * WT;
+
+  const unsigned char *Ag = static_cast<const unsigned char *>(p.A) +
+                            (static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda) * ESZ;
+  const unsigned char *Bg = static_cast<const unsigned char *>(p.B) +
+                            (static_cast<int64_t>(mat) * p.sB + static_cast<int64_t>(tj) * TILE * p.ldb) * ESZ;
+  const int64_t ldaB = p.lda * ESZ;
+  const int64_t ldbB = p.ldb * ESZ;
+
+  // global -> register -> LDS staging coordinates
+  const int lrow0 = tid >> 3;
+  const int lch = tid & 7;
+  const int wofs = lrow0 * 128 + ((lch ^ swz(lrow0)) << 4);  // + q * 32 rows * 128 B
+  const int64_t gA0 = lrow0 * ldaB + lch * 16;
+  const int64_t gB0 = lrow0 * ldbB + lch * 16;
+
+  // fragment read coordinates: block b of a wave covers rows wr/wc + b*32 + lane%32
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int fsw = swz(lr);
+
+  f32x16_t acc[NB][NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = p.K / BKE;
+  u32x4 ra[LOADS], rb[LOADS];
+#pragma unroll
+  for (int q = 0; q < LOADS; ++q) {
+    ra[q] = *reinterpret_cast<const u32x4 *>(Ag + gA0 + q * 32 * ldaB);
+    rb[q] = *reinterpret_cast<const u32x4 *>(Bg + gB0 + q * 32 * ldbB);
+  }
+#pragma unroll
+  for (int q = 0; q < LOADS; ++q) {
+    *reinterpret_cast<u32x4 *>(lds + wofs + q * 32 * 128) = ra[q];
+    *reinterpret_cast<u32x4 *>(lds + OPB + wofs + q * 32 * 128) = rb[q];
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int64_t kb = static_cast<int64_t>(kt + 1) * 128;
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q) {
+        ra[q] = *reinterpret_cast<const u32x4 *>(Ag + gA0 + q * 32 * ldaB + kb);
+        rb[q] = *reinterpret_cast<const u32x4 *>(Bg + gB0 + q * 32 * ldbB + kb);
+      }
+    }
+    const unsigned char *la = lds + cur * 2 * OPB;
+    const unsigned char *lb = la + OPB;
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      typename Mma<E>::Frag fa[NB], fb[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        fa[b] = Mma<E>::load(la + (wr + b * 32 + lr) * 128, s, lh, fsw);
+        fb[b] = Mma<E>::load(lb + (wc + b * 32 + lr) * 128, s, lh, fsw);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = Mma<E>::run(fa[i], fb[j], acc[i][j]);
+    }
+    if (more) {
+      unsigned char *wa = lds + (cur ^ 1) * 2 * OPB;
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q) {
+        *reinterpret_cast<u32x4 *>(wa + wofs + q * 32 * 128) = ra[q];
+        *reinterpret_cast<u32x4 *>(wa + OPB + wofs + q * 32 * 128) = rb[q];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // 32x32 accumulator layout: lane l, register r holds row
+  // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its block.
+  const int64_t row_base = static_cast<int64_t>(ti) * TILE + wr;
+  const int64_t col_base = static_cast<int64_t>(tj) * TILE + wc;
+  const S *Dm = p.D ? static_cast<const S *>(p.D) + static_cast<int64_t>(mat) * p.sD : nullptr;
+
+  if (MODE == MODE_SYM) {
+    S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
+    S *C2m = p.C2 ? static_cast<S *>(p.C2) + static_cast<int64_t>(mat) * p.sC2 : nullptr;
+    const bool diag_tile = (ti == tj);
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
+          const int64_t j = col_base + jb * 32 + lr;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = p.alpha * acc[ib][jb][4 * g + q];
+            if (Dm) v[q] += p.beta * E::ld(Dm[(i0 + q) * p.ldd + j]);
+          }
+          if (!diag_tile) {
+            S sv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              sv[q] = E::st(v[q]);
+              Cm[(i0 + q) * p.ldc + j] = sv[q];
+              if (C2m) C2m[(i0 + q) * p.ldc + j] = sv[q];
+            }
+            // mirrored copy: four consecutive entries of row j
+            if (ESZ == 2) {
+              uint2 pk;
+              pk.x = static_cast<uint32_t>(sv[0]) | (static_cast<uint32_t>(sv[1]) << 16);
+              pk.y = static_cast<uint32_t>(sv[2]) | (static_cast<uint32_t>(sv[3]) << 16);
+              *reinterpret_cast<uint2 *>(Cm + j * p.ldc + i0) = pk;
+              if (C2m) *reinterpret_cast<uint2 *>(C2m + j * p.ldc + i0) = pk;
+            } else {
+              float4 pk = make_float4(v[0], v[1], v[2], v[3]);
+              *reinterpret_cast<float4 *>(Cm + j * p.ldc + i0) = pk;
+              if (C2m) *reinterpret_cast<float4 *>(C2m + j * p.ldc + i0) = pk;
+            }
+          } else {
+            // Diagonal tile: keep the upper-triangle value of each pair and
+            // write it to both places, each entry exactly once.
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t i = i0 + q;
+              if (i > j) continue;
+              const float dg = (i == j && i < p.n_real) ? 1.0f : 0.0f;
+              const S s1 = E::st(v[q] + dg * p.diag1);
+              Cm[i * p.ldc + j] = s1;
+              if (i != j) Cm[j * p.ldc + i] = s1;
+              if (C2m) {
+                const S s2 = E::st(v[q] + dg * p.diag2);
+                C2m[i * p.ldc + j] = s2;
+                if (i != j) C2m[j * p.ldc + i] = s2;
+              }
+            }
+          }
+        }
+  } else if (MODE == MODE_GEN) {
+    S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
+    S *CTm = p.CT ? static_cast<S *>(p.CT) + static_cast<int64_t>(mat) * p.sCT : nullptr;
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
+          const int64_t j = col_base + jb * 32 + lr;
+          S sv[4];
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = p.alpha * acc[ib][jb][4 * g + q];
+            if (Dm) v[q] += p.beta * E::ld(Dm[(i0 + q) * p.ldd + j]);
+            sv[q] = E::st(v[q]);
+            Cm[(i0 + q) * p.ldc + j] = sv[q];
+          }
+          if (CTm) {
+            if (ESZ == 2) {
+              uint2 pk;
+              pk.x = static_cast<uint32_t>(sv[0]) | (static_cast<uint32_t>(sv[1]) << 16);
+              pk.y = static_cast<uint32_t>(sv[2]) | (static_cast<uint32_t>(sv[3]) << 16);
+              *reinterpret_cast<uint2 *>(CTm + j * p.ldct + i0) = pk;
+            } else {
+              *reinterpret_cast<float4 *>(CTm + j * p.ldct + i0) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+          }
+        }
+  } else {  // MODE_FINAL
+    const int64_t *ridx = p.row_idx ? p.row_idx + static_cast<int64_t>(mat) * p.rows_eff : nullptr;
+    const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
+          const int64_t j = col_base + jb * 32 + lr;
+          if (j >= p.out_cols) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t i = i0 + q;
+            if (i >= p.rows_eff) continue;
+            float v = p.alpha * acc[ib][jb][4 * g + q];
+            if (Dm) v += p.beta * E::ld(Dm[i * p.ldd + j]);
+            const int64_t row = ridx ? ridx[i] : i;
+            if (row < 0 || row >= p.out_rows) continue;
+            store_out(p.out, obase + row * p.out_cols + j, p.out_dtype, v);
+          }
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Frobenius norm, stage 1: per-workgroup partial sums of squares
+// ---------------------------------------------------------------------------
+template <class TIn>
+__global__ void __launch_bounds__(256)
+norm_partial(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int64_t *row_idx,
+             int parts, double *partials) {
+  using S = typename TIn::S;
+  const int b = blockIdx.y;
+  const int part = blockIdx.x;
+  const int64_t rpp = (rows_eff + parts - 1) / parts;
+  const int64_t r0 = part * rpp;
+  const int64_t r1 = (r0 + rpp < rows_eff) ? r0 + rpp : rows_eff;
+  const S *Xb = static_cast<const S *>(X) + static_cast<int64_t>(b) * n * m;
+  constexpr int VE = 16 / sizeof(S);  // elements per 16-byte vector
+  const bool vec = ((m * static_cast<int64_t>(sizeof(S))) % 16 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+  double dacc = 0.0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int64_t row = row_idx ? row_idx[static_cast<int64_t>(b) * rows_eff + r] : r;
+    if (row < 0 || row >= n) continue;
+    const S *xr = Xb + row * m;
+    float s = 0.0f;
+    if (vec) {
+      const uint4 *xv = reinterpret_cast<const uint4 *>(xr);
+      const int64_t nv = m / VE;
+      for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+        const uint4 u = xv[v];
+        const S *e = reinterpret_cast<const S *>(&u);
+#pragma unroll
+        for (int q = 0; q < VE; ++q) {
+          const float f = TIn::ld(e[q]);
+          s += f * f;
+        }
+      }
+    } else {
+      for (int64_t c = threadIdx.x; c < m; c += blockDim.x) {
+        const float f = TIn::ld(xr[c]);
+        s += f * f;
+      }
+    }
+    dacc += static_cast<double>(s);
+  }
+  // fixed-order reduction: wave tree, then the four waves in order
+  for (int off = 32; off > 0; off >>= 1) dacc += __shfl_down(dacc, off, 64);
+  __shared__ double wsum[4];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = dacc;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partials[static_cast<int64_t>(b) * parts + part] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// ---------------------------------------------------------------------------
+// X_hat = X / (||X||_F + eps), rounded to the compute dtype, in both layouts
+// ---------------------------------------------------------------------------
+template <class TIn, class TCmp>
+__global__ void __launch_bounds__(256)
+scale_transpose(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int64_t *row_idx,
+                const double *partials, int parts, double eps, void *Xh, void *XT, int64_t Np,
+                int64_t Mp) {
+  using SI = typename TIn::S;
+  using SC = typename TCmp::S;
+  const int b = blockIdx.z;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  __shared__ float inv_s;
+  __shared__ SC tileT[64][65];
+
+  if (threadIdx.x < 64) {  // norm stage 2, same fixed order in every workgroup
+    double s = 0.0;
+    for (int i = threadIdx.x; i < parts; i += 64) s += partials[static_cast<int64_t>(b) * parts + i];
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off, 64);
+    if (threadIdx.x == 0) inv_s = static_cast<float>(1.0 / (sqrt(s) + eps));
+  }
+  __syncthreads();
+  const float inv = inv_s;
+
+  const SI *Xb = static_cast<const SI *>(X) + static_cast<int64_t>(b) * n * m;
+  SC *Xhb = static_cast<SC *>(Xh) + static_cast<int64_t>(b) * Np * Mp;
+  SC *XTb = static_cast<SC *>(XT) + static_cast<int64_t>(b) * Mp * Np;
+  const int col = threadIdx.x & 63;
+  const int rg = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int rr = 0; rr < 16; ++rr) {
+    const int r = rg + 4 * rr;
+    const int64_t gr = r0 + r;
+    const int64_t gc = c0 + col;
+    float v = 0.0f;
+    if (gr < rows_eff && gc < m) {
+      const int64_t row = row_idx ? row_idx[static_cast<int64_t>(b) * rows_eff + gr] : gr;
+      if (row >= 0 && row < n) v = TIn::ld(Xb[row * m + gc]) * inv;
+    }
+    const SC sv = TCmp::st(v);
+    Xhb[gr * Mp + gc] = sv;
+    tileT[col][r] = sv;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int rr = 0; rr < 16; ++rr) {
+    const int c = rg + 4 * rr;
+    XTb[(c0 + c) * Np + r0 + col] = tileT[c][col];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// row subset check
+// ---------------------------------------------------------------------------
+__global__ void check_rows_init(int32_t *result) { *result = 0; }
+
+__global__ void __launch_bounds__(256)
+check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
+  __shared__ uint32_t seen[65536 / 32];
+  const int64_t words = (n + 31) / 32;
+  for (int64_t i = threadIdx.x; i < words; i += blockDim.x) seen[i] = 0u;
+  __syncthreads();
+  const int64_t *ri = row_idx + static_cast<int64_t>(blockIdx.x) * k;
+  int bad = 0;
+  for (int64_t i = threadIdx.x; i < k; i += blockDim.x) {
+    const int64_t r = ri[i];
+    if (r < 0 || r >= n) {
+      bad = bad > 1 ? bad : 1;
+      continue;
+    }
+    const uint32_t bit = 1u << (r & 31);
+    const uint32_t old = atomicOr(&seen[r >> 5], bit);
+    if (old & bit) bad = 2;
+  }
+  if (bad) atomicMax(result, bad);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <class E, int TILE>
+static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
+  const int grid = p.tiles_per_mat * p.batch;
+  if (grid <= 0) return hipSuccess;
+  switch (mode) {
+    case MODE_SYM: gemm_nt<E, TILE, MODE_SYM><<<grid, 256, 0, s>>>(p); break;
+    case MODE_GEN: gemm_nt<E, TILE, MODE_GEN><<<grid, 256, 0, s>>>(p); break;
+    default: gemm_nt<E, TILE, MODE_FINAL><<<grid, 256, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dt, int tile, int mode, const GemmParams &p, hipStream_t s) {
+  if (dt == DT_BF16) return tile == 256 ? launch_gemm_t<EBF16, 256>(mode, p, s) : launch_gemm_t<EBF16, 128>(mode, p, s);
+  if (dt == DT_F16) return tile == 256 ? launch_gemm_t<EF16, 256>(mode, p, s) : launch_gemm_t<EF16, 128>(mode, p, s);
+  return tile == 256 ? launch_gemm_t<EF32, 256>(mode, p, s) : launch_gemm_t<EF32, 128>(mode, p, s);
+}
+
+const char *gemm_kernel_name(int dt, int tile, int mode) {
+  static const char *names[3][2][3] = {
+      {{"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"},
+       {"gemm_nt<f32,256,sym>", "gemm_nt<f32,256,gen>", "gemm_nt<f32,256,final>"}},
+      {{"gemm_nt<bf16,128,sym>", "gemm_nt<bf16,128,gen>", "gemm_nt<bf16,128,final>"},
+       {"gemm_nt<bf16,256,sym>", "gemm_nt<bf16,256,gen>", "gemm_nt<bf16,256,final>"}},
+      {{"gemm_nt<f16,128,sym>", "gemm_nt<f16,128,gen>", "gemm_nt<f16,128,final>"},
+       {"gemm_nt<f16,256,sym>", "gemm_nt<f16,256,gen>", "gemm_nt<f16,256,final>"}}};
+  return names[dt][tile == 256 ? 1 : 0][mode];
+}
+
+hipError_t launch_norm_partial(int io, const void *X, int64_t batch, int64_t n, int64_t m,
+                               int64_t rows_eff, const int64_t *row_idx, int parts,
+                               double *partials, hipStream_t s) {
+  dim3 grid(parts, static_cast<unsigned>(batch));
+  if (io == DT_BF16) norm_partial<EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, parts, partials);
+  else if (io == DT_F16) norm_partial<EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, parts, partials);
+  else norm_partial<EF32><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, parts, partials);
+  return hipGetLastError();
+}
+
+template <class TIn>
+static void st_dispatch(int cdt, dim3 grid, hipStream_t s, const void *X, int64_t n, int64_t m,
+                        int64_t rows_eff, const int64_t *row_idx, const double *partials,
+                        int parts, double eps, void *Xh, void *XT, int64_t Np, int64_t Mp) {
+  if (cdt == DT_BF16)
+    scale_transpose<TIn, EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+  else if (cdt == DT_F16)
+    scale_transpose<TIn, EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+  else
+    scale_transpose<TIn, EF32><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+}
+
+hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch, int64_t n,
+                                  int64_t m, int64_t rows_eff, const int64_t *row_idx,
+                                  const double *partials, int parts, double eps, void *Xh,
+                                  void *XT, int64_t Np, int64_t Mp, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(Mp / 64), static_cast<unsigned>(Np / 64), static_cast<unsigned>(batch));
+  if (io == DT_BF16) st_dispatch<EBF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+  else if (io == DT_F16) st_dispatch<EF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+  else st_dispatch<EF32>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
+                             int32_t *result, hipStream_t s) {
+  check_rows_init<<<1, 1, 0, s>>>(result);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  check_rows<<<static_cast<unsigned>(batch), 256, 0, s>>>(row_idx, k, n, result);
+  return hipGetLastError();
+}
+
+}  // namespace gns

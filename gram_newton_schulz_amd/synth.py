@@ -21,6 +21,8 @@ Workloads (shapes of the pages' dense-MLP and MoE-expert weights):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -101,7 +103,8 @@ def draw_f64(dist: str, n: int, m: int, seed: int, index: int,
 def to_storage(x64: np.ndarray, dtype: torch.dtype, normalize: bool) -> torch.Tensor:
     """Optionally scale to unit Frobenius norm (float64), then round once."""
     if normalize:
-        x64 = x64 / np.sqrt(np.sum(x64 * x64))
+        flat = x64.ravel()
+        x64 = x64 / np.sqrt(np.dot(flat, flat))
     return torch.from_numpy(np.ascontiguousarray(x64)).to(dtype)
 
 
@@ -111,14 +114,31 @@ def matrix(n: int, m: int, *, seed: int, index: int = 0, dist: str = "normal",
     return to_storage(draw_f64(dist, n, m, seed, index, spectrum), dtype, normalize)
 
 
+def _workers(count: int) -> int:
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return max(1, min(count, cores, 16))
+
+
+def _fill(out: torch.Tensor, make) -> torch.Tensor:
+    """out[b] = make(b) for every b, on a thread pool (numpy's generators
+    release the GIL); each member has its own seed, so the result does not
+    depend on the pool size."""
+    def one(b):
+        out[b] = make(b)
+    with ThreadPoolExecutor(_workers(out.shape[0])) as ex:
+        list(ex.map(one, range(out.shape[0])))
+    return out
+
+
 def batch(count: int, n: int, m: int, *, seed: int, dist: str = "normal",
           dtype: torch.dtype = torch.bfloat16, normalize: bool = True,
           spectrum=(-4.0, 0.0), first: int = 0) -> torch.Tensor:
     out = torch.empty((count, n, m), dtype=dtype)
-    for b in range(count):
-        out[b] = matrix(n, m, seed=seed, index=first + b, dist=dist, dtype=dtype,
-                        normalize=normalize, spectrum=spectrum)
-    return out
+    return _fill(out, lambda b: matrix(n, m, seed=seed, index=first + b, dist=dist, dtype=dtype,
+                                       normalize=normalize, spectrum=spectrum))
 
 
 def row_subset(n: int, k: int, *, seed: int, index: int) -> np.ndarray:
@@ -138,9 +158,7 @@ def workload_batch(cfg: int, count: Optional[int] = None) -> torch.Tensor:
     w = WORKLOADS[cfg]
     count = w.batch if count is None else count
     out = torch.empty((count, w.n, w.m), dtype=w.dtype)
-    for b in range(count):
-        out[b] = workload_matrix(cfg, b)
-    return out
+    return _fill(out, lambda b: workload_matrix(cfg, b))
 
 
 def workload_rows(cfg: int, count: Optional[int] = None) -> Optional[torch.Tensor]:

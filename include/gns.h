@@ -1,0 +1,198 @@
+/*
+ * gns.h -- C ABI of the MI355X (gfx950) Gram Newton-Schulz library.
+ *
+ * The library orthogonalises batches of n x m matrices (n <= m) the way the
+ * Muon family of optimisers does: it approximates polar(X) = U V^T
+ * ("Dion3: Full-Stack Orthogonal Updates", §2.1 Definition 1) with a fixed
+ * number T of odd quintic steps p_t(x) = a_t x + b_t x^3 + c_t x^5
+ * (same paper, §2.2).  Two algorithms are exported:
+ *
+ *   gns_gram_batched      Gram Newton-Schulz (Dion3 §4, Algorithms 2 and 3):
+ *                         iterate on the n x n Gram matrix R = X X^T and the
+ *                         accumulated polynomial Q, restart at the given
+ *                         iterations (§4.2, Appendix B.2), return Q_T X.
+ *   gns_standard_batched  standard Newton-Schulz (Dion3 §2.2, Algorithm 1),
+ *                         the comparison path.
+ *
+ * Both optionally work on a row subset of every matrix (Dion3 §6,
+ * Algorithm 4: orthogonalise M[S,:] only).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked (device) are HIP device pointers; (host) are host
+ *   pointers read before the call returns.
+ * - X and out are contiguous row-major [batch][n][m] in the I/O dtype.
+ * - The caller owns every buffer, including the workspace; the library never
+ *   allocates or frees device memory and never synchronises the stream.
+ *   All work is enqueued on `stream` in order; the call returns once it is
+ *   enqueued.  Results are ready when the stream is.
+ * - Argument errors are detected on the host before anything is enqueued
+ *   (no partial work) and reported as a status code; nothing throws across
+ *   the ABI.  A failed kernel launch returns GNS_E_HIP.  Faults inside
+ *   kernels surface at the caller's next synchronisation.
+ * - out may be the same buffer as X (X is read completely into the
+ *   workspace before out is written).  The workspace must not overlap X or
+ *   out.
+ * - Results are deterministic for a fixed shape, dtype and option set (no
+ *   atomics, fixed reduction order).
+ * - batch == 0 is a no-op that returns GNS_OK (pointers may then be NULL).
+ * - Calls that share one workspace must be ordered on one stream; calls with
+ *   separate workspaces are independent and thread-safe.
+ */
+#ifndef GNS_H_
+#define GNS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GNS_ABI_VERSION 1
+
+typedef enum {
+  GNS_F32 = 0,  /* IEEE binary32                          */
+  GNS_BF16 = 1, /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+  GNS_F16 = 2   /* IEEE binary16                          */
+} gns_dtype;
+
+typedef enum {
+  GNS_OK = 0,
+  GNS_E_NULL = 1,      /* a required pointer is NULL                          */
+  GNS_E_SHAPE = 2,     /* n < 1, m < rows, k not in [1, n], or too large      */
+  GNS_E_DTYPE = 3,     /* unknown dtype                                       */
+  GNS_E_COEFF = 4,     /* T < 1, T > GNS_MAX_ITERS, or a non-finite coeff.    */
+  GNS_E_RESTART = 5,   /* restart list not strictly increasing in [1, T-1]    */
+  GNS_E_ROWIDX = 6,    /* row index out of range or repeated (check call)     */
+  GNS_E_ALIAS = 7,     /* workspace overlaps X or out                         */
+  GNS_E_WORKSPACE = 8, /* workspace NULL or smaller than gns_*_workspace_bytes */
+  GNS_E_HIP = 9,       /* a HIP launch or runtime call failed                 */
+  GNS_E_FLAGS = 10     /* unknown option bit                                  */
+} gns_status;
+
+#define GNS_MAX_ITERS 64
+
+/* Option bits for gns_gram_batched. */
+#define GNS_OPT_NAIVE_ALGEBRA 0x1u /* Algorithm 2 algebra: Z = aI + bR + cR^2,
+                                      Q <- QZ, R <- ZRZ (default: Algorithm 3's
+                                      reformulation with explicit a-terms,
+                                      Dion3 Appendix B.2.3); gns_gram_batched only */
+#define GNS_OPT_TILE_128 0x10u     /* force 128 x 128 output tiles            */
+#define GNS_OPT_TILE_256 0x20u     /* force 256 x 256 output tiles            */
+/* Without a TILE bit the library picks the tile edge from the problem size.
+   Results are identical up to floating-point summation order either way. */
+
+/* Version of this ABI (GNS_ABI_VERSION). */
+int gns_abi_version(void);
+
+/* Static string naming a status code. */
+const char *gns_status_str(gns_status s);
+
+/*
+ * Workspace bytes that gns_gram_batched needs for this problem.
+ *   rows = k when a row subset is used, else n.  Returns 0 for invalid
+ *   arguments (rows < 1, m < rows, unknown dtype) and for batch == 0.
+ */
+size_t gns_gram_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int64_t rows, int64_t m);
+
+/* Same for gns_standard_batched. */
+size_t gns_standard_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int64_t rows, int64_t m);
+
+/*
+ * Gram Newton-Schulz on a batch (Dion3 §4.2, Algorithm 3; §4 Algorithm 2
+ * with GNS_OPT_NAIVE_ALGEBRA).
+ *
+ *   X          (device) [batch][n][m], io_dtype, read only.
+ *   out        (device) [batch][n][m], io_dtype.  Without a row subset every
+ *              element is written.  With a row subset only the selected rows
+ *              are written; the others keep what the caller put there.
+ *   batch      number of matrices (>= 0).
+ *   n, m       matrix shape; the orthogonalised matrix (all rows, or the k
+ *              selected ones) must have rows <= m (the pages' n <= m).
+ *   io_dtype   dtype of X and out.
+ *   compute_dtype  dtype of the matrix products' operands (GNS_BF16 or
+ *              GNS_F16: MFMA with fp32 accumulation; GNS_F32: fp32 MFMA).
+ *              Every product accumulates in fp32, applies its a/b/c terms
+ *              in fp32 and rounds its result once to compute_dtype.
+ *   coeffs     (host) T x 3 doubles, row t = (a_t, b_t, c_t) of
+ *              p_t(x) = a_t x + b_t x^3 + c_t x^5 (used as given: a safety
+ *              factor s is applied by the caller as (a/s, b/s^3, c/s^5),
+ *              Dion3 Appendix B.2.2).
+ *   T          number of iterations, 1..GNS_MAX_ITERS.
+ *   restart_after (host) n_restart iterations s, strictly increasing, each in
+ *              [1, T-1]: before iteration s+1 the input is replaced by
+ *              Q_s X, R is re-formed from it and Q is reset to I (Dion3
+ *              §4.2; the pages' default is {2} for T = 5).  May be NULL when
+ *              n_restart == 0.
+ *   row_idx    (device) [batch][k] int64 or NULL.  When given, rows
+ *              row_idx[b][0..k) of X_b form one k x m matrix, normalised by
+ *              its own Frobenius norm (Dion3 §6, Algorithm 4), and its
+ *              orthogonalised rows are written to the same rows of out_b.
+ *              Indices must be distinct and in [0, n): this is a
+ *              precondition (checkable with gns_check_row_idx); kernels
+ *              never access memory outside X or out for a bad index (an
+ *              out-of-range row reads as zeros and is not written).
+ *   k          rows per matrix when row_idx != NULL (1 <= k <= n); ignored
+ *              otherwise.
+ *   opts       GNS_OPT_* bits.
+ *   workspace  (device) >= gns_gram_workspace_bytes(compute_dtype, batch,
+ *              rows, m) bytes, 256-byte aligned; contents on entry do not
+ *              matter and are clobbered.
+ *   stream     HIP stream (hipStream_t) or NULL for the default stream.
+ */
+gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                            gns_dtype io_dtype, gns_dtype compute_dtype,
+                            const double *coeffs, int T,
+                            const int *restart_after, int n_restart,
+                            const int64_t *row_idx, int64_t k, unsigned opts,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Standard Newton-Schulz on a batch (Dion3 §2.2, Algorithm 1) with the
+ * symmetric products computed once per pair of mirrored tiles (Dion3 §5,
+ * Appendix C.3): per iteration A = X X^T, B = b A + c A^2, X <- a X + B X.
+ * Arguments as for gns_gram_batched (no restarts; opts takes the TILE bits).
+ */
+gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                                gns_dtype io_dtype, gns_dtype compute_dtype,
+                                const double *coeffs, int T,
+                                const int64_t *row_idx, int64_t k, unsigned opts,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Enqueue a check of a row subset: writes to *result (device int32) 0 when
+ * every row_idx[b][i] is in [0, n) and the k indices of each matrix are
+ * distinct, 1 when an index is out of range, 2 when an index repeats.
+ * The caller reads *result after synchronising the stream.  Needs k <= n
+ * and n <= 65536.
+ */
+gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
+                             int32_t *result, void *stream);
+
+/*
+ * Optional per-launch timing for measurement tools.  While enabled, every
+ * kernel that a gns_*_batched call enqueues is bracketed by HIP events on the
+ * call's stream.  gns_timing_read synchronises those events and returns,
+ * for each kernel launched since the last reset, its name (static string),
+ * its algorithmic FLOP count (2 per multiply-add, symmetric products
+ * counted once per output pair), its algorithmic HBM bytes and its duration
+ * in milliseconds.  Returns the number of records available (it may exceed
+ * cap; only cap are copied).  Not thread-safe; for benchmarking only.
+ */
+typedef struct {
+  const char *name;   /* step of the method, e.g. "syrk", "q_update"       */
+  const char *kernel; /* kernel that ran it, e.g. "gemm_nt<bf16,256,sym>" */
+  double flops;
+  double bytes;
+  float ms;
+} gns_launch_record;
+
+void gns_timing_enable(int on);
+int gns_timing_read(gns_launch_record *records, int cap);
+void gns_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GNS_H_ */

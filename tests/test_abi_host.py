@@ -1,0 +1,130 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol include/gns.h declares, sizes workspaces, and rejects bad arguments
+with the documented status before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gns.h")
+
+gns = pytest.importorskip("gram_newton_schulz_amd")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gns.LIB_PATH),
+                                reason="libgns.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000000  # never dereferenced: every call below fails validation first
+E = {"OK": 0, "NULL": 1, "SHAPE": 2, "DTYPE": 3, "COEFF": 4, "RESTART": 5, "ROWIDX": 6,
+     "ALIAS": 7, "WORKSPACE": 8, "HIP": 9, "FLAGS": 10}
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gns_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = gns.lib()
+    decl = declared_functions()
+    assert decl, "no declarations parsed"
+    for name in decl:
+        assert hasattr(L, name), f"{name} declared in gns.h but not exported"
+    assert sorted(gns.EXPORTS) == decl
+
+
+def test_version_and_strings():
+    L = gns.lib()
+    assert L.gns_abi_version() == 1
+    for code in range(0, 11):
+        assert L.gns_status_str(code)
+
+
+def test_workspace_sizes():
+    b = gns.gram_workspace_bytes(gns.GNS_BF16, 8, 4096, 16384)
+    # X_hat, two transposed copies and five n x n iterates, bf16
+    assert b >= 8 * 2 * (3 * 4096 * 16384 + 5 * 4096 * 4096)
+    assert gns.gram_workspace_bytes(gns.GNS_BF16, 0, 4096, 16384) == 0
+    assert gns.gram_workspace_bytes(gns.GNS_BF16, 1, 10, 5) == 0          # rows > m
+    assert gns.gram_workspace_bytes(7, 1, 10, 20) == 0                     # bad dtype
+    assert gns.standard_workspace_bytes(gns.GNS_F32, 1, 64, 256) > 0
+    # ragged shapes are padded to whole tiles
+    small = gns.gram_workspace_bytes(gns.GNS_F32, 1, 1, 1)
+    assert small >= 4 * (3 * 128 * 128 + 5 * 128 * 128)
+
+
+def _gram(X=FAKE, out=FAKE + 1 << 20, batch=1, n=4, m=8, io=1, cdt=1, coeffs=None, T=None,
+          restarts=(2,), row_idx=None, k=0, opts=0, ws=None, ws_bytes=None):
+    L = gns.lib()
+    if coeffs is None:
+        coeffs = [(3.4445, -4.7750, 2.0315)] * 5
+    flat = [float(v) for row in coeffs for v in row]
+    carr = (ctypes.c_double * max(len(flat), 1))(*flat)
+    T = len(coeffs) if T is None else T
+    rs = list(restarts)
+    rarr = (ctypes.c_int * max(len(rs), 1))(*rs) if rs else None
+    rows = k if row_idx else n
+    need = L.gns_gram_workspace_bytes(cdt, batch, rows, m)
+    if ws is None:
+        ws = 0x7f0000000000
+    if ws_bytes is None:
+        ws_bytes = need
+    return L.gns_gram_batched(X, out, batch, n, m, io, cdt, carr, T, rarr, len(rs),
+                              row_idx, k, opts, ws, ws_bytes, None)
+
+
+def test_gram_argument_errors():
+    assert _gram(io=5) == E["DTYPE"]
+    assert _gram(cdt=9) == E["DTYPE"]
+    assert _gram(n=0) == E["SHAPE"]
+    assert _gram(n=9, m=8) == E["SHAPE"]                  # n > m
+    assert _gram(row_idx=FAKE, k=0) == E["SHAPE"]
+    assert _gram(row_idx=FAKE, k=5, n=4) == E["SHAPE"]    # k > n
+    assert _gram(coeffs=[], T=0, restarts=()) == E["COEFF"]
+    assert _gram(coeffs=[(float("nan"), 1, 1)] * 3, restarts=(1,)) == E["COEFF"]
+    assert _gram(coeffs=[(1, 1, 1)] * 65, restarts=()) == E["COEFF"]
+    assert _gram(restarts=(0,)) == E["RESTART"]
+    assert _gram(restarts=(5,)) == E["RESTART"]           # must be <= T-1
+    assert _gram(restarts=(3, 2)) == E["RESTART"]
+    assert _gram(restarts=(2, 2)) == E["RESTART"]
+    assert _gram(opts=0x80) == E["FLAGS"]
+    assert _gram(opts=0x30) == E["FLAGS"]                 # both tile bits
+    assert _gram(X=None) == E["NULL"]
+    assert _gram(out=None) == E["NULL"]
+    assert _gram(ws=None, ws_bytes=0) != E["OK"]
+    assert _gram(ws_bytes=100) == E["WORKSPACE"]
+    assert _gram(ws=0x7f0000000001) == E["WORKSPACE"]     # misaligned
+    # workspace overlapping X
+    assert _gram(X=0x7f0000000000 + 4096) == E["ALIAS"]
+
+
+def test_gram_batch_zero_is_noop():
+    assert _gram(batch=0, X=None, out=None, ws=None, ws_bytes=0) == E["OK"]
+
+
+def test_standard_argument_errors():
+    L = gns.lib()
+    carr = (ctypes.c_double * 15)(*([3.4445, -4.775, 2.0315] * 5))
+    ws = 0x7f0000000000
+    need = L.gns_standard_workspace_bytes(1, 1, 4, 8)
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 0, None, 0, 0, ws, need, None) == E["COEFF"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 8, 1, 1, carr, 5, None, 0, 0, ws, need, None) == E["SHAPE"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0, ws, 16, None) == E["WORKSPACE"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 1, ws, need, None) == E["FLAGS"]
+    assert L.gns_standard_batched(None, None, 0, 4, 8, 1, 1, carr, 5, None, 0, 0, None, 0, None) == E["OK"]
+
+
+def test_check_row_idx_argument_errors():
+    L = gns.lib()
+    assert L.gns_check_row_idx(None, 1, 2, 4, FAKE, None) == E["NULL"]
+    assert L.gns_check_row_idx(FAKE, 1, 5, 4, FAKE, None) == E["SHAPE"]
+    assert L.gns_check_row_idx(FAKE, 1, 2, 70000, FAKE, None) == E["SHAPE"]
+
+
+def test_binding_errors_are_raised():
+    import torch
+    X = torch.zeros(2, 3, 8)
+    with pytest.raises(gns.GnsError):
+        gns.gram_ns_batched(X, [(1, 0, 0)], restarts=(), compute_dtype=torch.int32)

@@ -1,0 +1,243 @@
+"""HIP path (through the C ABI) against the fp64 oracle on seeded inputs at
+sizes the oracle finishes in seconds: several tiles plus ragged tails, both
+tile edges, every dtype combination, restart sets, both algebras, the row
+subset, degenerate shapes, guard bands, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import (NS5, TOL_F32, TOL_HALF, need_gpu, per_matrix_rel, rel_err, say,
+                        oracle_gram, oracle_standard)
+from gram_newton_schulz_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _inputs(B, n, m, io, seed, dist="normal"):
+    X = synth.batch(B, n, m, seed=seed, dist=dist, dtype=DT[io])
+    return X, synth.as_f64(X)
+
+
+def _tol(cdt):
+    return TOL_F32 if cdt == "f32" else TOL_HALF
+
+
+def _run(gns, algo, Xd, cdt, **kw):
+    if algo == "gram":
+        return gns.gram_ns_batched(Xd, NS5, compute_dtype=DT[cdt], **kw)
+    kw.pop("restarts", None)
+    return gns.standard_ns_batched(Xd, NS5, compute_dtype=DT[cdt], **kw)
+
+
+def test_config1_fp32():
+    """64x256 fp32: Gram NS (restart after 2), standard NS and the SVD picture."""
+    gns = need_gpu()
+    X = synth.workload_batch(1)
+    X64 = synth.as_f64(X)
+    say("config1 fp32")
+    g = gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,))
+    s = gns.standard_ns_batched(X.cuda(), NS5)
+    torch.cuda.synchronize()
+    ref = oracle_gram(X64[0])
+    assert rel_err(synth.as_f64(g)[0], ref) <= TOL_F32
+    assert rel_err(synth.as_f64(s)[0], oracle_standard(X64[0])) <= TOL_F32
+    assert rel_err(ref, oracle.spectral_map(X64[0], NS5)) <= 1e-10
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("algo", ["gram", "standard"])
+@pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("bf16", "f16"), ("f32", "f32"),
+                                    ("f16", "f16"), ("f32", "bf16")])
+def test_ragged_parity(tile, algo, io, cdt):
+    gns = need_gpu()
+    B, n, m = 3, 300, 700          # 3 x 6 tiles of 128 with ragged tails
+    X, X64 = _inputs(B, n, m, io, seed=11)
+    say(f"ragged {algo} io={io} cdt={cdt} tile={tile} {B}x{n}x{m}")
+    out = _run(gns, algo, X.cuda(), cdt, tile=tile)
+    torch.cuda.synchronize()
+    got = synth.as_f64(out)
+    ref = np.stack([(oracle_gram if algo == "gram" else oracle_standard)(X64[b]) for b in range(B)])
+    errs = per_matrix_rel(got, ref)
+    say("  rel errs", errs)
+    assert max(errs) <= _tol(cdt)
+    assert out.dtype == X.dtype
+
+
+@pytest.mark.parametrize("restarts", [(), (1,), (2,), (1, 3), (1, 2, 3, 4)])
+def test_restart_sets_fp32(restarts):
+    gns = need_gpu()
+    X, X64 = _inputs(2, 200, 333, "f32", seed=12)
+    say(f"restarts {restarts}")
+    out = gns.gram_ns_batched(X.cuda(), NS5, restarts=restarts)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle_gram(X64[b], restarts=restarts) for b in range(2)])
+    assert max(per_matrix_rel(synth.as_f64(out), ref)) <= TOL_F32
+
+
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+def test_naive_algebra(cdt):
+    gns = need_gpu()
+    X, X64 = _inputs(2, 260, 520, "f32", seed=13)
+    say(f"naive algebra {cdt}")
+    out = gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,), naive_algebra=True,
+                              compute_dtype=DT[cdt])
+    torch.cuda.synchronize()
+    ref = np.stack([oracle_gram(X64[b], algebra="naive") for b in range(2)])
+    assert max(per_matrix_rel(synth.as_f64(out), ref)) <= _tol(cdt)
+
+
+def test_distinct_coefficients_per_iteration():
+    """A schedule whose iterations differ catches any mix-up of t or of (a,b,c)."""
+    gns = need_gpu()
+    co = [(3.0, -3.2, 1.2), (2.5, -2.0, 0.5), (15 / 8, -10 / 8, 3 / 8), (3.4445, -4.775, 2.0315),
+          (1.9, -1.3, 0.4), (1.5, -0.5, 0.0)]
+    X, X64 = _inputs(2, 150, 400, "f32", seed=14)
+    say("distinct coefficients")
+    g = gns.gram_ns_batched(X.cuda(), co, restarts=(2, 4))
+    s = gns.standard_ns_batched(X.cuda(), co)
+    torch.cuda.synchronize()
+    for b in range(2):
+        ref = oracle.gram_ns(X64[b], co, restarts=(2, 4))
+        assert rel_err(synth.as_f64(g)[b], ref) <= TOL_F32
+        assert rel_err(synth.as_f64(s)[b], oracle.standard_ns(X64[b], co)) <= TOL_F32
+
+
+@pytest.mark.parametrize("algo", ["gram", "standard"])
+@pytest.mark.parametrize("cdt", ["bf16", "f32"])
+def test_row_subset(algo, cdt):
+    """Dion3 rows: selected rows orthogonalised as one k x m matrix, the others
+    left bit-exact."""
+    gns = need_gpu()
+    B, n, m, k = 2, 200, 520, 77
+    io = "f32" if cdt == "f32" else "bf16"
+    X, X64 = _inputs(B, n, m, io, seed=15)
+    rows = np.stack([synth.row_subset(n, k, seed=15, index=b) for b in range(B)])
+    init = torch.randn(B, n, m, generator=torch.Generator().manual_seed(3)).to(DT[io])
+    out = init.clone().cuda()
+    say(f"row subset {algo} {cdt}")
+    _run(gns, algo, X.cuda(), cdt, row_idx=torch.from_numpy(rows).cuda(), out=out)
+    torch.cuda.synchronize()
+    got = synth.as_f64(out)
+    init64 = synth.as_f64(init)
+    for b in range(B):
+        sel = rows[b]
+        ref = (oracle_gram if algo == "gram" else oracle_standard)(X64[b][sel])
+        assert rel_err(got[b][sel], ref) <= _tol(cdt)
+        keep = np.setdiff1d(np.arange(n), sel)
+        assert np.array_equal(got[b][keep], init64[b][keep])
+
+
+def test_row_subset_full_permutation_matches_plain():
+    gns = need_gpu()
+    B, n, m = 2, 140, 300
+    X, _ = _inputs(B, n, m, "f32", seed=16)
+    perm = np.stack([np.random.default_rng(b).permutation(n) for b in range(B)])
+    say("full permutation")
+    a = gns.gram_ns_batched(X.cuda(), NS5, row_idx=torch.from_numpy(perm).cuda(),
+                            out=torch.zeros(B, n, m, device="cuda"))
+    b_ = gns.gram_ns_batched(X.cuda(), NS5)
+    torch.cuda.synchronize()
+    assert max(per_matrix_rel(synth.as_f64(a), synth.as_f64(b_))) <= 1e-5
+
+
+@pytest.mark.parametrize("shape", [(1, 37), (1, 1), (130, 130), (256, 256), (5, 4099), (129, 129)])
+@pytest.mark.parametrize("cdt", ["bf16", "f32"])
+def test_edge_shapes(shape, cdt):
+    gns = need_gpu()
+    n, m = shape
+    io = "f32" if cdt == "f32" else "bf16"
+    X, X64 = _inputs(2, n, m, io, seed=17)
+    say(f"edge {shape} {cdt}")
+    g = gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=DT[cdt])
+    s = gns.standard_ns_batched(X.cuda(), NS5, compute_dtype=DT[cdt])
+    torch.cuda.synchronize()
+    for b in range(2):
+        assert rel_err(synth.as_f64(g)[b], oracle_gram(X64[b])) <= _tol(cdt)
+        assert rel_err(synth.as_f64(s)[b], oracle_standard(X64[b])) <= _tol(cdt)
+
+
+def test_single_selected_row():
+    gns = need_gpu()
+    X, X64 = _inputs(1, 50, 90, "f32", seed=18)
+    ri = torch.tensor([[7]], dtype=torch.int64)
+    say("k = 1")
+    out = gns.gram_ns_batched(X.cuda(), NS5, row_idx=ri.cuda())
+    torch.cuda.synchronize()
+    assert rel_err(synth.as_f64(out)[0][[7]], oracle_gram(X64[0][[7]])) <= TOL_F32
+
+
+def test_zero_matrix_gives_zero():
+    gns = need_gpu()
+    X = torch.zeros(2, 64, 200, dtype=torch.bfloat16, device="cuda")
+    say("zero matrix")
+    g = gns.gram_ns_batched(X, NS5)
+    s = gns.standard_ns_batched(X, NS5)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g).item() == 0 and torch.count_nonzero(s).item() == 0
+
+
+def test_batch_zero_is_noop():
+    gns = need_gpu()
+    X = torch.empty(0, 16, 32, dtype=torch.bfloat16, device="cuda")
+    out = gns.gram_ns_batched(X, NS5)
+    assert out.shape == (0, 16, 32)
+
+
+def test_deterministic_and_inplace():
+    gns = need_gpu()
+    X, _ = _inputs(3, 300, 700, "bf16", seed=19)
+    Xd = X.cuda()
+    say("determinism")
+    a = gns.gram_ns_batched(Xd, NS5)
+    b = gns.gram_ns_batched(Xd, NS5)
+    c = Xd.clone()
+    gns.gram_ns_batched(c, NS5, out=c)          # out aliases X
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+
+
+def test_output_guard_band():
+    """Nothing is written outside out, and the workspace's leftovers from a
+    bigger problem do not leak into a smaller one."""
+    gns = need_gpu()
+    B, n, m = 2, 200, 450
+    X, X64 = _inputs(B, n, m, "bf16", seed=20)
+    pad = 4096
+    buf = torch.full((B * n * m + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + B * n * m].view(B, n, m)
+    ws = torch.full((gns.gram_workspace_bytes(torch.bfloat16, 4, 400, 900),), 0x7f,
+                    dtype=torch.uint8, device="cuda")
+    say("guard band")
+    gns.gram_ns_batched(X.cuda(), NS5, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[-pad:]).all()
+    assert not torch.isnan(out).any()
+    ref = np.stack([oracle_gram(X64[b]) for b in range(B)])
+    assert max(per_matrix_rel(synth.as_f64(out), ref)) <= TOL_HALF
+
+
+def test_check_row_idx():
+    gns = need_gpu()
+    good = torch.tensor([[0, 5, 3], [9, 1, 2]], dtype=torch.int64, device="cuda")
+    oob = torch.tensor([[0, 5, 3], [9, 10, 2]], dtype=torch.int64, device="cuda")
+    dup = torch.tensor([[0, 5, 5], [9, 1, 2]], dtype=torch.int64, device="cuda")
+    assert gns.check_row_idx(good, 10) == 0
+    assert gns.check_row_idx(oob, 10) == 1
+    assert gns.check_row_idx(dup, 10) == 2
+
+
+def test_out_of_range_rows_touch_nothing():
+    """A bad index reads as a zero row and is not written (no stray access)."""
+    gns = need_gpu()
+    X, _ = _inputs(1, 20, 40, "f32", seed=21)
+    out = torch.zeros(1, 20, 40, device="cuda")
+    ri = torch.tensor([[3, 25, 4]], dtype=torch.int64, device="cuda")
+    gns.gram_ns_batched(X.cuda(), NS5, row_idx=ri, out=out)
+    torch.cuda.synchronize()
+    keep = [i for i in range(20) if i not in (3, 4)]
+    assert torch.count_nonzero(out[0, keep]).item() == 0
+    assert torch.isfinite(out).all()
