@@ -306,6 +306,36 @@ gns_status workspace_checks(const void *X, const void *out, int64_t batch, int64
   return GNS_OK;
 }
 
+// Standard Newton-Schulz (Dion3 §2.2, Algorithm 1) on a validated problem;
+// the symmetric products go through the mirrored kernel (Appendix C.3).
+gns_status enqueue_standard(const Plan &pl, int cdt, int64_t batch, const void *X, void *out,
+                            int io, int64_t n, const double *coeffs, int T,
+                            const int64_t *row_idx, void *workspace, hipStream_t stream) {
+  Ctx c{&pl, cdt, batch, static_cast<unsigned char *>(workspace), stream};
+  void *A = c.sq(0), *B = c.sq(1);
+  void *XT[2] = {c.ws + pl.off_xt0, c.ws + pl.off_xt1};
+  int xcur = 0;
+  const double nn = static_cast<double>(pl.rows);
+  gns_status st;
+  if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
+  for (int t = 1; t <= T; ++t) {
+    const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);
+    const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
+    const float cc = static_cast<float>(coeffs[3 * (t - 1) + 2]);
+    if ((st = syrk(c, A)) != GNS_OK) return st;                                   // A = X X^T
+    st = symm(c, A, A, cc, b, A, B, nullptr, 0.0f, 0.0f, "std_poly", nn * nn * nn);  // B = bA + cA^2
+    if (st != GNS_OK) return st;
+    if (t < T) {
+      st = apply(c, B, XT[xcur], XT[xcur ^ 1], a, false, nullptr, io, n, nullptr, "std_apply");
+      xcur ^= 1;
+    } else {
+      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, n, row_idx, "std_final_apply");
+    }
+    if (st != GNS_OK) return st;
+  }
+  return GNS_OK;
+}
+
 }  // namespace
 
 // ==========================================================================
@@ -353,7 +383,8 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
   if (st != GNS_OK) return st;
   int tile_req = 0;
-  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA, &tile_req)) != GNS_OK) return st;
+  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
+    return st;
   if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
   std::vector<char> restart_at(T + 2, 0);
   for (int i = 0; i < n_restart; ++i) {
@@ -366,6 +397,12 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;
   st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
   if (st != GNS_OK) return st;
+  // Square matrices: both algorithms cost the same and standard NS needs
+  // fewer launches and never forms X X^T of an ill-conditioned square
+  // matrix, so the pages fall back to it (Dion3 §4.1, last paragraph).
+  if (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK))
+    return enqueue_standard(pl, static_cast<int>(cdt), batch, X, out, io, n, coeffs, T, row_idx,
+                            workspace, static_cast<hipStream_t>(stream));
 
   const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
   Ctx c{&pl, static_cast<int>(cdt), batch, static_cast<unsigned char *>(workspace),
@@ -449,29 +486,8 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
   if (!make_plan(cdt, batch, rows, m, 2, tile_req, &pl)) return GNS_E_SHAPE;
   st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
   if (st != GNS_OK) return st;
-  Ctx c{&pl, static_cast<int>(cdt), batch, static_cast<unsigned char *>(workspace),
-        static_cast<hipStream_t>(stream)};
-  void *A = c.sq(0), *B = c.sq(1);
-  void *XT[2] = {c.ws + pl.off_xt0, c.ws + pl.off_xt1};
-  int xcur = 0;
-  const double nn = static_cast<double>(rows);
-  if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
-  for (int t = 1; t <= T; ++t) {
-    const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);
-    const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
-    const float cc = static_cast<float>(coeffs[3 * (t - 1) + 2]);
-    if ((st = syrk(c, A)) != GNS_OK) return st;                                   // A = X X^T
-    st = symm(c, A, A, cc, b, A, B, nullptr, 0.0f, 0.0f, "std_poly", nn * nn * nn);  // B = bA + cA^2
-    if (st != GNS_OK) return st;
-    if (t < T) {
-      st = apply(c, B, XT[xcur], XT[xcur ^ 1], a, false, nullptr, io, n, nullptr, "std_apply");
-      xcur ^= 1;
-    } else {
-      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, n, row_idx, "std_final_apply");
-    }
-    if (st != GNS_OK) return st;
-  }
-  return GNS_OK;
+  return enqueue_standard(pl, cdt, batch, X, out, io, n, coeffs, T, row_idx, workspace,
+                          static_cast<hipStream_t>(stream));
 }
 
 gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,

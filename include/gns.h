@@ -78,6 +78,10 @@ typedef enum {
                                       Q <- QZ, R <- ZRZ (default: Algorithm 3's
                                       reformulation with explicit a-terms,
                                       Dion3 Appendix B.2.3); gns_gram_batched only */
+#define GNS_OPT_NO_SQUARE_FALLBACK 0x2u /* run Gram NS even when the orthogonalised
+                                      matrix is square (by default a square
+                                      problem runs standard NS, which costs the
+                                      same there, Dion3 §4.1); gns_gram_batched only */
 #define GNS_OPT_TILE_128 0x10u     /* force 128 x 128 output tiles            */
 #define GNS_OPT_TILE_256 0x20u     /* force 256 x 256 output tiles            */
 /* Without a TILE bit the library picks the tile edge from the problem size.

@@ -159,6 +159,24 @@ def test_edge_shapes(shape, cdt):
         assert rel_err(synth.as_f64(s)[b], oracle_standard(X64[b])) <= _tol(cdt)
 
 
+@pytest.mark.parametrize("cdt,tol", [("f16", TOL_HALF), ("f32", TOL_F32), ("bf16", 0.15)])
+def test_square_without_fallback(cdt, tol):
+    """Gram NS forced on square matrices.  Forming X X^T squares the condition
+    number of a square Gaussian, so bf16 products lose several percent (a CPU
+    model of the same rounding points gives 0.06-0.08) while fp16 and fp32
+    stay within their bounds; this is why square problems default to
+    standard NS."""
+    gns = need_gpu()
+    io = "f32" if cdt == "f32" else "bf16"
+    X, X64 = _inputs(2, 130, 130, io, seed=17)
+    say(f"square no fallback {cdt}")
+    g = gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=DT[cdt], square_fallback=False)
+    torch.cuda.synchronize()
+    errs = [rel_err(synth.as_f64(g)[b], oracle_gram(X64[b])) for b in range(2)]
+    say("  rel errs", errs)
+    assert max(errs) <= tol
+
+
 def test_single_selected_row():
     gns = need_gpu()
     X, X64 = _inputs(1, 50, 90, "f32", seed=18)
