@@ -62,12 +62,16 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
                Plan *pl) {
   if (!valid_dtype(cdt) || batch < 0 || rows < 1 || m < rows) return false;
   pl->tile = tile_request ? tile_request : choose_tile(cdt, batch, rows);
+  if (cdt == GNS_F32) pl->tile = 128;   // the fp32 kernels exist for 128-edge tiles only
   pl->rows = rows;
   pl->m = m;
   pl->Np = round_up(rows, pl->tile);
   pl->Mp = round_up(m, pl->tile);
   // per-matrix element offsets stay within int range of the kernels' math
   if (pl->Np * pl->Mp > (int64_t(1) << 31)) return false;
+  // operand panels (256 rows of a padded buffer) are addressed with 32-bit
+  // buffer offsets
+  if (int64_t(256) * std::max(pl->Np, pl->Mp) * gns::dtype_size(cdt) >= (int64_t(1) << 31)) return false;
   pl->parts = choose_parts(batch, rows);
   pl->esz = gns::dtype_size(cdt);
   size_t off = 0;
@@ -147,6 +151,19 @@ struct Ctx {
   int64_t rect_stride() const { return pl->Np * pl->Mp; }
 };
 
+// alpha * (A B^T) + beta * D is evaluated as alpha * (A B^T + (beta/alpha) D);
+// with alpha = 0 the product is skipped (K = 0) and the result is beta * D.
+void set_scale(GemmParams *p, float alpha, float beta) {
+  if (alpha != 0.0f) {
+    p->alpha = alpha;
+    p->init_scale = beta / alpha;
+  } else {
+    p->alpha = 1.0f;
+    p->init_scale = beta;
+    p->K = 0;
+  }
+}
+
 GemmParams base_params(const Ctx &c) {
   GemmParams p;
   std::memset(&p, 0, sizeof(p));
@@ -167,8 +184,8 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.K = static_cast<int>(N);
   p.tiles_m = p.tiles_n = nt;
   p.tiles_per_mat = nt * (nt + 1) / 2;
-  p.alpha = alpha; p.beta = beta;
-  p.D = D; p.ldd = N; p.sD = c.sq_stride();
+  set_scale(&p, alpha, beta);
+  if (D) { p.DT = D; p.lddt = N; p.sDT = c.sq_stride(); }   // D is symmetric
   p.C = C; p.ldc = N; p.sC = c.sq_stride();
   p.C2 = C2; p.sC2 = c.sq_stride();
   p.diag1 = diag1; p.diag2 = diag2;
@@ -216,8 +233,9 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   p.K = static_cast<int>(N);
   p.tiles_m = tm; p.tiles_n = tn;
   p.tiles_per_mat = tm * tn;
-  p.beta = beta;
-  if (beta != 0.0f) { p.D = Xh; p.ldd = M; p.sD = c.rect_stride(); }
+  set_scale(&p, 1.0f, beta);
+  // the beta term reads X through its transposed copy, the B operand
+  if (beta != 0.0f) { p.DT = XT_in; p.lddt = N; p.sDT = c.rect_stride(); }
   const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
   double bytes = c.batch * (n * n + n * m) * c.pl->esz;
   if (final) {

@@ -20,7 +20,8 @@ enum GemmMode : int {
   MODE_FINAL = 2  // general result converted into the caller's output
 };
 
-// C = alpha * (A . B^T) + beta * D over a batch, A and B row-major with the
+// C = alpha * (A . B^T) + beta * D over a batch (computed as
+// alpha * (A . B^T + (beta/alpha) D), or with K = 0 when alpha = 0), A and B row-major with the
 // contraction index contiguous.  All internal buffers are padded to whole
 // tiles and zero-filled there, so the kernel needs no bounds checks except
 // for the caller's output in MODE_FINAL.
@@ -31,8 +32,10 @@ struct GemmParams {
   int tiles_m, tiles_n;             // output tiles per matrix along rows / cols
   int tiles_per_mat;                // sym: tiles_m*(tiles_m+1)/2
   int batch;
-  float alpha, beta;
-  const void *D; int64_t ldd, sD;   // beta term (same layout as C); may be null
+  float alpha;                      // C = alpha * (acc)
+  float init_scale;                 // acc starts at init_scale * D
+  const void *DT; int64_t lddt, sDT;  // D read transposed: D(i,j) = DT[j*lddt + i];
+                                      // may be null (D = 0)
   void *C; int64_t ldc, sC;
   void *C2; int64_t sC2;            // MODE_SYM second output (ld = ldc); may be null
   float diag1, diag2;               // MODE_SYM: added to C / C2 on the diagonal

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gns_kernels.h"
 
 namespace gns {
@@ -81,6 +83,7 @@ struct Mma;
 
 template <>
 struct Mma<EBF16> {
+  static constexpr int kInstr = 1;
   typedef u32x4 Frag;
   __device__ static __forceinline__ Frag load(const unsigned char *row, int s, int h, int sw) {
     return *reinterpret_cast<const u32x4 *>(row + (((2 * s + h) ^ sw) << 4));
@@ -92,6 +95,7 @@ struct Mma<EBF16> {
 };
 template <>
 struct Mma<EF16> {
+  static constexpr int kInstr = 1;
   typedef u32x4 Frag;
   __device__ static __forceinline__ Frag load(const unsigned char *row, int s, int h, int sw) {
     return *reinterpret_cast<const u32x4 *>(row + (((2 * s + h) ^ sw) << 4));
@@ -103,6 +107,7 @@ struct Mma<EF16> {
 };
 template <>
 struct Mma<EF32> {
+  static constexpr int kInstr = 8;
   struct Frag {
     u32x4 lo, hi;
   };
@@ -133,28 +138,54 @@ __device__ __forceinline__ void store_out(void *base, int64_t idx, int dt, float
   }
 }
 
-// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: rows r and
-// r' within any aligned group of 8 (and the even / odd rows of any aligned
-// group of 16) land on different banks for the column-wise fragment reads.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row.  Fragment
+// reads take one chunk from each of 32 consecutive rows; with this swizzle
+// the rows that share a bank window (r, r+2, r+4, r+6 for 32 banks; r, r+4,
+// r+8, r+12 for 64 banks) always use four different chunks.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
 // ---------------------------------------------------------------------------
 // NT product with fused epilogues
 // ---------------------------------------------------------------------------
+// Wave layout per tile edge: 256 -> 8 waves (two per SIMD) in a 4 x 2 grid of
+// 64 x 128 wave tiles; 128 -> 4 waves in a 2 x 2 grid of 64 x 64.  Two waves
+// per SIMD let one wave's MFMAs run while the other waits on LDS or memory.
+template <int TILE>
+struct WaveLayout {
+  static constexpr int WGM = TILE == 256 ? 4 : 2;   // wave rows
+  static constexpr int WGN = 2;                     // wave columns
+  static constexpr int THREADS = 64 * WGM * WGN;
+};
+
 template <class E, int TILE, int MODE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(WaveLayout<TILE>::THREADS)
 gemm_nt(GemmParams p) {
   using S = typename E::S;
   constexpr int ESZ = sizeof(S);
-  constexpr int BKE = 128 / ESZ;          // contraction elements per K step
-  constexpr int SUB = BKE / 16;           // 16-deep slices per K step
-  constexpr int CPF = (8 * ESZ) / 16;     // 16-byte chunks per lane fragment
-  constexpr int WT = TILE / 2;            // wave tile edge
-  constexpr int NB = WT / 32;             // 32x32 blocks per wave edge
-  constexpr int LOADS = TILE / 32;        // 16-byte chunks per thread per operand
-  constexpr int OPB = TILE * 128;         // bytes of one operand buffer
+  constexpr int SB = 64;                  // bytes of one row of one K stage
+  constexpr int BKE = SB / ESZ;           // contraction elements per stage
+  constexpr int SUB = BKE / 16;           // 16-deep slices per stage (2, or 1 for fp32)
+  constexpr int WGM = WaveLayout<TILE>::WGM;
+  constexpr int WGN = WaveLayout<TILE>::WGN;
+  constexpr int NT = WaveLayout<TILE>::THREADS;
+  constexpr int WTM = TILE / WGM;         // wave tile rows
+  constexpr int WTN = TILE / WGN;         // wave tile columns
+  constexpr int NBI = WTM / 32;           // 32x32 blocks per wave, rows
+  constexpr int NBJ = WTN / 32;           // 32x32 blocks per wave, columns
+  constexpr int RPP = NT / 4;             // rows staged per pass (4 chunks per row)
+  constexpr int LOADS = TILE / RPP;       // 16-byte chunks per thread per operand per stage
+  constexpr int OPB = TILE * SB;          // bytes of one operand in one stage
+  constexpr int NST = 3;                  // LDS ring depth (stages)
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * OPB];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * 2 * OPB];
 
   // Workgroup -> tile.  Consecutive tiles share an operand panel; the
   // hardware deals workgroups round-robin over the 8 XCDs, so regroup ids to
@@ -180,8 +211,8 @@ gemm_nt(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = (wave >> 1) * WT;
-  const int wc = (wave & 1) * WT;
+  const int wr = (wave / WGN) * WTM;
+  const int wc = (wave % WGN) * WTN;
 
   const unsigned char *Ag = static_cast<const unsigned char *>(p.A) +
                             (static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda) * ESZ;
@@ -190,75 +221,156 @@ gemm_nt(GemmParams p) {
   const int64_t ldaB = p.lda * ESZ;
   const int64_t ldbB = p.ldb * ESZ;
 
-  // global -> register -> LDS staging coordinates
-  const int lrow0 = tid >> 3;
-  const int lch = tid & 7;
-  const int wofs = lrow0 * 128 + ((lch ^ swz(lrow0)) << 4);  // + q * 32 rows * 128 B
-  const int64_t gA0 = lrow0 * ldaB + lch * 16;
-  const int64_t gB0 = lrow0 * ldbB + lch * 16;
+  // global -> register -> LDS staging coordinates: thread t moves 16-byte
+  // chunk (t & 3) of rows (t >> 2) + RPP q of each operand
+  const int lrow0 = tid >> 2;
+  const int lch = tid & 3;
+  const int wofs = lrow0 * SB + ((lch ^ swz(lrow0)) << 4);  // + q * RPP rows * SB
+
+  // Buffer resources over this tile's A and B panels: one VGPR offset per
+  // lane, the row-block and K offsets as uniform SGPR offsets, and a
+  // hardware range check (loads past the panel return zeros).
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(Ag), 0, static_cast<int>(TILE * ldaB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(Bg), 0, static_cast<int>(TILE * ldbB), 0x00020000);
+  const int vA = lrow0 * static_cast<int>(ldaB) + lch * 16;
+  const int vB = lrow0 * static_cast<int>(ldbB) + lch * 16;
+  const int sA64 = RPP * static_cast<int>(ldaB);
+  const int sB64 = RPP * static_cast<int>(ldbB);
 
   // fragment read coordinates: block b of a wave covers rows wr/wc + b*32 + lane%32
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int fsw = swz(lr);
 
-  f32x16_t acc[NB][NB];
+  // Accumulators start at (beta/alpha) * D so that the epilogue is a plain
+  // scale-and-store.  D is read through its transposed copy DT (D itself
+  // for symmetric D), where the four rows held by a lane are contiguous.
+  f32x16_t acc[NBI][NBJ];
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i = 0; i < NBI; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (p.DT) {
+    const S *DTm = static_cast<const S *>(p.DT) + static_cast<int64_t>(mat) * p.sDT;
+    const int64_t i_base = static_cast<int64_t>(ti) * TILE + wr + 4 * lh;
+    const int64_t j_base = static_cast<int64_t>(tj) * TILE + wc + lr;
+#pragma unroll
+    for (int i = 0; i < NBI; ++i)
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const S *src = DTm + (j_base + j * 32) * p.lddt + i_base + i * 32 + 8 * g;
+          float v[4];
+          if constexpr (ESZ == 2) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(src);
+            v[0] = E::ld(static_cast<S>(u.x & 0xffffu));
+            v[1] = E::ld(static_cast<S>(u.x >> 16));
+            v[2] = E::ld(static_cast<S>(u.y & 0xffffu));
+            v[3] = E::ld(static_cast<S>(u.y >> 16));
+          } else {
+            const float4 u = *reinterpret_cast<const float4 *>(src);
+            v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = p.init_scale * v[q];
+        }
+  }
 
+  // Main loop over K stages of 64 bytes per row, three stages resident in
+  // LDS.  Iteration i multiplies stage i; during it the global loads of
+  // stage i+3 are issued into one register staging set, the other set
+  // (stage i+2, loaded one iteration earlier) is written to LDS, and the
+  // fragments of the next slice (stage i+1 slice 0 in the last slice) are
+  // read from LDS.  Every fragment read therefore targets a stage that was
+  // completed before the previous barrier, so no wave ever waits for LDS
+  // data right after a barrier: with one wave per SIMD any such wait would
+  // idle the matrix core.
   const int nk = p.K / BKE;
-  u32x4 ra[LOADS], rb[LOADS];
+  if (nk > 0) {
+    using Frag = typename Mma<E>::Frag;
+    u32x4 st[2][2 * LOADS];                 // [set][A chunks, then B chunks]
+    auto gload = [&](int set, int stage) {
+      const int kb = (stage < nk ? stage : nk - 1) * SB;
 #pragma unroll
-  for (int q = 0; q < LOADS; ++q) {
-    ra[q] = *reinterpret_cast<const u32x4 *>(Ag + gA0 + q * 32 * ldaB);
-    rb[q] = *reinterpret_cast<const u32x4 *>(Bg + gB0 + q * 32 * ldbB);
-  }
+      for (int q = 0; q < LOADS; ++q) {
+        st[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rA, vA, q * sA64 + kb, 0);
+        st[set][LOADS + q] = __builtin_amdgcn_raw_buffer_load_b128(rB, vB, q * sB64 + kb, 0);
+      }
+    };
+    auto swrite = [&](int set, int buf) {
+      unsigned char *wa = lds + buf * 2 * OPB;
 #pragma unroll
-  for (int q = 0; q < LOADS; ++q) {
-    *reinterpret_cast<u32x4 *>(lds + wofs + q * 32 * 128) = ra[q];
-    *reinterpret_cast<u32x4 *>(lds + OPB + wofs + q * 32 * 128) = rb[q];
-  }
-  __syncthreads();
+      for (int q = 0; q < LOADS; ++q) {
+        *reinterpret_cast<u32x4 *>(wa + wofs + q * RPP * SB) = st[set][q];
+        *reinterpret_cast<u32x4 *>(wa + OPB + wofs + q * RPP * SB) = st[set][LOADS + q];
+      }
+    };
+    Frag fa[2][NBI], fb[2][NBJ];
+    auto fload = [&](int slot, int buf, int sub) {
+      const unsigned char *la = lds + buf * 2 * OPB;
+#pragma unroll
+      for (int b = 0; b < NBI; ++b) fa[slot][b] = Mma<E>::load(la + (wr + b * 32 + lr) * SB, sub, lh, fsw);
+#pragma unroll
+      for (int b = 0; b < NBJ; ++b) fb[slot][b] = Mma<E>::load(la + OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
+    };
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t kb = static_cast<int64_t>(kt + 1) * 128;
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q) {
-        ra[q] = *reinterpret_cast<const u32x4 *>(Ag + gA0 + q * 32 * ldaB + kb);
-        rb[q] = *reinterpret_cast<const u32x4 *>(Bg + gB0 + q * 32 * ldbB + kb);
-      }
-    }
-    const unsigned char *la = lds + cur * 2 * OPB;
-    const unsigned char *lb = la + OPB;
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      typename Mma<E>::Frag fa[NB], fb[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        fa[b] = Mma<E>::load(la + (wr + b * 32 + lr) * 128, s, lh, fsw);
-        fb[b] = Mma<E>::load(lb + (wc + b * 32 + lr) * 128, s, lh, fsw);
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = Mma<E>::run(fa[i], fb[j], acc[i][j]);
-    }
-    if (more) {
-      unsigned char *wa = lds + (cur ^ 1) * 2 * OPB;
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q) {
-        *reinterpret_cast<u32x4 *>(wa + wofs + q * 32 * 128) = ra[q];
-        *reinterpret_cast<u32x4 *>(wa + OPB + wofs + q * 32 * 128) = rb[q];
-      }
-    }
+    // prologue: stages 0 and 1 resident, stage 2 in flight, slice (0,0) in registers
+    gload(0, 0);
+    gload(1, 1);
+    swrite(0, 0);
+    swrite(1, 1);
     __syncthreads();
+    gload(0, 2);
+    fload(0, 0, 0);
+
+    // one iteration; the staging set is a compile-time constant (the loop
+    // below is unrolled by two) so that the staging registers stay registers
+    int buf = 0;                            // buffer of stage i
+    auto iteration = [&](int i, auto slc) {
+      constexpr int sl = decltype(slc)::value;   // staging set holding stage i+2
+      const int bnext = buf == NST - 1 ? 0 : buf + 1;        // stage i+1
+      const int bwrite = bnext == NST - 1 ? 0 : bnext + 1;   // stage i+2
+      gload(sl ^ 1, i + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, SUB>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int cur = s & 1;          // fragment slot of this slice
+        if constexpr (s + 1 < SUB) {
+          fload(cur ^ 1, buf, s + 1);
+        } else {
+          // last slice: next fragments come from stage i+1; stage i+2 goes
+          // from registers to LDS behind this slice's MFMAs
+          fload(cur ^ 1, bnext, 0);
+          swrite(sl, bwrite);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ii = 0; ii < NBI; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < NBJ; ++jj) acc[ii][jj] = Mma<E>::run(fa[cur][ii], fb[cur][jj], acc[ii][jj]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr ((SUB & 1) == 1) {
+        // an odd number of slices leaves the next fragments in slot 1
+#pragma unroll
+        for (int b = 0; b < NBI; ++b) fa[0][b] = fa[1][b];
+#pragma unroll
+        for (int b = 0; b < NBJ; ++b) fb[0][b] = fb[1][b];
+      }
+      __syncthreads();
+      buf = bnext;
+    };
+    int i = 0;
+    for (; i + 1 < nk; i += 2) {
+      iteration(i, std::integral_constant<int, 0>{});
+      iteration(i + 1, std::integral_constant<int, 1>{});
+    }
+    if (i < nk) iteration(i, std::integral_constant<int, 0>{});
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -266,26 +378,22 @@ gemm_nt(GemmParams p) {
   // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its block.
   const int64_t row_base = static_cast<int64_t>(ti) * TILE + wr;
   const int64_t col_base = static_cast<int64_t>(tj) * TILE + wc;
-  const S *Dm = p.D ? static_cast<const S *>(p.D) + static_cast<int64_t>(mat) * p.sD : nullptr;
 
   if (MODE == MODE_SYM) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *C2m = p.C2 ? static_cast<S *>(p.C2) + static_cast<int64_t>(mat) * p.sC2 : nullptr;
     const bool diag_tile = (ti == tj);
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
+    for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb)
+      for (int jb = 0; jb < NBJ; ++jb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
           const int64_t j = col_base + jb * 32 + lr;
           float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] = p.alpha * acc[ib][jb][4 * g + q];
-            if (Dm) v[q] += p.beta * E::ld(Dm[(i0 + q) * p.ldd + j]);
-          }
+          for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[ib][jb][4 * g + q];
           if (!diag_tile) {
             S sv[4];
 #pragma unroll
@@ -329,9 +437,9 @@ gemm_nt(GemmParams p) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *CTm = p.CT ? static_cast<S *>(p.CT) + static_cast<int64_t>(mat) * p.sCT : nullptr;
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
+    for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb)
+      for (int jb = 0; jb < NBJ; ++jb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
@@ -341,7 +449,6 @@ gemm_nt(GemmParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[q] = p.alpha * acc[ib][jb][4 * g + q];
-            if (Dm) v[q] += p.beta * E::ld(Dm[(i0 + q) * p.ldd + j]);
             sv[q] = E::st(v[q]);
             Cm[(i0 + q) * p.ldc + j] = sv[q];
           }
@@ -360,9 +467,9 @@ gemm_nt(GemmParams p) {
     const int64_t *ridx = p.row_idx ? p.row_idx + static_cast<int64_t>(mat) * p.rows_eff : nullptr;
     const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
+    for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb)
+      for (int jb = 0; jb < NBJ; ++jb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
@@ -372,8 +479,7 @@ gemm_nt(GemmParams p) {
           for (int q = 0; q < 4; ++q) {
             const int64_t i = i0 + q;
             if (i >= p.rows_eff) continue;
-            float v = p.alpha * acc[ib][jb][4 * g + q];
-            if (Dm) v += p.beta * E::ld(Dm[i * p.ldd + j]);
+            const float v = p.alpha * acc[ib][jb][4 * g + q];
             const int64_t row = ridx ? ridx[i] : i;
             if (row < 0 || row >= p.out_rows) continue;
             store_out(p.out, obase + row * p.out_cols + j, p.out_dtype, v);
@@ -519,10 +625,11 @@ template <class E, int TILE>
 static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
   const int grid = p.tiles_per_mat * p.batch;
   if (grid <= 0) return hipSuccess;
+  constexpr int nt = WaveLayout<TILE>::THREADS;
   switch (mode) {
-    case MODE_SYM: gemm_nt<E, TILE, MODE_SYM><<<grid, 256, 0, s>>>(p); break;
-    case MODE_GEN: gemm_nt<E, TILE, MODE_GEN><<<grid, 256, 0, s>>>(p); break;
-    default: gemm_nt<E, TILE, MODE_FINAL><<<grid, 256, 0, s>>>(p); break;
+    case MODE_SYM: gemm_nt<E, TILE, MODE_SYM><<<grid, nt, 0, s>>>(p); break;
+    case MODE_GEN: gemm_nt<E, TILE, MODE_GEN><<<grid, nt, 0, s>>>(p); break;
+    default: gemm_nt<E, TILE, MODE_FINAL><<<grid, nt, 0, s>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -530,13 +637,13 @@ static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
 hipError_t launch_gemm(int dt, int tile, int mode, const GemmParams &p, hipStream_t s) {
   if (dt == DT_BF16) return tile == 256 ? launch_gemm_t<EBF16, 256>(mode, p, s) : launch_gemm_t<EBF16, 128>(mode, p, s);
   if (dt == DT_F16) return tile == 256 ? launch_gemm_t<EF16, 256>(mode, p, s) : launch_gemm_t<EF16, 128>(mode, p, s);
-  return tile == 256 ? launch_gemm_t<EF32, 256>(mode, p, s) : launch_gemm_t<EF32, 128>(mode, p, s);
+  return launch_gemm_t<EF32, 128>(mode, p, s);   // fp32 always uses 128-edge tiles
 }
 
 const char *gemm_kernel_name(int dt, int tile, int mode) {
   static const char *names[3][2][3] = {
       {{"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"},
-       {"gemm_nt<f32,256,sym>", "gemm_nt<f32,256,gen>", "gemm_nt<f32,256,final>"}},
+       {"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"}},
       {{"gemm_nt<bf16,128,sym>", "gemm_nt<bf16,128,gen>", "gemm_nt<bf16,128,final>"},
        {"gemm_nt<bf16,256,sym>", "gemm_nt<bf16,256,gen>", "gemm_nt<bf16,256,final>"}},
       {{"gemm_nt<f16,128,sym>", "gemm_nt<f16,128,gen>", "gemm_nt<f16,128,final>"},

@@ -85,7 +85,8 @@ typedef enum {
 #define GNS_OPT_TILE_128 0x10u     /* force 128 x 128 output tiles            */
 #define GNS_OPT_TILE_256 0x20u     /* force 256 x 256 output tiles            */
 /* Without a TILE bit the library picks the tile edge from the problem size.
-   Results are identical up to floating-point summation order either way. */
+   Results are identical up to floating-point summation order either way.
+   fp32 compute always runs 128-edge tiles (GNS_OPT_TILE_256 is ignored). */
 
 /* Version of this ABI (GNS_ABI_VERSION). */
 int gns_abi_version(void);
