@@ -71,6 +71,7 @@ struct EF32 {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // One lane's share of a 16-deep slice of the contraction: 8 consecutive
 // elements (one 16-byte chunk for 16-bit types, two for fp32).  A and B
@@ -180,10 +181,11 @@ gemm_nt(GemmParams p) {
   constexpr int WTN = TILE / WGN;         // wave tile columns
   constexpr int NBI = WTM / 32;           // 32x32 blocks per wave, rows
   constexpr int NBJ = WTN / 32;           // 32x32 blocks per wave, columns
-  constexpr int RPP = NT / 4;             // rows staged per pass (4 chunks per row)
-  constexpr int LOADS = TILE / RPP;       // 16-byte chunks per thread per operand per stage
   constexpr int OPB = TILE * SB;          // bytes of one operand in one stage
-  constexpr int NST = 3;                  // LDS ring depth (stages)
+  constexpr int NST = 5;                  // LDS ring depth (stages)
+  constexpr int NW = NT / 64;             // waves
+  constexpr int BPW = (TILE / 16) / NW;   // 1 KiB LDS blocks per wave per operand per stage
+  static_assert(BPW * NW * 16 == TILE, "blocks must cover the tile");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[NST * 2 * OPB];
 
@@ -221,23 +223,31 @@ gemm_nt(GemmParams p) {
   const int64_t ldaB = p.lda * ESZ;
   const int64_t ldbB = p.ldb * ESZ;
 
-  // global -> register -> LDS staging coordinates: thread t moves 16-byte
-  // chunk (t & 3) of rows (t >> 2) + RPP q of each operand
-  const int lrow0 = tid >> 2;
-  const int lch = tid & 3;
-  const int wofs = lrow0 * SB + ((lch ^ swz(lrow0)) << 4);  // + q * RPP rows * SB
-
-  // Buffer resources over this tile's A and B panels: one VGPR offset per
-  // lane, the row-block and K offsets as uniform SGPR offsets, and a
-  // hardware range check (loads past the panel return zeros).
-  const __amdgpu_buffer_rsrc_t rA =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(Ag), 0, static_cast<int>(TILE * ldaB), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rB =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(Bg), 0, static_cast<int>(TILE * ldbB), 0x00020000);
-  const int vA = lrow0 * static_cast<int>(ldaB) + lch * 16;
-  const int vB = lrow0 * static_cast<int>(ldbB) + lch * 16;
-  const int sA64 = RPP * static_cast<int>(ldaB);
-  const int sB64 = RPP * static_cast<int>(ldbB);
+  // Operands move from HBM/L2 straight into LDS with the LDS-DMA form of the
+  // buffer load: one instruction fills 1 KiB (16 rows x 64 bytes) of a stage,
+  // lane l writing bytes 16 l .. 16 l + 15.  Lane l therefore fetches row
+  // l / 4 of its block and the logical chunk that the swizzle places at
+  // physical chunk l % 4.  Wave w fills blocks w, w + NW, ... of each operand.
+  const int dma_row = lane >> 2;
+  const int dma_chunk = (lane & 3) ^ swz(dma_row);
+  const int vA = dma_row * static_cast<int>(ldaB) + dma_chunk * 16;
+  const int vB = dma_row * static_cast<int>(ldbB) + dma_chunk * 16;
+  // buffer descriptors over this tile's A and B panels (hardware range check:
+  // loads past the panel return zeros)
+  const uint64_t aBase = reinterpret_cast<uint64_t>(Ag);
+  const uint64_t bBase = reinterpret_cast<uint64_t>(Bg);
+  // (readfirstlane: these values are wave-uniform; the asm needs them in SGPRs)
+  const i32x4 rA = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(aBase))),
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(aBase >> 32) & 0xffff)),
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(TILE * ldaB)), 0x00020000};
+  const i32x4 rB = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(bBase))),
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(bBase >> 32) & 0xffff)),
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(TILE * ldbB)), 0x00020000};
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int ldaB32 = __builtin_amdgcn_readfirstlane(static_cast<int>(ldaB));
+  const int ldbB32 = __builtin_amdgcn_readfirstlane(static_cast<int>(ldbB));
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(lds)));
 
   // fragment read coordinates: block b of a wave covers rows wr/wc + b*32 + lane%32
   const int lr = lane & 31;
@@ -281,33 +291,34 @@ gemm_nt(GemmParams p) {
         }
   }
 
-  // Main loop over K stages of 64 bytes per row, three stages resident in
-  // LDS.  Iteration i multiplies stage i; during it the global loads of
-  // stage i+3 are issued into one register staging set, the other set
-  // (stage i+2, loaded one iteration earlier) is written to LDS, and the
-  // fragments of the next slice (stage i+1 slice 0 in the last slice) are
-  // read from LDS.  Every fragment read therefore targets a stage that was
-  // completed before the previous barrier, so no wave ever waits for LDS
-  // data right after a barrier: with one wave per SIMD any such wait would
-  // idle the matrix core.
+  // Main loop over K stages of 64 bytes per row in an NST-deep LDS ring.
+  // Iteration i multiplies stage i; its last slice already reads the first
+  // fragments of stage i+1, so at the start of every iteration stages i and
+  // i+1 are complete and NST-3 later stages are in flight.  After the
+  // barrier that closes iteration i, the buffer of stage i is refilled with
+  // stage i+NST, which gives each load NST-2 iterations to arrive.  The
+  // loads bypass the compiler's wait bookkeeping (inline assembly), so the
+  // waits are explicit: before the barrier of iteration i every wave waits
+  // until its share of stage i+2 has landed.
   const int nk = p.K / BKE;
   if (nk > 0) {
     using Frag = typename Mma<E>::Frag;
-    u32x4 st[2][2 * LOADS];                 // [set][A chunks, then B chunks]
-    auto gload = [&](int set, int stage) {
-      const int kb = (stage < nk ? stage : nk - 1) * SB;
+    auto dma_stage = [&](int stage) {
+      const int st = stage < nk ? stage : nk - 1;   // past the end: harmless reload
+      const uint32_t buf_lds = lds_base + static_cast<uint32_t>((stage % NST) * 2 * OPB);
 #pragma unroll
-      for (int q = 0; q < LOADS; ++q) {
-        st[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rA, vA, q * sA64 + kb, 0);
-        st[set][LOADS + q] = __builtin_amdgcn_raw_buffer_load_b128(rB, vB, q * sB64 + kb, 0);
-      }
-    };
-    auto swrite = [&](int set, int buf) {
-      unsigned char *wa = lds + buf * 2 * OPB;
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q) {
-        *reinterpret_cast<u32x4 *>(wa + wofs + q * RPP * SB) = st[set][q];
-        *reinterpret_cast<u32x4 *>(wa + OPB + wofs + q * RPP * SB) = st[set][LOADS + q];
+      for (int q = 0; q < BPW; ++q) {
+        const int blk = wave_u + q * NW;
+        const int soA = blk * 16 * ldaB32 + st * SB;
+        const int soB = blk * 16 * ldbB32 + st * SB;
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            :: "s"(buf_lds + blk * 1024), "v"(vA), "s"(rA), "s"(soA) : "memory", "m0");
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            :: "s"(buf_lds + OPB + blk * 1024), "v"(vB), "s"(rB), "s"(soB) : "memory", "m0");
       }
     };
     Frag fa[2][NBI], fb[2][NBJ];
@@ -319,34 +330,24 @@ gemm_nt(GemmParams p) {
       for (int b = 0; b < NBJ; ++b) fb[slot][b] = Mma<E>::load(la + OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
     };
 
-    // prologue: stages 0 and 1 resident, stage 2 in flight, slice (0,0) in registers
-    gload(0, 0);
-    gload(1, 1);
-    swrite(0, 0);
-    swrite(1, 1);
+    // prologue: all NST stages in flight; wait for stages 0 and 1
+#pragma unroll
+    for (int j = 0; j < NST; ++j) dma_stage(j);
+    static_assert(2 * BPW * (NST - 2) < 64, "wait count out of range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 2)) : "memory");
     __syncthreads();
-    gload(0, 2);
     fload(0, 0, 0);
 
-    // one iteration; the staging set is a compile-time constant (the loop
-    // below is unrolled by two) so that the staging registers stay registers
     int buf = 0;                            // buffer of stage i
-    auto iteration = [&](int i, auto slc) {
-      constexpr int sl = decltype(slc)::value;   // staging set holding stage i+2
-      const int bnext = buf == NST - 1 ? 0 : buf + 1;        // stage i+1
-      const int bwrite = bnext == NST - 1 ? 0 : bnext + 1;   // stage i+2
-      gload(sl ^ 1, i + 3);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < nk; ++i) {
+      const int bnext = buf == NST - 1 ? 0 : buf + 1;
       static_for<0, SUB>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
-        constexpr int cur = s & 1;          // fragment slot of this slice
+        constexpr int cur = s & 1;
         if constexpr (s + 1 < SUB) {
           fload(cur ^ 1, buf, s + 1);
         } else {
-          // last slice: next fragments come from stage i+1; stage i+2 goes
-          // from registers to LDS behind this slice's MFMAs
           fload(cur ^ 1, bnext, 0);
-          swrite(sl, bwrite);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -356,21 +357,19 @@ gemm_nt(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
       });
       if constexpr ((SUB & 1) == 1) {
-        // an odd number of slices leaves the next fragments in slot 1
 #pragma unroll
         for (int b = 0; b < NBI; ++b) fa[0][b] = fa[1][b];
 #pragma unroll
         for (int b = 0; b < NBJ; ++b) fb[0][b] = fb[1][b];
       }
+      // stage i+2 must be complete before the barrier; stages i+3 .. i+NST-1
+      // may still be in flight
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 3)) : "memory");
       __syncthreads();
+      dma_stage(i + NST);
       buf = bnext;
-    };
-    int i = 0;
-    for (; i + 1 < nk; i += 2) {
-      iteration(i, std::integral_constant<int, 0>{});
-      iteration(i + 1, std::integral_constant<int, 1>{});
     }
-    if (i < nk) iteration(i, std::integral_constant<int, 0>{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // ---------------------------------------------------------------- epilogue
