@@ -42,6 +42,121 @@ def flops_standard_sym(n, m, T):
     return T * (3.0 * m * n * n + n ** 3)
 
 
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (read the csv files rocprofv3 writes; nothing here runs
+# on the GPU)
+# --------------------------------------------------------------------------
+KERNEL_SRC = os.path.join(ROOT, "gram_newton_schulz_amd", "csrc", "gns_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def short_kernel(name):
+    import re
+    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)>", name)
+    if m:
+        return f"gemm_nt<{m.group(1).lower()},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
+    for k in ("norm_partial", "scale_transpose", "check_rows"):
+        if k in name:
+            return k
+    return name.split("(")[0][:60]
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirname, suffix):
+    for root, _, files in os.walk(dirname):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirname}")
+
+
+def summarize_stats(dirname):
+    rows = _csv(_find(dirname, "kernel_stats.csv"))
+    print(f"{'kernel':34s} {'calls':>6s} {'total_ms':>10s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in rows:
+        name = short_kernel(r["Name"])
+        print(f"{name:34s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+              f"{float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
+              f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
+
+
+def _pmc_per_dispatch(dirname, counter):
+    out = {}
+    for r in _csv(_find(dirname, "counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        d = out.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"], "v": 0.0})
+        d["v"] += float(r["Counter_Value"])
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, calib_mib):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scaled by the
+    reading of the calibration copy (a device copy of calib_mib MiB, which
+    reads and writes exactly that many bytes)."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    def first(d, pred):
+        for k in sorted(d):
+            if pred(d[k]["kernel"]):
+                return d[k]["v"]
+        return None
+    fs = ws = 1.0
+    if calib_mib:
+        is_copy = lambda k: "copy" in k.lower()
+        cf, cw = first(fetch, is_copy), first(write, is_copy)
+        if cf and cw:
+            fs, ws = calib_mib * 1024.0 / cf, calib_mib * 1024.0 / cw
+    print(f"calibration copy {calib_mib} MiB: fetch scale {fs:.4f}, write scale {ws:.4f}")
+    agg = {}
+    for src, key, scale in ((fetch, "fetch", fs), (write, "write", ws)):
+        for d in src.values():
+            name = short_kernel(d["kernel"])
+            if not (name.startswith("gemm_nt") or name in ("norm_partial", "scale_transpose")):
+                continue
+            a = agg.setdefault(name, {"fetch": [], "write": []})
+            a[key].append(d["v"] * 1024.0 * scale)
+    print(f"{'kernel':34s} {'launches':>8s} {'fetch_MiB/launch':>17s} {'write_MiB/launch':>17s}")
+    for name, a in sorted(agg.items()):
+        nf = max(len(a["fetch"]), 1)
+        nw = max(len(a["write"]), 1)
+        f_avg = sum(a["fetch"]) / nf
+        w_avg = sum(a["write"]) / nw
+        print(f"{name:34s} {nf:8d} {f_avg / 2 ** 20:17.1f} {w_avg / 2 ** 20:17.1f}")
+        print("TRAFFIC " + json.dumps({"kernel": name, "bytes_per_launch": f_avg + w_avg,
+                                        "fetch_bytes": f_avg, "write_bytes": w_avg,
+                                        "source_sha256_16": kernel_source_hash()}))
+
+
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` recorded in profiles/ by
+    --summarize-pmc, or None when absent or taken on a different kernel source."""
+    try:
+        names = [n for n in os.listdir(PROFILES) if n.endswith(".txt")]
+    except FileNotFoundError:
+        return None
+    h = kernel_source_hash()
+    for n in names:
+        with open(os.path.join(PROFILES, n)) as f:
+            for line in f:
+                if line.startswith("TRAFFIC "):
+                    rec = json.loads(line[len("TRAFFIC "):])
+                    if rec.get("kernel") == kernel and rec.get("source_sha256_16") == h:
+                        return round(rec["bytes_per_launch"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -51,7 +166,20 @@ def main():
     ap.add_argument("--compute", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--no-standard", action="store_true", help="skip the standard-NS comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a known-size "
+                         "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="print a summary of a rocprofv3 --kernel-trace --stats csv directory and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print per-kernel HBM traffic from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, calib_mib=args.calib_copy_mib)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -66,6 +194,13 @@ def main():
     from gram_newton_schulz_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")   # contents irrelevant
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     coeffs = synth.NS5_MUON
     T, restarts = 5, (2,)
@@ -146,7 +281,7 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(dom_tflops / peak, 4),
-        "traffic": None,
+        "traffic": traffic_from_profile(dom_name),
         "avg_launch_ms": round(dom_avg_ms, 4),
         "launches_per_step": dom["launches"] / args.steps,
         "share_of_step": round(dom["ms"] / args.steps / ms, 4),

@@ -206,8 +206,15 @@ gemm_nt(GemmParams p) {
     tj = bj;
     ti = t - bj * (bj + 1) / 2;
   } else {
-    ti = t % p.tiles_m;
-    tj = t / p.tiles_m;
+    // grouped raster: runs of 32 consecutive tiles form 4 x 8 blocks, so the
+    // tiles that one XCD runs together touch 4 A panels and 8 B panels
+    constexpr int GM = 4;
+    const int group = t / (GM * p.tiles_n);
+    const int first = group * GM;
+    const int gm = (p.tiles_m - first) < GM ? (p.tiles_m - first) : GM;
+    const int r = t - group * GM * p.tiles_n;
+    ti = first + r % gm;
+    tj = r / gm;
   }
 
   const int tid = threadIdx.x;
@@ -330,44 +337,87 @@ gemm_nt(GemmParams p) {
       for (int b = 0; b < NBJ; ++b) fb[slot][b] = Mma<E>::load(la + OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
     };
 
-    // prologue: all NST stages in flight; wait for stages 0 and 1
+    if constexpr (NW == 8) {
+      // Ping-pong over the two waves of every SIMD.  Every wave runs the same
+      // stream per stage i -- L(i): issue its DMA share of stage i+NST-1 and
+      // read its fragments of stage i; barrier; C(i): the MFMAs of stage i;
+      // barrier -- but waves 4-7 start one barrier later than waves 0-3.
+      // At every barrier the two waves of a SIMD are therefore in opposite
+      // phases: one multiplies while the other reads, and the matrix core
+      // never drains at a barrier.  Stage i+NST-1 goes into the buffer of
+      // stage i-1, which both groups finished reading one barrier earlier;
+      // at the end of L(i) each wave waits for its share of stage i+1, which
+      // the other group reads one barrier later at the earliest.
+      const bool g1 = wave_u >= 4;
+      auto load_stage = [&](int b) {
+        static_for<0, SUB>([&](auto sc) { fload(decltype(sc)::value, b, decltype(sc)::value); });
+      };
+      constexpr int kWait = 2 * BPW * (NST - 2);   // this wave's loads of stages i+2 .. i+NST-1
+      static_assert(kWait < 64, "wait count out of range");
 #pragma unroll
-    for (int j = 0; j < NST; ++j) dma_stage(j);
-    static_assert(2 * BPW * (NST - 2) < 64, "wait count out of range");
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 2)) : "memory");
-    __syncthreads();
-    fload(0, 0, 0);
-
-    int buf = 0;                            // buffer of stage i
-    for (int i = 0; i < nk; ++i) {
-      const int bnext = buf == NST - 1 ? 0 : buf + 1;
-      static_for<0, SUB>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        constexpr int cur = s & 1;
-        if constexpr (s + 1 < SUB) {
-          fload(cur ^ 1, buf, s + 1);
-        } else {
-          fload(cur ^ 1, bnext, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ii = 0; ii < NBI; ++ii)
-#pragma unroll
-          for (int jj = 0; jj < NBJ; ++jj) acc[ii][jj] = Mma<E>::run(fa[cur][ii], fb[cur][jj], acc[ii][jj]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      if constexpr ((SUB & 1) == 1) {
-#pragma unroll
-        for (int b = 0; b < NBI; ++b) fa[0][b] = fa[1][b];
-#pragma unroll
-        for (int b = 0; b < NBJ; ++b) fb[0][b] = fb[1][b];
-      }
-      // stage i+2 must be complete before the barrier; stages i+3 .. i+NST-1
-      // may still be in flight
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 3)) : "memory");
+      for (int j = 0; j < NST - 1; ++j) dma_stage(j);
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 2)) : "memory");
       __syncthreads();
-      dma_stage(i + NST);
-      buf = bnext;
+      if (g1) __syncthreads();
+      int buf = 0;                          // buffer of stage i
+      for (int i = 0; i < nk; ++i) {
+        dma_stage(i + NST - 1);             // into the buffer of stage i-1
+        load_stage(buf);
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
+        __syncthreads();
+        __builtin_amdgcn_s_setprio(1);
+        static_for<0, SUB>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+#pragma unroll
+          for (int ii = 0; ii < NBI; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < NBJ; ++jj) acc[ii][jj] = Mma<E>::run(fa[s][ii], fb[s][jj], acc[ii][jj]);
+        });
+        __builtin_amdgcn_s_setprio(0);
+        __syncthreads();
+        buf = buf == NST - 1 ? 0 : buf + 1;
+      }
+      if (!g1) __syncthreads();
+    } else {
+      // prologue: all NST stages in flight; wait for stages 0 and 1
+  #pragma unroll
+      for (int j = 0; j < NST; ++j) dma_stage(j);
+      static_assert(2 * BPW * (NST - 2) < 64, "wait count out of range");
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 2)) : "memory");
+      __syncthreads();
+      fload(0, 0, 0);
+
+      int buf = 0;                            // buffer of stage i
+      for (int i = 0; i < nk; ++i) {
+        const int bnext = buf == NST - 1 ? 0 : buf + 1;
+        static_for<0, SUB>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          constexpr int cur = s & 1;
+          if constexpr (s + 1 < SUB) {
+            fload(cur ^ 1, buf, s + 1);
+          } else {
+            fload(cur ^ 1, bnext, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int ii = 0; ii < NBI; ++ii)
+  #pragma unroll
+            for (int jj = 0; jj < NBJ; ++jj) acc[ii][jj] = Mma<E>::run(fa[cur][ii], fb[cur][jj], acc[ii][jj]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr ((SUB & 1) == 1) {
+  #pragma unroll
+          for (int b = 0; b < NBI; ++b) fa[0][b] = fa[1][b];
+  #pragma unroll
+          for (int b = 0; b < NBJ; ++b) fb[0][b] = fb[1][b];
+        }
+        // stage i+2 must be complete before the barrier; stages i+3 .. i+NST-1
+        // may still be in flight
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 3)) : "memory");
+        __syncthreads();
+        dma_stage(i + NST);
+        buf = bnext;
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
