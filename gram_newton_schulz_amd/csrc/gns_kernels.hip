@@ -641,6 +641,68 @@ scale_transpose(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int
   }
 }
 
+// Same operation for 16-bit input and compute types with m a multiple of 8:
+// 16-byte loads and stores on every global access (rows of X and X_hat, and
+// 8-row runs of each X^T row), transposed through a padded LDS tile.
+template <class TIn, class TCmp>
+__global__ void __launch_bounds__(256)
+scale_transpose16(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int64_t *row_idx,
+                  const double *partials, int parts, double eps, void *Xh, void *XT, int64_t Np,
+                  int64_t Mp) {
+  static_assert(sizeof(typename TIn::S) == 2 && sizeof(typename TCmp::S) == 2, "16-bit types only");
+  const int b = blockIdx.z;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  __shared__ float inv_s;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // 144-byte rows
+
+  if (threadIdx.x < 64) {  // norm stage 2, same fixed order in every workgroup
+    double sum = 0.0;
+    for (int i = threadIdx.x; i < parts; i += 64) sum += partials[static_cast<int64_t>(b) * parts + i];
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_down(sum, off, 64);
+    if (threadIdx.x == 0) inv_s = static_cast<float>(1.0 / (sqrt(sum) + eps));
+  }
+  __syncthreads();
+  const float inv = inv_s;
+
+  const uint16_t *Xb = static_cast<const uint16_t *>(X) + static_cast<int64_t>(b) * n * m;
+  uint16_t *Xhb = static_cast<uint16_t *>(Xh) + static_cast<int64_t>(b) * Np * Mp;
+  uint16_t *XTb = static_cast<uint16_t *>(XT) + static_cast<int64_t>(b) * Mp * Np;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    const int row = v >> 3;
+    const int cv = (v & 7) * 8;
+    const int64_t gr = r0 + row;
+    const int64_t gc = c0 + cv;
+    u32x4 in = {0u, 0u, 0u, 0u};
+    if (gr < rows_eff && gc < m) {
+      const int64_t src = row_idx ? row_idx[static_cast<int64_t>(b) * rows_eff + gr] : gr;
+      if (src >= 0 && src < n) in = *reinterpret_cast<const u32x4 *>(Xb + src * m + gc);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = TCmp::st(TIn::ld(static_cast<uint16_t>(in[q] & 0xffffu)) * inv);
+      const uint32_t hi = TCmp::st(TIn::ld(static_cast<uint16_t>(in[q] >> 16)) * inv);
+      o[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4 *>(Xhb + gr * Mp + gc) = o;
+    *reinterpret_cast<u32x4 *>(&tile[row][cv]) = o;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = threadIdx.x & 63;
+    const int k = (threadIdx.x >> 6) + 4 * h;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = static_cast<uint32_t>(tile[8 * k + 2 * q][c]) | (static_cast<uint32_t>(tile[8 * k + 2 * q + 1][c]) << 16);
+    *reinterpret_cast<u32x4 *>(XTb + (c0 + c) * Np + r0 + 8 * k) = o;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // row subset check
 // ---------------------------------------------------------------------------
@@ -727,6 +789,18 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
                                   const double *partials, int parts, double eps, void *Xh,
                                   void *XT, int64_t Np, int64_t Mp, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(Mp / 64), static_cast<unsigned>(Np / 64), static_cast<unsigned>(batch));
+  const bool vec = (m % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && io != DT_F32 && cdt != DT_F32;
+  if (vec) {
+    if (io == DT_BF16 && cdt == DT_BF16)
+      scale_transpose16<EBF16, EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    else if (io == DT_BF16)
+      scale_transpose16<EBF16, EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    else if (cdt == DT_BF16)
+      scale_transpose16<EF16, EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    else
+      scale_transpose16<EF16, EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    return hipGetLastError();
+  }
   if (io == DT_BF16) st_dispatch<EBF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
   else if (io == DT_F16) st_dispatch<EF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
   else st_dispatch<EF32>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
