@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgns.so")
 GNS_F32, GNS_BF16, GNS_F16 = 0, 1, 2
 GNS_OPT_NAIVE_ALGEBRA = 0x1
 GNS_OPT_NO_SQUARE_FALLBACK = 0x2
+GNS_OPT_ONE_STREAM = 0x4
 GNS_OPT_TILE_128 = 0x10
 GNS_OPT_TILE_256 = 0x20
 MAX_ITERS = 64
@@ -150,7 +151,7 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.
 def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] = (2,), *,
                     row_idx: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     compute_dtype=None, naive_algebra: bool = False, square_fallback: bool = True,
-                    tile: Optional[int] = None,
+                    tile: Optional[int] = None, split_batch: bool = True,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Gram Newton-Schulz of every matrix in X ([batch, n, m] or [n, m]) via
     gns_gram_batched.  ``row_idx`` ([batch, k] int64, device) selects the
@@ -182,7 +183,8 @@ def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] =
         _ptr(Xb), _ptr(out), B, n, m, _dtype_code(Xb.dtype), cdt, carr, T, rarr, len(rs),
         _ptr(row_idx), k,
         (GNS_OPT_NAIVE_ALGEBRA if naive_algebra else 0)
-        | (0 if square_fallback else GNS_OPT_NO_SQUARE_FALLBACK) | _tile_opts(tile),
+        | (0 if square_fallback else GNS_OPT_NO_SQUARE_FALLBACK) | _tile_opts(tile)
+        | (0 if split_batch else GNS_OPT_ONE_STREAM),
         _ptr(ws), ws.numel(), _stream(stream)))
     return out.squeeze(0) if squeeze else out
 
@@ -190,7 +192,7 @@ def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] =
 def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
                         row_idx: Optional[torch.Tensor] = None,
                         out: Optional[torch.Tensor] = None, compute_dtype=None,
-                        tile: Optional[int] = None,
+                        tile: Optional[int] = None, split_batch: bool = True,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Standard Newton-Schulz (Algorithm 1) via gns_standard_batched."""
     squeeze = X.dim() == 2
@@ -215,7 +217,8 @@ def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
     carr, T = _coeff_array(coeffs)
     _check(lib().gns_standard_batched(
         _ptr(Xb), _ptr(out), B, n, m, _dtype_code(Xb.dtype), cdt, carr, T,
-        _ptr(row_idx), k, _tile_opts(tile), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(row_idx), k, _tile_opts(tile) | (0 if split_batch else GNS_OPT_ONE_STREAM),
+        _ptr(ws), ws.numel(), _stream(stream)))
     return out.squeeze(0) if squeeze else out
 
 

@@ -140,15 +140,24 @@ struct LaunchScope {
 // --------------------------------------------------------------------------
 // launch helpers
 // --------------------------------------------------------------------------
+// One sub-batch: matrices [b0, b0 + batch) of a call, enqueued on stream s.
+// Every workspace region is strided per matrix, so a sub-batch addresses its
+// share with a plain offset.
 struct Ctx {
   const Plan *pl;
   int cdt;
   int64_t batch;
+  int64_t b0;
   unsigned char *ws;
   hipStream_t s;
-  void *sq(int i) const { return ws + pl->off_sq[i]; }
   int64_t sq_stride() const { return pl->Np * pl->Np; }
   int64_t rect_stride() const { return pl->Np * pl->Mp; }
+  void *sq(int i) const { return ws + pl->off_sq[i] + b0 * sq_stride() * pl->esz; }
+  void *xh() const { return ws + pl->off_xh + b0 * rect_stride() * pl->esz; }
+  void *xt(int i) const { return ws + (i ? pl->off_xt1 : pl->off_xt0) + b0 * rect_stride() * pl->esz; }
+  double *partials() const {
+    return reinterpret_cast<double *>(ws + pl->off_partials) + b0 * pl->parts;
+  }
 };
 
 // alpha * (A B^T) + beta * D is evaluated as alpha * (A B^T + (beta/alpha) D);
@@ -203,7 +212,7 @@ gns_status syrk(const Ctx &c, void *R) {
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int nt = static_cast<int>(N / c.pl->tile);
-  const void *Xh = c.ws + c.pl->off_xh;
+  const void *Xh = c.xh();
   p.A = Xh; p.lda = M; p.sA = c.rect_stride();
   p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
   p.K = static_cast<int>(M);
@@ -227,7 +236,7 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int tm = static_cast<int>(N / c.pl->tile), tn = static_cast<int>(M / c.pl->tile);
-  void *Xh = c.ws + c.pl->off_xh;
+  void *Xh = c.xh();
   p.A = S; p.lda = N; p.sA = c.sq_stride();
   p.B = XT_in; p.ldb = N; p.sB = c.rect_stride();
   p.K = static_cast<int>(N);
@@ -258,7 +267,7 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
 
 // Norm + scale + cast + transpose of the (row-selected) input.
 gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const int64_t *row_idx) {
-  double *partials = reinterpret_cast<double *>(c.ws + c.pl->off_partials);
+  double *partials = c.partials();
   const double rows = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
   {
     LaunchScope ls(c.s, "norm_partial", "norm_partial", 2.0 * rows * m * c.batch,
@@ -273,8 +282,7 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
                    c.batch * rows * m * (gns::dtype_size(io) + 2.0 * c.pl->esz));
     hipError_t e = gns::launch_scale_transpose(io, c.cdt, X, c.batch, n_total, c.pl->m, c.pl->rows,
                                                row_idx, partials, c.pl->parts, kEps,
-                                               c.ws + c.pl->off_xh, c.ws + c.pl->off_xt0,
-                                               c.pl->Np, c.pl->Mp, c.s);
+                                               c.xh(), c.xt(0), c.pl->Np, c.pl->Mp, c.s);
     ls.done();
     if (e != hipSuccess) return GNS_E_HIP;
   }
@@ -282,7 +290,7 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
 }
 
 gns_status parse_opts(unsigned opts, unsigned allowed, int *tile) {
-  allowed |= GNS_OPT_TILE_128 | GNS_OPT_TILE_256;
+  allowed |= GNS_OPT_TILE_128 | GNS_OPT_TILE_256 | GNS_OPT_ONE_STREAM;
   if (opts & ~allowed) return GNS_E_FLAGS;
   if ((opts & GNS_OPT_TILE_128) && (opts & GNS_OPT_TILE_256)) return GNS_E_FLAGS;
   *tile = (opts & GNS_OPT_TILE_128) ? 128 : (opts & GNS_OPT_TILE_256) ? 256 : 0;
@@ -326,12 +334,11 @@ gns_status workspace_checks(const void *X, const void *out, int64_t batch, int64
 
 // Standard Newton-Schulz (Dion3 §2.2, Algorithm 1) on a validated problem;
 // the symmetric products go through the mirrored kernel (Appendix C.3).
-gns_status enqueue_standard(const Plan &pl, int cdt, int64_t batch, const void *X, void *out,
-                            int io, int64_t n, const double *coeffs, int T,
-                            const int64_t *row_idx, void *workspace, hipStream_t stream) {
-  Ctx c{&pl, cdt, batch, static_cast<unsigned char *>(workspace), stream};
+gns_status enqueue_standard(const Ctx &c, const void *X, void *out, int io, int64_t n,
+                            const double *coeffs, int T, const int64_t *row_idx) {
+  const Plan &pl = *c.pl;
   void *A = c.sq(0), *B = c.sq(1);
-  void *XT[2] = {c.ws + pl.off_xt0, c.ws + pl.off_xt1};
+  void *XT[2] = {c.xt(0), c.xt(1)};
   int xcur = 0;
   const double nn = static_cast<double>(pl.rows);
   gns_status st;
@@ -354,83 +361,18 @@ gns_status enqueue_standard(const Plan &pl, int cdt, int64_t batch, const void *
   return GNS_OK;
 }
 
-}  // namespace
-
-// ==========================================================================
-// exported ABI
-// ==========================================================================
-extern "C" {
-
-int gns_abi_version(void) { return GNS_ABI_VERSION; }
-
-const char *gns_status_str(gns_status s) {
-  switch (s) {
-    case GNS_OK: return "ok";
-    case GNS_E_NULL: return "required pointer is NULL";
-    case GNS_E_SHAPE: return "invalid shape";
-    case GNS_E_DTYPE: return "unsupported dtype";
-    case GNS_E_COEFF: return "invalid iteration count or coefficient";
-    case GNS_E_RESTART: return "restart iterations must be strictly increasing in [1, T-1]";
-    case GNS_E_ROWIDX: return "row index out of range or repeated";
-    case GNS_E_ALIAS: return "workspace overlaps X or out";
-    case GNS_E_WORKSPACE: return "workspace missing, misaligned or too small";
-    case GNS_E_HIP: return "HIP launch failed";
-    case GNS_E_FLAGS: return "unknown option bits";
-  }
-  return "unknown status";
-}
-
-size_t gns_gram_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t rows, int64_t m) {
-  Plan pl;
-  if (batch <= 0 || !make_plan(cdt, batch, rows, m, 5, 256, &pl)) return 0;
-  return pl.bytes;
-}
-
-size_t gns_standard_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t rows, int64_t m) {
-  Plan pl;
-  if (batch <= 0 || !make_plan(cdt, batch, rows, m, 2, 256, &pl)) return 0;
-  return pl.bytes;
-}
-
-gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
-                            gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
-                            const int *restart_after, int n_restart, const int64_t *row_idx,
-                            int64_t k, unsigned opts, void *workspace, size_t workspace_bytes,
-                            void *stream) {
-  int64_t rows = 0;
-  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
-  if (st != GNS_OK) return st;
-  int tile_req = 0;
-  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
-    return st;
-  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
-  std::vector<char> restart_at(T + 2, 0);
-  for (int i = 0; i < n_restart; ++i) {
-    const int r = restart_after[i];
-    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
-    restart_at[r] = 1;
-  }
-  if (batch == 0) return GNS_OK;
-  Plan pl;
-  if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;
-  st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
-  if (st != GNS_OK) return st;
-  // Square matrices: both algorithms cost the same and standard NS needs
-  // fewer launches and never forms X X^T of an ill-conditioned square
-  // matrix, so the pages fall back to it (Dion3 §4.1, last paragraph).
-  if (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK))
-    return enqueue_standard(pl, static_cast<int>(cdt), batch, X, out, io, n, coeffs, T, row_idx,
-                            workspace, static_cast<hipStream_t>(stream));
-
-  const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
-  Ctx c{&pl, static_cast<int>(cdt), batch, static_cast<unsigned char *>(workspace),
-        static_cast<hipStream_t>(stream)};
+// Gram Newton-Schulz (Dion3 §4.2, Algorithm 3; Algorithm 2 algebra when
+// `naive`) on one sub-batch of a validated problem.
+gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t n,
+                        const double *coeffs, int T, const std::vector<char> &restart_at,
+                        const int64_t *row_idx, bool naive) {
+  gns_status st;
   void *R = c.sq(0), *Z = c.sq(1), *RZ = c.sq(2);
   void *Qb[2] = {c.sq(3), c.sq(4)};
-  void *XT[2] = {c.ws + pl.off_xt0, c.ws + pl.off_xt1};
+  void *XT[2] = {c.xt(0), c.xt(1)};
   int qcur = 0, xcur = 0;
   bool q_is_identity = true;
-  const double nn = static_cast<double>(rows);
+  const double nn = static_cast<double>(c.pl->rows);
   const double n3 = nn * nn * nn;
 
   if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
@@ -490,6 +432,154 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   return apply(c, Qb[qcur], XT[xcur], nullptr, 0.0f, true, out, io, n, row_idx, "final_apply");
 }
 
+// --------------------------------------------------------------------------
+// sub-batch fan-out
+// --------------------------------------------------------------------------
+// A call's matrices are independent, so a batch is split into two halves that
+// run the whole sequence on two library-owned streams.  The kernels of one
+// half then fill the CUs that the other half's launch leaves idle in its last,
+// partial wave of tiles.  The caller's stream forks to both streams and waits
+// for both before anything it enqueues later, so ordering is as if every
+// kernel ran on the caller's stream.
+constexpr int kSplit = 2;
+constexpr int kMaxDevices = 64;
+
+struct Fanout {
+  std::mutex mu;            // one call at a time uses the streams and events
+  bool tried = false, ok = false;
+  hipStream_t s[kSplit] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kSplit] = {};
+};
+Fanout g_fanout[kMaxDevices];
+
+// Streams and events of the current device, created on first use (default
+// priority, non-blocking); nullptr when the device cannot provide them.
+Fanout *fanout_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  Fanout *f = &g_fanout[dev];
+  std::lock_guard<std::mutex> lk(f->mu);
+  if (!f->tried) {
+    f->tried = true;
+    bool ok = hipEventCreateWithFlags(&f->fork, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; i < kSplit && ok; ++i) {
+      ok = hipStreamCreateWithFlags(&f->s[i], hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&f->join[i], hipEventDisableTiming) == hipSuccess;
+    }
+    f->ok = ok;
+  }
+  return f->ok ? f : nullptr;
+}
+
+// Enqueues body(ctx) for the whole batch on `caller`, or for two halves on the
+// fan-out streams.  body enqueues the matrices [ctx.b0, ctx.b0 + ctx.batch).
+template <class Body>
+gns_status run_batches(const Plan &pl, int cdt, int64_t batch, void *workspace,
+                       hipStream_t caller, bool split, Body &&body) {
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  Fanout *f = (split && batch >= kSplit) ? fanout_for_current_device() : nullptr;
+  if (!f) return body(Ctx{&pl, cdt, batch, 0, ws, caller});
+  std::lock_guard<std::mutex> lk(f->mu);
+  if (hipEventRecord(f->fork, caller) != hipSuccess) return GNS_E_HIP;
+  gns_status st = GNS_OK;
+  const int64_t half = (batch + 1) / 2;
+  for (int i = 0; i < kSplit; ++i) {
+    const int64_t b0 = i * half;
+    const int64_t nb = i == 0 ? half : batch - half;
+    if (hipStreamWaitEvent(f->s[i], f->fork, 0) != hipSuccess) { st = GNS_E_HIP; continue; }
+    if (st == GNS_OK) st = body(Ctx{&pl, cdt, nb, b0, ws, f->s[i]});
+  }
+  // always join, so that the caller's stream orders after whatever was enqueued
+  for (int i = 0; i < kSplit; ++i) {
+    if (hipEventRecord(f->join[i], f->s[i]) != hipSuccess ||
+        hipStreamWaitEvent(caller, f->join[i], 0) != hipSuccess)
+      st = GNS_E_HIP;
+  }
+  return st;
+}
+
+}  // namespace
+
+// ==========================================================================
+// exported ABI
+// ==========================================================================
+extern "C" {
+
+int gns_abi_version(void) { return GNS_ABI_VERSION; }
+
+const char *gns_status_str(gns_status s) {
+  switch (s) {
+    case GNS_OK: return "ok";
+    case GNS_E_NULL: return "required pointer is NULL";
+    case GNS_E_SHAPE: return "invalid shape";
+    case GNS_E_DTYPE: return "unsupported dtype";
+    case GNS_E_COEFF: return "invalid iteration count or coefficient";
+    case GNS_E_RESTART: return "restart iterations must be strictly increasing in [1, T-1]";
+    case GNS_E_ROWIDX: return "row index out of range or repeated";
+    case GNS_E_ALIAS: return "workspace overlaps X or out";
+    case GNS_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GNS_E_HIP: return "HIP launch failed";
+    case GNS_E_FLAGS: return "unknown option bits";
+  }
+  return "unknown status";
+}
+
+size_t gns_gram_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t rows, int64_t m) {
+  Plan pl;
+  if (batch <= 0 || !make_plan(cdt, batch, rows, m, 5, 256, &pl)) return 0;
+  return pl.bytes;
+}
+
+size_t gns_standard_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t rows, int64_t m) {
+  Plan pl;
+  if (batch <= 0 || !make_plan(cdt, batch, rows, m, 2, 256, &pl)) return 0;
+  return pl.bytes;
+}
+
+gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                            gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
+                            const int *restart_after, int n_restart, const int64_t *row_idx,
+                            int64_t k, unsigned opts, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  int64_t rows = 0;
+  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
+  if (st != GNS_OK) return st;
+  int tile_req = 0;
+  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
+    return st;
+  const bool split = !(opts & GNS_OPT_ONE_STREAM);
+  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
+  std::vector<char> restart_at(T + 2, 0);
+  for (int i = 0; i < n_restart; ++i) {
+    const int r = restart_after[i];
+    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
+    restart_at[r] = 1;
+  }
+  if (batch == 0) return GNS_OK;
+  Plan pl;
+  if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;
+  st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
+  if (st != GNS_OK) return st;
+  // Square matrices: both algorithms cost the same and standard NS needs
+  // fewer launches and never forms X X^T of an ill-conditioned square
+  // matrix, so the pages fall back to it (Dion3 §4.1, last paragraph).
+  const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  if (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK))
+    return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c) {
+      return enqueue_standard(c, static_cast<const unsigned char *>(X) + c.b0 * io_mat,
+                              static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
+                              row_idx ? row_idx + c.b0 * k : nullptr);
+    });
+  const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
+  return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c) {
+    return enqueue_gram(c, static_cast<const unsigned char *>(X) + c.b0 * io_mat,
+                        static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
+                        restart_at, row_idx ? row_idx + c.b0 * k : nullptr, naive);
+  });
+}
+
 gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
                                 gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
                                 const int64_t *row_idx, int64_t k, unsigned opts, void *workspace,
@@ -499,13 +589,19 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
   if (st != GNS_OK) return st;
   int tile_req = 0;
   if ((st = parse_opts(opts, 0u, &tile_req)) != GNS_OK) return st;
+  const bool split = !(opts & GNS_OPT_ONE_STREAM);
   if (batch == 0) return GNS_OK;
   Plan pl;
   if (!make_plan(cdt, batch, rows, m, 2, tile_req, &pl)) return GNS_E_SHAPE;
   st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
   if (st != GNS_OK) return st;
-  return enqueue_standard(pl, cdt, batch, X, out, io, n, coeffs, T, row_idx, workspace,
-                          static_cast<hipStream_t>(stream));
+  const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
+  return run_batches(pl, cdt, batch, workspace, static_cast<hipStream_t>(stream), split,
+                     [&](const Ctx &c) {
+                       return enqueue_standard(c, static_cast<const unsigned char *>(X) + c.b0 * io_mat,
+                                               static_cast<unsigned char *>(out) + c.b0 * io_mat, io,
+                                               n, coeffs, T, row_idx ? row_idx + c.b0 * k : nullptr);
+                     });
 }
 
 gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,

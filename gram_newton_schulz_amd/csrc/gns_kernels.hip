@@ -515,6 +515,24 @@ gemm_nt(GemmParams p) {
   } else {  // MODE_FINAL
     const int64_t *ridx = p.row_idx ? p.row_idx + static_cast<int64_t>(mat) * p.rows_eff : nullptr;
     const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
+    if (!ridx && p.out_dtype == E::code && row_base + WTM <= p.rows_eff &&
+        col_base + WTN <= p.out_cols) {
+      // the whole wave tile lies inside the caller's matrix and needs no
+      // conversion: plain stores, consecutive lanes on consecutive columns
+      S *O = static_cast<S *>(p.out) + obase;
+#pragma unroll
+      for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < NBJ; ++jb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
+            const int64_t j = col_base + jb * 32 + lr;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) O[(i0 + q) * p.out_cols + j] = E::st(p.alpha * acc[ib][jb][4 * g + q]);
+          }
+      return;
+    }
 #pragma unroll
     for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll

@@ -24,8 +24,15 @@
  * - X and out are contiguous row-major [batch][n][m] in the I/O dtype.
  * - The caller owns every buffer, including the workspace; the library never
  *   allocates or frees device memory and never synchronises the stream.
- *   All work is enqueued on `stream` in order; the call returns once it is
- *   enqueued.  Results are ready when the stream is.
+ *   The call returns once its work is enqueued; results are ready when
+ *   `stream` is.  With batch >= 2 (and without GNS_OPT_ONE_STREAM) the two
+ *   halves of the batch run on two streams that the library creates once per
+ *   device: they start after everything already enqueued on `stream`, and
+ *   `stream` waits for both before anything enqueued on it later, so the
+ *   caller sees the same ordering as if all work ran on `stream`.  The
+ *   halves then fill each other's idle CUs in the last, partial wave of
+ *   tiles of every launch.  Calls from several host threads on one device
+ *   share those streams (they are serialised, still correct).
  * - Argument errors are detected on the host before anything is enqueued
  *   (no partial work) and reported as a status code; nothing throws across
  *   the ABI.  A failed kernel launch returns GNS_E_HIP.  Faults inside
@@ -82,6 +89,9 @@ typedef enum {
                                       matrix is square (by default a square
                                       problem runs standard NS, which costs the
                                       same there, Dion3 §4.1); gns_gram_batched only */
+#define GNS_OPT_ONE_STREAM 0x4u    /* enqueue everything on `stream` itself
+                                      instead of splitting the batch over the
+                                      library's two streams (see below)      */
 #define GNS_OPT_TILE_128 0x10u     /* force 128 x 128 output tiles            */
 #define GNS_OPT_TILE_256 0x20u     /* force 256 x 256 output tiles            */
 /* Without a TILE bit the library picks the tile edge from the problem size.
@@ -157,7 +167,8 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
  * Standard Newton-Schulz on a batch (Dion3 §2.2, Algorithm 1) with the
  * symmetric products computed once per pair of mirrored tiles (Dion3 §5,
  * Appendix C.3): per iteration A = X X^T, B = b A + c A^2, X <- a X + B X.
- * Arguments as for gns_gram_batched (no restarts; opts takes the TILE bits).
+ * Arguments as for gns_gram_batched (no restarts; opts takes the TILE bits
+ * and GNS_OPT_ONE_STREAM).
  */
 gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
                                 gns_dtype io_dtype, gns_dtype compute_dtype,

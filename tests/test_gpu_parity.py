@@ -259,3 +259,42 @@ def test_out_of_range_rows_touch_nothing():
     keep = [i for i in range(20) if i not in (3, 4)]
     assert torch.count_nonzero(out[0, keep]).item() == 0
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("algo", ["gram", "standard"])
+def test_batch_split_matches_one_stream(algo):
+    """Splitting a batch over the library's two streams gives bit-identical
+    results to running every matrix on the caller's stream (odd batch)."""
+    gns = need_gpu()
+    X, X64 = _inputs(5, 300, 700, "bf16", seed=22)
+    Xd = X.cuda()
+    say(f"split vs one stream {algo}")
+    a = _run(gns, algo, Xd, "bf16")
+    b = _run(gns, algo, Xd, "bf16", split_batch=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = np.stack([(oracle_gram if algo == "gram" else oracle_standard)(X64[b_]) for b_ in range(5)])
+    assert max(per_matrix_rel(synth.as_f64(a), ref)) <= TOL_HALF
+
+
+def test_split_orders_against_caller_stream():
+    """Work enqueued on the caller's stream before the call is seen by both
+    halves, and work enqueued after it sees their results, with no device-wide
+    synchronisation in between."""
+    gns = need_gpu()
+    X, _ = _inputs(4, 256, 1024, "bf16", seed=23)
+    X2, _ = _inputs(4, 256, 1024, "bf16", seed=24)
+    Xd = X.cuda()
+    X2d = X2.cuda()
+    ref = gns.gram_ns_batched(X2d, NS5, split_batch=False)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    say("split ordering on a side stream")
+    with torch.cuda.stream(s):
+        buf = Xd.clone()
+        buf.copy_(X2d)                       # must be visible to both halves
+        out = gns.gram_ns_batched(buf, NS5, stream=s)
+        total = out.float().sum(dim=(1, 2))  # must see both halves' results
+    s.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(total, ref.float().sum(dim=(1, 2)))
