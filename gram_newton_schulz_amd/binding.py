@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgns.so")
 
-GNS_F32, GNS_BF16, GNS_F16 = 0, 1, 2
+GNS_F32, GNS_BF16, GNS_F16, GNS_BF16X3 = 0, 1, 2, 3
 GNS_OPT_NAIVE_ALGEBRA = 0x1
 GNS_OPT_NO_SQUARE_FALLBACK = 0x2
 GNS_OPT_ONE_STREAM = 0x4
@@ -97,8 +97,12 @@ def _check(code: int) -> None:
 
 
 def _dtype_code(dt) -> int:
+    """torch dtype -> gns_dtype code; also accepts a code, or "bf16x3" for the
+    split-bf16 compute type (GNS_BF16X3)."""
     if isinstance(dt, int):
         return dt
+    if dt == "bf16x3":
+        return GNS_BF16X3
     if dt not in _DT:
         raise GnsError(3, f"unsupported dtype {dt}")
     return _DT[dt]

@@ -26,22 +26,24 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 bool valid_dtype(int dt) { return dt == GNS_F32 || dt == GNS_BF16 || dt == GNS_F16; }
+bool valid_compute(int dt) { return valid_dtype(dt) || dt == GNS_BF16X3; }
 
 // --------------------------------------------------------------------------
 // problem plan: tile edge, padded sizes, workspace layout
 // --------------------------------------------------------------------------
 struct Plan {
   int tile = 128;
-  int64_t rows = 0, m = 0, Np = 0, Mp = 0;
+  int64_t batch = 0, rows = 0, m = 0, Np = 0, Mp = 0;
   int parts = 1;
   int esz = 2;
+  int planes = 1;                      // 2: split hi/lo storage (GNS_BF16X3)
   size_t off_partials = 0, off_xh = 0, off_xt0 = 0, off_xt1 = 0;
   size_t off_sq[5] = {0, 0, 0, 0, 0};  // R, Z, RZ, Q0, Q1 (standard NS: A, B)
   size_t bytes = 0;
 };
 
 int choose_tile(int cdt, int64_t batch, int64_t rows) {
-  if (cdt == GNS_F32) return 128;
+  if (cdt == GNS_F32 || cdt == GNS_BF16X3) return 128;
   // 256-edge tiles halve operand traffic per FLOP; use them when the
   // symmetric products still give every CU a couple of workgroups.
   const int64_t t256 = (rows + 255) / 256;
@@ -60,9 +62,11 @@ int choose_parts(int64_t batch, int64_t rows) {
 // for 256-padded buffers so that any tile choice fits.
 bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, int tile_request,
                Plan *pl) {
-  if (!valid_dtype(cdt) || batch < 0 || rows < 1 || m < rows) return false;
+  if (!valid_compute(cdt) || batch < 0 || rows < 1 || m < rows) return false;
   pl->tile = tile_request ? tile_request : choose_tile(cdt, batch, rows);
-  if (cdt == GNS_F32) pl->tile = 128;   // the fp32 kernels exist for 128-edge tiles only
+  // the fp32 and split-plane kernels exist for 128-edge tiles only
+  if (cdt == GNS_F32 || cdt == GNS_BF16X3) pl->tile = 128;
+  pl->batch = batch;
   pl->rows = rows;
   pl->m = m;
   pl->Np = round_up(rows, pl->tile);
@@ -74,11 +78,13 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
   if (int64_t(256) * std::max(pl->Np, pl->Mp) * gns::dtype_size(cdt) >= (int64_t(1) << 31)) return false;
   pl->parts = choose_parts(batch, rows);
   pl->esz = gns::dtype_size(cdt);
+  pl->planes = gns::dtype_planes(cdt);
   size_t off = 0;
   pl->off_partials = off;
   off = align_up(off + sizeof(double) * batch * pl->parts, kAlign);
-  const size_t rect = static_cast<size_t>(batch) * pl->Np * pl->Mp * pl->esz;
-  const size_t sq = static_cast<size_t>(batch) * pl->Np * pl->Np * pl->esz;
+  // every region holds `planes` planes of `batch` matrices, lo after hi
+  const size_t rect = static_cast<size_t>(pl->planes) * batch * pl->Np * pl->Mp * pl->esz;
+  const size_t sq = static_cast<size_t>(pl->planes) * batch * pl->Np * pl->Np * pl->esz;
   pl->off_xh = off;
   off = align_up(off + rect, kAlign);
   pl->off_xt0 = off;
@@ -158,6 +164,9 @@ struct Ctx {
   double *partials() const {
     return reinterpret_cast<double *>(ws + pl->off_partials) + b0 * pl->parts;
   }
+  // element offset from a hi plane to its lo plane (split storage only)
+  int64_t plane_sq() const { return pl->planes == 2 ? pl->batch * sq_stride() : 0; }
+  int64_t plane_rect() const { return pl->planes == 2 ? pl->batch * rect_stride() : 0; }
 };
 
 // alpha * (A B^T) + beta * D is evaluated as alpha * (A B^T + (beta/alpha) D);
@@ -197,6 +206,7 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   if (D) { p.DT = D; p.lddt = N; p.sDT = c.sq_stride(); }   // D is symmetric
   p.C = C; p.ldc = N; p.sC = c.sq_stride();
   p.C2 = C2; p.sC2 = c.sq_stride();
+  p.pA = p.pB = p.pDT = p.pC = p.pC2 = c.plane_sq();
   p.diag1 = diag1; p.diag2 = diag2;
   const double n = static_cast<double>(c.pl->rows);
   const double bytes = c.batch * n * n * c.pl->esz * (3.0 + (D ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
@@ -219,6 +229,8 @@ gns_status syrk(const Ctx &c, void *R) {
   p.tiles_m = p.tiles_n = nt;
   p.tiles_per_mat = nt * (nt + 1) / 2;
   p.C = R; p.ldc = N; p.sC = c.sq_stride();
+  p.pA = p.pB = c.plane_rect();
+  p.pC = c.plane_sq();
   const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
   LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), n * n * m * c.batch,
                  c.batch * (n * m + n * n) * c.pl->esz);
@@ -245,6 +257,8 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   set_scale(&p, 1.0f, beta);
   // the beta term reads X through its transposed copy, the B operand
   if (beta != 0.0f) { p.DT = XT_in; p.lddt = N; p.sDT = c.rect_stride(); }
+  p.pA = c.plane_sq();
+  p.pB = p.pDT = p.pC = p.pCT = c.plane_rect();
   const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
   double bytes = c.batch * (n * n + n * m) * c.pl->esz;
   if (final) {
@@ -282,7 +296,8 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
                    c.batch * rows * m * (gns::dtype_size(io) + 2.0 * c.pl->esz));
     hipError_t e = gns::launch_scale_transpose(io, c.cdt, X, c.batch, n_total, c.pl->m, c.pl->rows,
                                                row_idx, partials, c.pl->parts, kEps,
-                                               c.xh(), c.xt(0), c.pl->Np, c.pl->Mp, c.s);
+                                               c.xh(), c.xt(0), c.pl->Np, c.pl->Mp,
+                                               c.plane_rect(), c.plane_rect(), c.s);
     ls.done();
     if (e != hipSuccess) return GNS_E_HIP;
   }
@@ -305,7 +320,7 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
 gns_status common_checks(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
                          gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
                          const int64_t *row_idx, int64_t k, int64_t *rows) {
-  if (!valid_dtype(io) || !valid_dtype(cdt)) return GNS_E_DTYPE;
+  if (!valid_dtype(io) || !valid_compute(cdt)) return GNS_E_DTYPE;
   if (batch < 0 || n < 1 || m < 1) return GNS_E_SHAPE;
   if (row_idx) {
     if (k < 1 || k > n) return GNS_E_SHAPE;

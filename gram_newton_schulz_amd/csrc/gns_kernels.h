@@ -7,9 +7,12 @@
 
 namespace gns {
 
-enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+// DT_BF16X3 is a compute type only: every matrix is stored as two bf16
+// planes hi + lo, and every product sums hi*hi + hi*lo + lo*hi.
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_BF16X3 = 3 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+inline int dtype_planes(int dt) { return dt == DT_BF16X3 ? 2 : 1; }
 
 // Epilogue of the NT product kernel.
 enum GemmMode : int {
@@ -28,6 +31,9 @@ enum GemmMode : int {
 struct GemmParams {
   const void *A; int64_t lda, sA;   // leading dim and batch stride (elements)
   const void *B; int64_t ldb, sB;
+  // split storage (DT_BF16X3): element offset from each hi plane to its lo
+  // plane; unused otherwise
+  int64_t pA, pB, pDT, pC, pC2, pCT;
   int K;                            // contraction length, multiple of 128 bytes
   int tiles_m, tiles_n;             // output tiles per matrix along rows / cols
   int tiles_per_mat;                // sym: tiles_m*(tiles_m+1)/2
@@ -58,11 +64,14 @@ hipError_t launch_norm_partial(int io_dtype, const void *X, int64_t batch, int64
                                int64_t m, int64_t rows_eff, const int64_t *row_idx,
                                int parts, double *partials, hipStream_t s);
 
+// X_hat = X / (||X||_F + eps) in the compute type, row-major into Xh and
+// transposed into XT; for DT_BF16X3 the lo planes sit plane_h / plane_t
+// elements after Xh / XT.
 hipError_t launch_scale_transpose(int io_dtype, int compute_dtype, const void *X,
                                   int64_t batch, int64_t n, int64_t m, int64_t rows_eff,
                                   const int64_t *row_idx, const double *partials,
                                   int parts, double eps, void *Xh, void *XT, int64_t Np,
-                                  int64_t Mp, hipStream_t s);
+                                  int64_t Mp, int64_t plane_h, int64_t plane_t, hipStream_t s);
 
 hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, hipStream_t s);

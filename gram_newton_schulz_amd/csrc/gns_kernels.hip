@@ -166,10 +166,48 @@ struct WaveLayout {
   static constexpr int THREADS = 64 * WGM * WGN;
 };
 
-template <class E, int TILE, int MODE>
+// Split storage (PL = 2): a value v is kept as two bf16 planes, hi = bf16(v)
+// and lo = bf16(v - hi), the lo plane `plane` elements after the hi plane.
+// Products take the three significant terms hi*hi + hi*lo + lo*hi.
+template <class E, int PL>
+struct Store {
+  using S = typename E::S;
+  __device__ static __forceinline__ void put(S *base, int64_t idx, int64_t plane, float v) {
+    const S h = E::st(v);
+    base[idx] = h;
+    if constexpr (PL == 2) base[idx + plane] = E::st(v - E::ld(h));
+  }
+  // four consecutive entries of a row
+  __device__ static __forceinline__ void put4(S *base, int64_t idx, int64_t plane, const float *v) {
+    static_assert(sizeof(S) == 2, "16-bit storage only");
+    S h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[q] = E::st(v[q]);
+      l[q] = E::st(v[q] - E::ld(h[q]));
+    }
+    uint2 pk;
+    pk.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+    pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
+    *reinterpret_cast<uint2 *>(base + idx) = pk;
+    if constexpr (PL == 2) {
+      pk.x = static_cast<uint32_t>(l[0]) | (static_cast<uint32_t>(l[1]) << 16);
+      pk.y = static_cast<uint32_t>(l[2]) | (static_cast<uint32_t>(l[3]) << 16);
+      *reinterpret_cast<uint2 *>(base + idx + plane) = pk;
+    }
+  }
+  __device__ static __forceinline__ float get(const S *base, int64_t idx, int64_t plane) {
+    float v = E::ld(base[idx]);
+    if constexpr (PL == 2) v += E::ld(base[idx + plane]);
+    return v;
+  }
+};
+
+template <class E, int TILE, int MODE, int PL>
 __global__ void __launch_bounds__(WaveLayout<TILE>::THREADS)
 gemm_nt(GemmParams p) {
   using S = typename E::S;
+  using St = Store<E, PL>;
   constexpr int ESZ = sizeof(S);
   constexpr int SB = 64;                  // bytes of one row of one K stage
   constexpr int BKE = SB / ESZ;           // contraction elements per stage
@@ -181,13 +219,17 @@ gemm_nt(GemmParams p) {
   constexpr int WTN = TILE / WGN;         // wave tile columns
   constexpr int NBI = WTM / 32;           // 32x32 blocks per wave, rows
   constexpr int NBJ = WTN / 32;           // 32x32 blocks per wave, columns
-  constexpr int OPB = TILE * SB;          // bytes of one operand in one stage
+  constexpr int OPB = TILE * SB;          // bytes of one operand plane in one stage
+  constexpr int STB = 2 * PL * OPB;       // bytes of one stage: A planes, then B planes
   constexpr int NST = 5;                  // LDS ring depth (stages)
   constexpr int NW = NT / 64;             // waves
-  constexpr int BPW = (TILE / 16) / NW;   // 1 KiB LDS blocks per wave per operand per stage
+  constexpr int BPW = (TILE / 16) / NW;   // 1 KiB LDS blocks per wave per plane per stage
+  constexpr int LPS = 2 * PL * BPW;       // DMA instructions per wave per stage
   static_assert(BPW * NW * 16 == TILE, "blocks must cover the tile");
+  static_assert(PL == 1 || (ESZ == 2 && NW == 4), "split planes: 16-bit types, 128-edge tiles");
+  static_assert(NST * STB <= 160 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * 2 * OPB];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STB];
 
   // Workgroup -> tile.  Consecutive tiles share an operand panel; the
   // hardware deals workgroups round-robin over the 8 XCDs, so regroup ids to
@@ -223,10 +265,6 @@ gemm_nt(GemmParams p) {
   const int wr = (wave / WGN) * WTM;
   const int wc = (wave % WGN) * WTN;
 
-  const unsigned char *Ag = static_cast<const unsigned char *>(p.A) +
-                            (static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda) * ESZ;
-  const unsigned char *Bg = static_cast<const unsigned char *>(p.B) +
-                            (static_cast<int64_t>(mat) * p.sB + static_cast<int64_t>(tj) * TILE * p.ldb) * ESZ;
   const int64_t ldaB = p.lda * ESZ;
   const int64_t ldbB = p.ldb * ESZ;
 
@@ -234,22 +272,29 @@ gemm_nt(GemmParams p) {
   // buffer load: one instruction fills 1 KiB (16 rows x 64 bytes) of a stage,
   // lane l writing bytes 16 l .. 16 l + 15.  Lane l therefore fetches row
   // l / 4 of its block and the logical chunk that the swizzle places at
-  // physical chunk l % 4.  Wave w fills blocks w, w + NW, ... of each operand.
+  // physical chunk l % 4.  Wave w fills blocks w, w + NW, ... of each plane.
   const int dma_row = lane >> 2;
   const int dma_chunk = (lane & 3) ^ swz(dma_row);
   const int vA = dma_row * static_cast<int>(ldaB) + dma_chunk * 16;
   const int vB = dma_row * static_cast<int>(ldbB) + dma_chunk * 16;
-  // buffer descriptors over this tile's A and B panels (hardware range check:
-  // loads past the panel return zeros)
-  const uint64_t aBase = reinterpret_cast<uint64_t>(Ag);
-  const uint64_t bBase = reinterpret_cast<uint64_t>(Bg);
-  // (readfirstlane: these values are wave-uniform; the asm needs them in SGPRs)
-  const i32x4 rA = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(aBase))),
-                    __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(aBase >> 32) & 0xffff)),
-                    __builtin_amdgcn_readfirstlane(static_cast<int>(TILE * ldaB)), 0x00020000};
-  const i32x4 rB = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(bBase))),
-                    __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(bBase >> 32) & 0xffff)),
-                    __builtin_amdgcn_readfirstlane(static_cast<int>(TILE * ldbB)), 0x00020000};
+  // buffer descriptors over this tile's A and B panels, one per plane
+  // (hardware range check: loads past the panel return zeros; the values are
+  // wave-uniform, readfirstlane puts them in SGPRs for the asm)
+  auto descriptor = [&](const void *base, int64_t panel_off, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(static_cast<const unsigned char *>(base) + panel_off * ESZ);
+    const i32x4 r = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))),
+                     __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff)),
+                     __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
+    return r;
+  };
+  const int64_t offA = static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda;
+  const int64_t offB = static_cast<int64_t>(mat) * p.sB + static_cast<int64_t>(tj) * TILE * p.ldb;
+  i32x4 rA[PL], rB[PL];
+#pragma unroll
+  for (int pl = 0; pl < PL; ++pl) {
+    rA[pl] = descriptor(p.A, offA + pl * p.pA, TILE * ldaB);
+    rB[pl] = descriptor(p.B, offB + pl * p.pB, TILE * ldbB);
+  }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ldaB32 = __builtin_amdgcn_readfirstlane(static_cast<int>(ldaB));
   const int ldbB32 = __builtin_amdgcn_readfirstlane(static_cast<int>(ldbB));
@@ -282,16 +327,19 @@ gemm_nt(GemmParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const S *src = DTm + (j_base + j * 32) * p.lddt + i_base + i * 32 + 8 * g;
-          float v[4];
-          if constexpr (ESZ == 2) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(src);
-            v[0] = E::ld(static_cast<S>(u.x & 0xffffu));
-            v[1] = E::ld(static_cast<S>(u.x >> 16));
-            v[2] = E::ld(static_cast<S>(u.y & 0xffffu));
-            v[3] = E::ld(static_cast<S>(u.y >> 16));
-          } else {
-            const float4 u = *reinterpret_cast<const float4 *>(src);
-            v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+          float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int pl = 0; pl < PL; ++pl) {
+            if constexpr (ESZ == 2) {
+              const uint2 u = *reinterpret_cast<const uint2 *>(src + pl * p.pDT);
+              v[0] += E::ld(static_cast<S>(u.x & 0xffffu));
+              v[1] += E::ld(static_cast<S>(u.x >> 16));
+              v[2] += E::ld(static_cast<S>(u.y & 0xffffu));
+              v[3] += E::ld(static_cast<S>(u.y >> 16));
+            } else {
+              const float4 u = *reinterpret_cast<const float4 *>(src);
+              v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+            }
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = p.init_scale * v[q];
@@ -299,49 +347,66 @@ gemm_nt(GemmParams p) {
   }
 
   // Main loop over K stages of 64 bytes per row in an NST-deep LDS ring.
-  // Iteration i multiplies stage i; its last slice already reads the first
-  // fragments of stage i+1, so at the start of every iteration stages i and
-  // i+1 are complete and NST-3 later stages are in flight.  After the
-  // barrier that closes iteration i, the buffer of stage i is refilled with
-  // stage i+NST, which gives each load NST-2 iterations to arrive.  The
-  // loads bypass the compiler's wait bookkeeping (inline assembly), so the
-  // waits are explicit: before the barrier of iteration i every wave waits
-  // until its share of stage i+2 has landed.
+  // The loads bypass the compiler's wait bookkeeping (inline assembly), so
+  // the waits are explicit counts of this wave's outstanding loads.
   const int nk = p.K / BKE;
   if (nk > 0) {
     using Frag = typename Mma<E>::Frag;
     auto dma_stage = [&](int stage) {
       const int st = stage < nk ? stage : nk - 1;   // past the end: harmless reload
-      const uint32_t buf_lds = lds_base + static_cast<uint32_t>((stage % NST) * 2 * OPB);
+      const uint32_t buf_lds = lds_base + static_cast<uint32_t>((stage % NST) * STB);
 #pragma unroll
       for (int q = 0; q < BPW; ++q) {
         const int blk = wave_u + q * NW;
         const int soA = blk * 16 * ldaB32 + st * SB;
         const int soB = blk * 16 * ldbB32 + st * SB;
-        asm volatile(
-            "s_mov_b32 m0, %0\n\t"
-            "buffer_load_dwordx4 %1, %2, %3 offen lds"
-            :: "s"(buf_lds + blk * 1024), "v"(vA), "s"(rA), "s"(soA) : "memory", "m0");
-        asm volatile(
-            "s_mov_b32 m0, %0\n\t"
-            "buffer_load_dwordx4 %1, %2, %3 offen lds"
-            :: "s"(buf_lds + OPB + blk * 1024), "v"(vB), "s"(rB), "s"(soB) : "memory", "m0");
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl) {
+          asm volatile(
+              "s_mov_b32 m0, %0\n\t"
+              "buffer_load_dwordx4 %1, %2, %3 offen lds"
+              :: "s"(buf_lds + pl * OPB + blk * 1024), "v"(vA), "s"(rA[pl]), "s"(soA) : "memory", "m0");
+          asm volatile(
+              "s_mov_b32 m0, %0\n\t"
+              "buffer_load_dwordx4 %1, %2, %3 offen lds"
+              :: "s"(buf_lds + (PL + pl) * OPB + blk * 1024), "v"(vB), "s"(rB[pl]), "s"(soB) : "memory", "m0");
+        }
       }
     };
-    Frag fa[2][NBI], fb[2][NBJ];
+    Frag fa[2][PL][NBI], fb[2][PL][NBJ];
     auto fload = [&](int slot, int buf, int sub) {
-      const unsigned char *la = lds + buf * 2 * OPB;
+      const unsigned char *la = lds + buf * STB;
 #pragma unroll
-      for (int b = 0; b < NBI; ++b) fa[slot][b] = Mma<E>::load(la + (wr + b * 32 + lr) * SB, sub, lh, fsw);
+      for (int pl = 0; pl < PL; ++pl) {
 #pragma unroll
-      for (int b = 0; b < NBJ; ++b) fb[slot][b] = Mma<E>::load(la + OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
+        for (int b = 0; b < NBI; ++b)
+          fa[slot][pl][b] = Mma<E>::load(la + pl * OPB + (wr + b * 32 + lr) * SB, sub, lh, fsw);
+#pragma unroll
+        for (int b = 0; b < NBJ; ++b)
+          fb[slot][pl][b] = Mma<E>::load(la + (PL + pl) * OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
+      }
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+      for (int ii = 0; ii < NBI; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < NBJ; ++jj) {
+          if constexpr (PL == 2) {
+            // small terms first
+            acc[ii][jj] = Mma<E>::run(fa[slot][1][ii], fb[slot][0][jj], acc[ii][jj]);
+            acc[ii][jj] = Mma<E>::run(fa[slot][0][ii], fb[slot][1][jj], acc[ii][jj]);
+          }
+          acc[ii][jj] = Mma<E>::run(fa[slot][0][ii], fb[slot][0][jj], acc[ii][jj]);
+        }
     };
 
     if constexpr (NW == 8) {
       // Ping-pong over the two waves of every SIMD.  Every wave runs the same
-      // stream per stage i -- L(i): issue its DMA share of stage i+NST-1 and
-      // read its fragments of stage i; barrier; C(i): the MFMAs of stage i;
-      // barrier -- but waves 4-7 start one barrier later than waves 0-3.
+      // stream per stage i -- L(i): read its fragments of stage i, then issue
+      // its DMA share of stage i+NST-1 (reads first, so that a DMA issue
+      // stalled by a busy memory path does not delay them); barrier; C(i):
+      // the MFMAs of stage i; barrier -- but waves 4-7 start one barrier
+      // later than waves 0-3.
       // At every barrier the two waves of a SIMD are therefore in opposite
       // phases: one multiplies while the other reads, and the matrix core
       // never drains at a barrier.  Stage i+NST-1 goes into the buffer of
@@ -349,41 +414,39 @@ gemm_nt(GemmParams p) {
       // at the end of L(i) each wave waits for its share of stage i+1, which
       // the other group reads one barrier later at the earliest.
       const bool g1 = wave_u >= 4;
-      auto load_stage = [&](int b) {
-        static_for<0, SUB>([&](auto sc) { fload(decltype(sc)::value, b, decltype(sc)::value); });
-      };
-      constexpr int kWait = 2 * BPW * (NST - 2);   // this wave's loads of stages i+2 .. i+NST-1
+      constexpr int kWait = LPS * (NST - 2);   // this wave's loads of stages i+2 .. i+NST-1
       static_assert(kWait < 64, "wait count out of range");
 #pragma unroll
       for (int j = 0; j < NST - 1; ++j) dma_stage(j);
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 2)) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
       __syncthreads();
       if (g1) __syncthreads();
       int buf = 0;                          // buffer of stage i
       for (int i = 0; i < nk; ++i) {
+        static_for<0, SUB>([&](auto sc) { fload(decltype(sc)::value, buf, decltype(sc)::value); });
         dma_stage(i + NST - 1);             // into the buffer of stage i-1
-        load_stage(buf);
         asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
         __syncthreads();
         __builtin_amdgcn_s_setprio(1);
-        static_for<0, SUB>([&](auto sc) {
-          constexpr int s = decltype(sc)::value;
-#pragma unroll
-          for (int ii = 0; ii < NBI; ++ii)
-#pragma unroll
-            for (int jj = 0; jj < NBJ; ++jj) acc[ii][jj] = Mma<E>::run(fa[s][ii], fb[s][jj], acc[ii][jj]);
-        });
+        static_for<0, SUB>([&](auto sc) { mma(decltype(sc)::value); });
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         buf = buf == NST - 1 ? 0 : buf + 1;
       }
       if (!g1) __syncthreads();
     } else {
+      // Iteration i multiplies stage i; its last slice already reads the
+      // first fragments of stage i+1, so at the start of every iteration
+      // stages i and i+1 are complete and NST-3 later stages are in flight.
+      // After the barrier that closes iteration i, the buffer of stage i is
+      // refilled with stage i+NST, which gives each load NST-2 iterations to
+      // arrive.  Before that barrier every wave waits until its share of
+      // stage i+2 has landed.
       // prologue: all NST stages in flight; wait for stages 0 and 1
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < NST; ++j) dma_stage(j);
-      static_assert(2 * BPW * (NST - 2) < 64, "wait count out of range");
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 2)) : "memory");
+      static_assert(LPS * (NST - 2) < 64, "wait count out of range");
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 2)) : "memory");
       __syncthreads();
       fload(0, 0, 0);
 
@@ -399,21 +462,21 @@ gemm_nt(GemmParams p) {
             fload(cur ^ 1, bnext, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-          for (int ii = 0; ii < NBI; ++ii)
-  #pragma unroll
-            for (int jj = 0; jj < NBJ; ++jj) acc[ii][jj] = Mma<E>::run(fa[cur][ii], fb[cur][jj], acc[ii][jj]);
+          mma(cur);
           __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr ((SUB & 1) == 1) {
-  #pragma unroll
-          for (int b = 0; b < NBI; ++b) fa[0][b] = fa[1][b];
-  #pragma unroll
-          for (int b = 0; b < NBJ; ++b) fb[0][b] = fb[1][b];
+#pragma unroll
+          for (int pl = 0; pl < PL; ++pl) {
+#pragma unroll
+            for (int b = 0; b < NBI; ++b) fa[0][pl][b] = fa[1][pl][b];
+#pragma unroll
+            for (int b = 0; b < NBJ; ++b) fb[0][pl][b] = fb[1][pl][b];
+          }
         }
         // stage i+2 must be complete before the barrier; stages i+3 .. i+NST-1
         // may still be in flight
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BPW * (NST - 3)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 3)) : "memory");
         __syncthreads();
         dma_stage(i + NST);
         buf = bnext;
@@ -444,20 +507,15 @@ gemm_nt(GemmParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[ib][jb][4 * g + q];
           if (!diag_tile) {
-            S sv[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              sv[q] = E::st(v[q]);
-              Cm[(i0 + q) * p.ldc + j] = sv[q];
-              if (C2m) C2m[(i0 + q) * p.ldc + j] = sv[q];
+              St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
+              if (C2m) St::put(C2m, (i0 + q) * p.ldc + j, p.pC2, v[q]);
             }
             // mirrored copy: four consecutive entries of row j
-            if (ESZ == 2) {
-              uint2 pk;
-              pk.x = static_cast<uint32_t>(sv[0]) | (static_cast<uint32_t>(sv[1]) << 16);
-              pk.y = static_cast<uint32_t>(sv[2]) | (static_cast<uint32_t>(sv[3]) << 16);
-              *reinterpret_cast<uint2 *>(Cm + j * p.ldc + i0) = pk;
-              if (C2m) *reinterpret_cast<uint2 *>(C2m + j * p.ldc + i0) = pk;
+            if constexpr (ESZ == 2) {
+              St::put4(Cm, j * p.ldc + i0, p.pC, v);
+              if (C2m) St::put4(C2m, j * p.ldc + i0, p.pC2, v);
             } else {
               float4 pk = make_float4(v[0], v[1], v[2], v[3]);
               *reinterpret_cast<float4 *>(Cm + j * p.ldc + i0) = pk;
@@ -471,13 +529,13 @@ gemm_nt(GemmParams p) {
               const int64_t i = i0 + q;
               if (i > j) continue;
               const float dg = (i == j && i < p.n_real) ? 1.0f : 0.0f;
-              const S s1 = E::st(v[q] + dg * p.diag1);
-              Cm[i * p.ldc + j] = s1;
-              if (i != j) Cm[j * p.ldc + i] = s1;
+              const float v1 = v[q] + dg * p.diag1;
+              St::put(Cm, i * p.ldc + j, p.pC, v1);
+              if (i != j) St::put(Cm, j * p.ldc + i, p.pC, v1);
               if (C2m) {
-                const S s2 = E::st(v[q] + dg * p.diag2);
-                C2m[i * p.ldc + j] = s2;
-                if (i != j) C2m[j * p.ldc + i] = s2;
+                const float v2 = v[q] + dg * p.diag2;
+                St::put(C2m, i * p.ldc + j, p.pC2, v2);
+                if (i != j) St::put(C2m, j * p.ldc + i, p.pC2, v2);
               }
             }
           }
@@ -493,20 +551,15 @@ gemm_nt(GemmParams p) {
         for (int g = 0; g < 4; ++g) {
           const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
           const int64_t j = col_base + jb * 32 + lr;
-          S sv[4];
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[q] = p.alpha * acc[ib][jb][4 * g + q];
-            sv[q] = E::st(v[q]);
-            Cm[(i0 + q) * p.ldc + j] = sv[q];
+            St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
           }
           if (CTm) {
-            if (ESZ == 2) {
-              uint2 pk;
-              pk.x = static_cast<uint32_t>(sv[0]) | (static_cast<uint32_t>(sv[1]) << 16);
-              pk.y = static_cast<uint32_t>(sv[2]) | (static_cast<uint32_t>(sv[3]) << 16);
-              *reinterpret_cast<uint2 *>(CTm + j * p.ldct + i0) = pk;
+            if constexpr (ESZ == 2) {
+              St::put4(CTm, j * p.ldct + i0, p.pCT, v);
             } else {
               *reinterpret_cast<float4 *>(CTm + j * p.ldct + i0) = make_float4(v[0], v[1], v[2], v[3]);
             }
@@ -610,18 +663,20 @@ norm_partial(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int64_
 // ---------------------------------------------------------------------------
 // X_hat = X / (||X||_F + eps), rounded to the compute dtype, in both layouts
 // ---------------------------------------------------------------------------
-template <class TIn, class TCmp>
+// PL = 2 (split storage) also writes the lo planes X - hi, plane_h and
+// plane_t elements after the hi planes.
+template <class TIn, class TCmp, int PL>
 __global__ void __launch_bounds__(256)
 scale_transpose(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int64_t *row_idx,
                 const double *partials, int parts, double eps, void *Xh, void *XT, int64_t Np,
-                int64_t Mp) {
+                int64_t Mp, int64_t plane_h, int64_t plane_t) {
   using SI = typename TIn::S;
   using SC = typename TCmp::S;
   const int b = blockIdx.z;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
   __shared__ float inv_s;
-  __shared__ SC tileT[64][65];
+  __shared__ SC tileT[PL][64][65];
 
   if (threadIdx.x < 64) {  // norm stage 2, same fixed order in every workgroup
     double s = 0.0;
@@ -649,30 +704,36 @@ scale_transpose(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int
     }
     const SC sv = TCmp::st(v);
     Xhb[gr * Mp + gc] = sv;
-    tileT[col][r] = sv;
+    tileT[0][col][r] = sv;
+    if constexpr (PL == 2) {
+      const SC sl = TCmp::st(v - TCmp::ld(sv));
+      Xhb[plane_h + gr * Mp + gc] = sl;
+      tileT[PL - 1][col][r] = sl;
+    }
   }
   __syncthreads();
 #pragma unroll 4
   for (int rr = 0; rr < 16; ++rr) {
     const int c = rg + 4 * rr;
-    XTb[(c0 + c) * Np + r0 + col] = tileT[c][col];
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) XTb[pl * plane_t + (c0 + c) * Np + r0 + col] = tileT[pl][c][col];
   }
 }
 
 // Same operation for 16-bit input and compute types with m a multiple of 8:
 // 16-byte loads and stores on every global access (rows of X and X_hat, and
 // 8-row runs of each X^T row), transposed through a padded LDS tile.
-template <class TIn, class TCmp>
+template <class TIn, class TCmp, int PL>
 __global__ void __launch_bounds__(256)
 scale_transpose16(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int64_t *row_idx,
                   const double *partials, int parts, double eps, void *Xh, void *XT, int64_t Np,
-                  int64_t Mp) {
+                  int64_t Mp, int64_t plane_h, int64_t plane_t) {
   static_assert(sizeof(typename TIn::S) == 2 && sizeof(typename TCmp::S) == 2, "16-bit types only");
   const int b = blockIdx.z;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
   __shared__ float inv_s;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // 144-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t tile[PL][64][72];   // 144-byte rows
 
   if (threadIdx.x < 64) {  // norm stage 2, same fixed order in every workgroup
     double sum = 0.0;
@@ -698,26 +759,38 @@ scale_transpose16(const void *X, int64_t n, int64_t m, int64_t rows_eff, const i
       const int64_t src = row_idx ? row_idx[static_cast<int64_t>(b) * rows_eff + gr] : gr;
       if (src >= 0 && src < n) in = *reinterpret_cast<const u32x4 *>(Xb + src * m + gc);
     }
-    u32x4 o;
+    // each 32-bit word holds two consecutive elements (even one in the low half)
+    u32x4 o[PL];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = TCmp::st(TIn::ld(static_cast<uint16_t>(in[q] & 0xffffu)) * inv);
-      const uint32_t hi = TCmp::st(TIn::ld(static_cast<uint16_t>(in[q] >> 16)) * inv);
-      o[q] = lo | (hi << 16);
+      const float f0 = TIn::ld(static_cast<uint16_t>(in[q] & 0xffffu)) * inv;
+      const float f1 = TIn::ld(static_cast<uint16_t>(in[q] >> 16)) * inv;
+      const uint16_t h0 = TCmp::st(f0), h1 = TCmp::st(f1);
+      o[0][q] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+      if constexpr (PL == 2)
+        o[PL - 1][q] = static_cast<uint32_t>(TCmp::st(f0 - TCmp::ld(h0))) |
+                       (static_cast<uint32_t>(TCmp::st(f1 - TCmp::ld(h1))) << 16);
     }
-    *reinterpret_cast<u32x4 *>(Xhb + gr * Mp + gc) = o;
-    *reinterpret_cast<u32x4 *>(&tile[row][cv]) = o;
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+      *reinterpret_cast<u32x4 *>(Xhb + pl * plane_h + gr * Mp + gc) = o[pl];
+      *reinterpret_cast<u32x4 *>(&tile[pl][row][cv]) = o[pl];
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = threadIdx.x & 63;
     const int k = (threadIdx.x >> 6) + 4 * h;
-    u32x4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = static_cast<uint32_t>(tile[8 * k + 2 * q][c]) | (static_cast<uint32_t>(tile[8 * k + 2 * q + 1][c]) << 16);
-    *reinterpret_cast<u32x4 *>(XTb + (c0 + c) * Np + r0 + 8 * k) = o;
+    for (int pl = 0; pl < PL; ++pl) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = static_cast<uint32_t>(tile[pl][8 * k + 2 * q][c]) |
+               (static_cast<uint32_t>(tile[pl][8 * k + 2 * q + 1][c]) << 16);
+      *reinterpret_cast<u32x4 *>(XTb + pl * plane_t + (c0 + c) * Np + r0 + 8 * k) = o;
+    }
   }
 }
 
@@ -750,15 +823,15 @@ check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <class E, int TILE>
+template <class E, int TILE, int PL = 1>
 static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
   const int grid = p.tiles_per_mat * p.batch;
   if (grid <= 0) return hipSuccess;
   constexpr int nt = WaveLayout<TILE>::THREADS;
   switch (mode) {
-    case MODE_SYM: gemm_nt<E, TILE, MODE_SYM><<<grid, nt, 0, s>>>(p); break;
-    case MODE_GEN: gemm_nt<E, TILE, MODE_GEN><<<grid, nt, 0, s>>>(p); break;
-    default: gemm_nt<E, TILE, MODE_FINAL><<<grid, nt, 0, s>>>(p); break;
+    case MODE_SYM: gemm_nt<E, TILE, MODE_SYM, PL><<<grid, nt, 0, s>>>(p); break;
+    case MODE_GEN: gemm_nt<E, TILE, MODE_GEN, PL><<<grid, nt, 0, s>>>(p); break;
+    default: gemm_nt<E, TILE, MODE_FINAL, PL><<<grid, nt, 0, s>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -766,17 +839,20 @@ static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
 hipError_t launch_gemm(int dt, int tile, int mode, const GemmParams &p, hipStream_t s) {
   if (dt == DT_BF16) return tile == 256 ? launch_gemm_t<EBF16, 256>(mode, p, s) : launch_gemm_t<EBF16, 128>(mode, p, s);
   if (dt == DT_F16) return tile == 256 ? launch_gemm_t<EF16, 256>(mode, p, s) : launch_gemm_t<EF16, 128>(mode, p, s);
+  if (dt == DT_BF16X3) return launch_gemm_t<EBF16, 128, 2>(mode, p, s);   // split planes: 128-edge tiles
   return launch_gemm_t<EF32, 128>(mode, p, s);   // fp32 always uses 128-edge tiles
 }
 
 const char *gemm_kernel_name(int dt, int tile, int mode) {
-  static const char *names[3][2][3] = {
+  static const char *names[4][2][3] = {
       {{"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"},
        {"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"}},
       {{"gemm_nt<bf16,128,sym>", "gemm_nt<bf16,128,gen>", "gemm_nt<bf16,128,final>"},
        {"gemm_nt<bf16,256,sym>", "gemm_nt<bf16,256,gen>", "gemm_nt<bf16,256,final>"}},
       {{"gemm_nt<f16,128,sym>", "gemm_nt<f16,128,gen>", "gemm_nt<f16,128,final>"},
-       {"gemm_nt<f16,256,sym>", "gemm_nt<f16,256,gen>", "gemm_nt<f16,256,final>"}}};
+       {"gemm_nt<f16,256,sym>", "gemm_nt<f16,256,gen>", "gemm_nt<f16,256,final>"}},
+      {{"gemm_nt<bf16x3,128,sym>", "gemm_nt<bf16x3,128,gen>", "gemm_nt<bf16x3,128,final>"},
+       {"gemm_nt<bf16x3,128,sym>", "gemm_nt<bf16x3,128,gen>", "gemm_nt<bf16x3,128,final>"}}};
   return names[dt][tile == 256 ? 1 : 0][mode];
 }
 
@@ -793,35 +869,43 @@ hipError_t launch_norm_partial(int io, const void *X, int64_t batch, int64_t n, 
 template <class TIn>
 static void st_dispatch(int cdt, dim3 grid, hipStream_t s, const void *X, int64_t n, int64_t m,
                         int64_t rows_eff, const int64_t *row_idx, const double *partials,
-                        int parts, double eps, void *Xh, void *XT, int64_t Np, int64_t Mp) {
+                        int parts, double eps, void *Xh, void *XT, int64_t Np, int64_t Mp,
+                        int64_t ph, int64_t pt) {
   if (cdt == DT_BF16)
-    scale_transpose<TIn, EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    scale_transpose<TIn, EBF16, 1><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
+  else if (cdt == DT_BF16X3)
+    scale_transpose<TIn, EBF16, 2><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   else if (cdt == DT_F16)
-    scale_transpose<TIn, EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    scale_transpose<TIn, EF16, 1><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   else
-    scale_transpose<TIn, EF32><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+    scale_transpose<TIn, EF32, 1><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
 }
 
 hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch, int64_t n,
                                   int64_t m, int64_t rows_eff, const int64_t *row_idx,
                                   const double *partials, int parts, double eps, void *Xh,
-                                  void *XT, int64_t Np, int64_t Mp, hipStream_t s) {
+                                  void *XT, int64_t Np, int64_t Mp, int64_t ph, int64_t pt,
+                                  hipStream_t s) {
   dim3 grid(static_cast<unsigned>(Mp / 64), static_cast<unsigned>(Np / 64), static_cast<unsigned>(batch));
   const bool vec = (m % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && io != DT_F32 && cdt != DT_F32;
   if (vec) {
-    if (io == DT_BF16 && cdt == DT_BF16)
-      scale_transpose16<EBF16, EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
-    else if (io == DT_BF16)
-      scale_transpose16<EBF16, EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
-    else if (cdt == DT_BF16)
-      scale_transpose16<EF16, EBF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
-    else
-      scale_transpose16<EF16, EF16><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+#define GNS_ST16(TI, TC, PL) \
+  scale_transpose16<TI, TC, PL><<<grid, 256, 0, s>>>(X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt)
+    if (io == DT_BF16) {
+      if (cdt == DT_BF16) GNS_ST16(EBF16, EBF16, 1);
+      else if (cdt == DT_BF16X3) GNS_ST16(EBF16, EBF16, 2);
+      else GNS_ST16(EBF16, EF16, 1);
+    } else {
+      if (cdt == DT_BF16) GNS_ST16(EF16, EBF16, 1);
+      else if (cdt == DT_BF16X3) GNS_ST16(EF16, EBF16, 2);
+      else GNS_ST16(EF16, EF16, 1);
+    }
+#undef GNS_ST16
     return hipGetLastError();
   }
-  if (io == DT_BF16) st_dispatch<EBF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
-  else if (io == DT_F16) st_dispatch<EF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
-  else st_dispatch<EF32>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp);
+  if (io == DT_BF16) st_dispatch<EBF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
+  else if (io == DT_F16) st_dispatch<EF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
+  else st_dispatch<EF32>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   return hipGetLastError();
 }
 

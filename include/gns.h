@@ -59,9 +59,17 @@ extern "C" {
 #define GNS_ABI_VERSION 1
 
 typedef enum {
-  GNS_F32 = 0,  /* IEEE binary32                          */
-  GNS_BF16 = 1, /* bfloat16 (8-bit exponent, 7-bit mantissa) */
-  GNS_F16 = 2   /* IEEE binary16                          */
+  GNS_F32 = 0,   /* IEEE binary32                          */
+  GNS_BF16 = 1,  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+  GNS_F16 = 2,   /* IEEE binary16                          */
+  GNS_BF16X3 = 3 /* compute type only: every matrix the method forms is kept
+                    as a pair of bf16 planes hi + lo (hi = bf16(v), lo =
+                    bf16(v - hi)), and every product sums the three bf16
+                    MFMA terms hi*hi + hi*lo + lo*hi in fp32.  About 16
+                    significant bits at three times the bf16 MFMA work: the
+                    accurate mode for ill-conditioned inputs, where forming
+                    X X^T squares the condition number ("Dion3", Appendix
+                    B.2.2).  Uses 128-edge tiles. */
 } gns_dtype;
 
 typedef enum {
@@ -127,9 +135,11 @@ size_t gns_standard_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int6
  *              selected ones) must have rows <= m (the pages' n <= m).
  *   io_dtype   dtype of X and out.
  *   compute_dtype  dtype of the matrix products' operands (GNS_BF16 or
- *              GNS_F16: MFMA with fp32 accumulation; GNS_F32: fp32 MFMA).
+ *              GNS_F16: MFMA with fp32 accumulation; GNS_F32: fp32 MFMA;
+ *              GNS_BF16X3: hi/lo bf16 pairs, three bf16 MFMAs per product).
  *              Every product accumulates in fp32, applies its a/b/c terms
- *              in fp32 and rounds its result once to compute_dtype.
+ *              in fp32 and rounds its result once to compute_dtype (for
+ *              GNS_BF16X3: splits it once into hi and lo).
  *   coeffs     (host) T x 3 doubles, row t = (a_t, b_t, c_t) of
  *              p_t(x) = a_t x + b_t x^3 + c_t x^5 (used as given: a safety
  *              factor s is applied by the caller as (a/s, b/s^3, c/s^5),

@@ -50,6 +50,10 @@ def test_workspace_sizes():
     assert gns.gram_workspace_bytes(gns.GNS_BF16, 1, 10, 5) == 0          # rows > m
     assert gns.gram_workspace_bytes(7, 1, 10, 20) == 0                     # bad dtype
     assert gns.standard_workspace_bytes(gns.GNS_F32, 1, 64, 256) > 0
+    # split storage: two planes of every region, 128-edge tiles
+    x3 = gns.gram_workspace_bytes(gns.GNS_BF16X3, 2, 300, 700)
+    assert x3 >= 2 * 2 * 2 * (3 * 384 * 768 + 5 * 384 * 384)
+    assert gns.standard_workspace_bytes(gns.GNS_BF16X3, 2, 300, 700) > 0
     # ragged shapes are padded to whole tiles
     small = gns.gram_workspace_bytes(gns.GNS_F32, 1, 1, 1)
     assert small >= 4 * (3 * 128 * 128 + 5 * 128 * 128)
@@ -78,6 +82,7 @@ def _gram(X=FAKE, out=FAKE + 1 << 20, batch=1, n=4, m=8, io=1, cdt=1, coeffs=Non
 def test_gram_argument_errors():
     assert _gram(io=5) == E["DTYPE"]
     assert _gram(cdt=9) == E["DTYPE"]
+    assert _gram(io=gns.GNS_BF16X3) == E["DTYPE"]     # a compute type only
     assert _gram(n=0) == E["SHAPE"]
     assert _gram(n=9, m=8) == E["SHAPE"]                  # n > m
     assert _gram(row_idx=FAKE, k=0) == E["SHAPE"]

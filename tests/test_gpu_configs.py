@@ -11,34 +11,41 @@ from gram_newton_schulz_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def test_config2_logspectrum_f16_compute():
+def test_config2_logspectrum():
     """16 x 1024x4096, singular values log-uniform in [1e-4, 1].  Forming X X^T
-    squares the condition number, so bf16 products lose the small singular
-    values; fp16 products (the pages' default precision) keep the error
-    within the bound."""
+    squares the condition number, so plain bf16 products lose the small
+    singular values; the split-bf16 compute type (hi/lo bf16 pairs, three
+    bf16 MFMAs per product) and fp16 products (the pages' default precision)
+    keep the error within the bound."""
     gns = need_gpu()
     X = synth.workload_batch(2)
     X64 = synth.as_f64(X)
-    say("config2 f16 compute")
-    out16 = gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=torch.float16)
-    out_bf = gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=torch.bfloat16)
+    say("config2 bf16x3 / f16 / bf16 compute")
+    outs = {
+        "bf16x3": gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,), compute_dtype="bf16x3"),
+        "f16": gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,), compute_dtype=torch.float16),
+        "bf16": gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,), compute_dtype=torch.bfloat16),
+    }
     torch.cuda.synchronize()
     ref = np.stack([oracle_gram(X64[b]) for b in range(X.shape[0])])
-    e16 = per_matrix_rel(synth.as_f64(out16), ref)
-    ebf = per_matrix_rel(synth.as_f64(out_bf), ref)
-    say(f"  f16 max {max(e16):.4g}  bf16 max {max(ebf):.4g}")
-    assert max(e16) <= TOL_HALF
-    assert max(ebf) < 0.5          # bf16 products: degraded but not diverged
+    err = {c: max(per_matrix_rel(synth.as_f64(o), ref)) for c, o in outs.items()}
+    say("  max rel errs", err)
+    assert err["bf16x3"] <= TOL_HALF
+    assert err["f16"] <= TOL_HALF
+    assert err["bf16"] < 0.5          # plain bf16 products: degraded but not diverged
 
 
 def test_config3_dense_mlp():
-    """8 x 4096x16384 bf16 (aspect ratio 4): Gram NS and standard NS, matrices 0 and 7."""
+    """8 x 4096x16384 bf16 (aspect ratio 4): Gram NS (bf16 and split-bf16
+    compute) and standard NS, matrices 0 and 7."""
     gns = need_gpu()
     X = synth.workload_batch(3)
     say("config3 upload")
     Xd = X.cuda()
     say("config3 gram")
     g = gns.gram_ns_batched(Xd, NS5, restarts=(2,))
+    say("config3 gram bf16x3")
+    g3 = gns.gram_ns_batched(Xd, NS5, restarts=(2,), compute_dtype="bf16x3")
     say("config3 standard")
     s = gns.standard_ns_batched(Xd, NS5)
     torch.cuda.synchronize()
@@ -46,9 +53,10 @@ def test_config3_dense_mlp():
         say(f"  oracle matrix {b}")
         ref = oracle_gram(synth.as_f64(X[b]))
         eg = rel_err(synth.as_f64(g[b]), ref)
+        e3 = rel_err(synth.as_f64(g3[b]), ref)
         es = rel_err(synth.as_f64(s[b]), ref)
-        say(f"  matrix {b}: gram {eg:.4g} standard {es:.4g}")
-        assert eg <= TOL_HALF and es <= TOL_HALF
+        say(f"  matrix {b}: gram {eg:.4g} gram bf16x3 {e3:.4g} standard {es:.4g}")
+        assert eg <= TOL_HALF and es <= TOL_HALF and e3 <= TOL_HALF
     assert torch.isfinite(g).all()
 
 

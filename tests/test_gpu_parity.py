@@ -13,7 +13,7 @@ from gram_newton_schulz_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "bf16x3": "bf16x3"}
 
 
 def _inputs(B, n, m, io, seed, dist="normal"):
@@ -23,6 +23,7 @@ def _inputs(B, n, m, io, seed, dist="normal"):
 
 def _tol(cdt):
     return TOL_F32 if cdt == "f32" else TOL_HALF
+
 
 
 def _run(gns, algo, Xd, cdt, **kw):
@@ -50,7 +51,8 @@ def test_config1_fp32():
 @pytest.mark.parametrize("tile", [128, 256])
 @pytest.mark.parametrize("algo", ["gram", "standard"])
 @pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("bf16", "f16"), ("f32", "f32"),
-                                    ("f16", "f16"), ("f32", "bf16")])
+                                    ("f16", "f16"), ("f32", "bf16"), ("bf16", "bf16x3"),
+                                    ("f32", "bf16x3")])
 def test_ragged_parity(tile, algo, io, cdt):
     gns = need_gpu()
     B, n, m = 3, 300, 700          # 3 x 6 tiles of 128 with ragged tails
@@ -106,7 +108,7 @@ def test_distinct_coefficients_per_iteration():
 
 
 @pytest.mark.parametrize("algo", ["gram", "standard"])
-@pytest.mark.parametrize("cdt", ["bf16", "f32"])
+@pytest.mark.parametrize("cdt", ["bf16", "f32", "bf16x3"])
 def test_row_subset(algo, cdt):
     """Dion3 rows: selected rows orthogonalised as one k x m matrix, the others
     left bit-exact."""
@@ -298,3 +300,23 @@ def test_split_orders_against_caller_stream():
     s.synchronize()
     assert torch.equal(out, ref)
     assert torch.equal(total, ref.float().sum(dim=(1, 2)))
+
+
+def test_split_planes_tighter_than_bf16():
+    """The split-bf16 compute type keeps about 16 significant bits in every
+    stored iterate: on a log-uniform spectrum it must beat plain bf16 by a
+    wide margin and stay close to the fp32 path."""
+    gns = need_gpu()
+    B, n, m = 2, 256, 1024
+    # fp32 input and output, so that no output rounding hides the difference
+    X = synth.batch(B, n, m, seed=25, dist="logspec", dtype=torch.float32)
+    X64 = synth.as_f64(X)
+    say("split planes vs bf16 vs fp32, log spectrum 256x1024, fp32 I/O")
+    outs = {c: gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=DT[c]) for c in ("bf16", "bf16x3", "f32")}
+    torch.cuda.synchronize()
+    ref = np.stack([oracle_gram(X64[b]) for b in range(B)])
+    err = {c: max(per_matrix_rel(synth.as_f64(o), ref)) for c, o in outs.items()}
+    say("  errs", err)
+    assert err["bf16x3"] <= 1e-3
+    assert err["bf16x3"] < 0.25 * err["bf16"]
+    assert err["f32"] <= TOL_F32
