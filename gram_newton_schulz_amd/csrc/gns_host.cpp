@@ -182,6 +182,20 @@ void set_scale(GemmParams *p, float alpha, float beta) {
   }
 }
 
+// Runs of tiles dealt to one XCD (the kernel's xcd_chunk): one matrix per
+// run with xpm = 1, else 1/xpm of a matrix so that xpm XCDs share each
+// matrix.  Falls back to one contiguous run per XCD when the sizes do not
+// divide.
+int xcd_chunk(int64_t tiles_per_mat, int64_t batch, int xpm) {
+  const int64_t S = ((tiles_per_mat * batch) & ~int64_t(7)) / 8;
+  if (S == 0) return 1;
+  if (xpm > 1 && tiles_per_mat % xpm == 0) {
+    const int64_t c = tiles_per_mat / xpm;
+    if (S % c == 0) return static_cast<int>(c);
+  }
+  return static_cast<int>(S);
+}
+
 GemmParams base_params(const Ctx &c) {
   GemmParams p;
   std::memset(&p, 0, sizeof(p));
@@ -202,6 +216,7 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.K = static_cast<int>(N);
   p.tiles_m = p.tiles_n = nt;
   p.tiles_per_mat = nt * (nt + 1) / 2;
+  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
   set_scale(&p, alpha, beta);
   if (D) { p.DT = D; p.lddt = N; p.sDT = c.sq_stride(); }   // D is symmetric
   p.C = C; p.ldc = N; p.sC = c.sq_stride();
@@ -228,6 +243,7 @@ gns_status syrk(const Ctx &c, void *R) {
   p.K = static_cast<int>(M);
   p.tiles_m = p.tiles_n = nt;
   p.tiles_per_mat = nt * (nt + 1) / 2;
+  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 1);
   p.C = R; p.ldc = N; p.sC = c.sq_stride();
   p.pA = p.pB = c.plane_rect();
   p.pC = c.plane_sq();
@@ -254,6 +270,7 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   p.K = static_cast<int>(N);
   p.tiles_m = tm; p.tiles_n = tn;
   p.tiles_per_mat = tm * tn;
+  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
   set_scale(&p, 1.0f, beta);
   // the beta term reads X through its transposed copy, the B operand
   if (beta != 0.0f) { p.DT = XT_in; p.lddt = N; p.sDT = c.rect_stride(); }

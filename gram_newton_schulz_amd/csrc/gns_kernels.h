@@ -38,6 +38,8 @@ struct GemmParams {
   int tiles_m, tiles_n;             // output tiles per matrix along rows / cols
   int tiles_per_mat;                // sym: tiles_m*(tiles_m+1)/2
   int batch;
+  int xcd_chunk;                    // tiles per run dealt to one XCD (see gemm_nt);
+                                    // must divide (grid & ~7) / 8
   float alpha;                      // C = alpha * (acc)
   float init_scale;                 // acc starts at init_scale * D
   const void *DT; int64_t lddt, sDT;  // D read transposed: D(i,j) = DT[j*lddt + i];

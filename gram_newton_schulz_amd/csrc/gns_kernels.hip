@@ -231,13 +231,23 @@ gemm_nt(GemmParams p) {
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STB];
 
-  // Workgroup -> tile.  Consecutive tiles share an operand panel; the
-  // hardware deals workgroups round-robin over the 8 XCDs, so regroup ids to
-  // keep runs of consecutive tiles on one XCD (one L2).
+  // Workgroup -> tile.  Consecutive tiles share operand panels; the hardware
+  // deals workgroups round-robin over the 8 XCDs (one L2 each), so ids are
+  // regrouped: the logical tile order is cut into runs of xcd_chunk tiles,
+  // run r goes to XCD r % 8, and each XCD works through its runs in order.
+  // Long runs keep one matrix per XCD (most L2 reuse); runs of a fraction of
+  // a matrix let several XCDs work on the same matrix at once, which keeps
+  // the set of matrices in flight small enough for the shared last-level
+  // cache.
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int G8 = G & ~7;
-  const int lw = (w < G8) ? ((w & 7) * (G8 >> 3) + (w >> 3)) : w;
+  int lw = w;
+  if (w < G8 && p.xcd_chunk > 0) {
+    const int c = p.xcd_chunk, slot = w >> 3;
+    lw = ((slot / c) * 8 + (w & 7)) * c + slot % c;
+    if (lw >= G8) lw = w;   // only when xcd_chunk does not divide G8 / 8 (a host error)
+  }
   const int mat = lw / p.tiles_per_mat;
   const int t = lw - mat * p.tiles_per_mat;
   int ti, tj;
