@@ -7,12 +7,14 @@
 //                       transposed [m][n] (zero padded to whole tiles); the
 //                       second stage of the norm reduction runs in its prologue.
 // * gemm_nt          -- C = alpha * A B^T + beta * D on bf16/fp16 (32x32x16)
-//                       or fp32 (32x32x2) MFMA with fp32 accumulation.  A
-//                       256x256 (or 128x128) workgroup tile, four waves in a
-//                       2x2 grid, 64-element (128-byte) K steps staged through
-//                       double-buffered, XOR-swizzled LDS.  Symmetric results
-//                       compute only the upper tiles and mirror them ("Dion3:
-//                       Full-Stack Orthogonal Updates", §5 and App. C.1-C.2).
+//                       or fp32 (32x32x2) MFMA with fp32 accumulation, or on
+//                       split hi/lo bf16 pairs (three bf16 MFMAs per product).
+//                       256x256 workgroup tiles with 8 waves in ping-pong, or
+//                       128x128 tiles with 4 waves; operands reach LDS by
+//                       LDS-DMA buffer loads into a 5-stage ring of 32-element
+//                       K stages, XOR-swizzled.  Symmetric results compute only
+//                       the upper tiles and mirror them ("Dion3: Full-Stack
+//                       Orthogonal Updates", §5 and App. C.1-C.2).
 //
 // Every product of the method is written as A B^T with both operands stored
 // row-major along the contraction index: X X^T directly; products of two
