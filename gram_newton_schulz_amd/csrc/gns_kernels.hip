@@ -503,6 +503,51 @@ gemm_nt(GemmParams p) {
   const int64_t row_base = static_cast<int64_t>(ti) * TILE + wr;
   const int64_t col_base = static_cast<int64_t>(tj) * TILE + wc;
 
+  // Transposed outputs (the mirrored half of a symmetric result, the
+  // transposed copy of a general one) take four consecutive rows per lane,
+  // i.e. 16-byte pieces of 32 different rows per store.  With 256-edge tiles
+  // and 16-bit types they are staged through LDS instead: each wave writes
+  // its accumulators transposed into a tile with 528-byte rows, and the whole
+  // workgroup then stores that tile as full 512-byte rows.
+  constexpr bool kStageT = (TILE == 256 && PL == 1 && ESZ == 2);
+  constexpr int TP = TILE + 8;                         // staged row pitch (elements)
+  static_assert(!kStageT || TILE * TP * 2 <= NST * STB, "staging tile fits the ring");
+  S *const Tt = reinterpret_cast<S *>(lds);
+  // Tt[c][r] = value of tile row r, tile column c
+  auto stage_transposed = [&]() {
+    // every wave is past its last read of the ring and every DMA has landed
+    __syncthreads();
+#pragma unroll
+    for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < NBJ; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = wc + jb * 32 + lr;
+          const int r0 = wr + ib * 32 + 8 * g + 4 * lh;
+          uint32_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = E::st(p.alpha * acc[ib][jb][4 * g + q]);
+          uint2 pk;
+          pk.x = h[0] | (h[1] << 16);
+          pk.y = h[2] | (h[3] << 16);
+          *reinterpret_cast<uint2 *>(Tt + c * TP + r0) = pk;
+        }
+    __syncthreads();
+  };
+  // row c of the staged tile -> row (tj*TILE + c), columns ti*TILE .. of dst
+  auto store_transposed = [&](S *dst, int64_t ld) {
+    constexpr int CHUNKS = TILE * TILE / 8;            // 16-byte pieces
+#pragma unroll 4
+    for (int k = tid; k < CHUNKS; k += NT) {
+      const int c = k / (TILE / 8);
+      const int r = (k % (TILE / 8)) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(Tt + c * TP + r);
+      *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(tj) * TILE + c) * ld +
+                                 static_cast<int64_t>(ti) * TILE + r) = v;
+    }
+  };
+
   if (MODE == MODE_SYM) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *C2m = p.C2 ? static_cast<S *>(p.C2) + static_cast<int64_t>(mat) * p.sC2 : nullptr;
@@ -524,8 +569,10 @@ gemm_nt(GemmParams p) {
               St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
               if (C2m) St::put(C2m, (i0 + q) * p.ldc + j, p.pC2, v[q]);
             }
-            // mirrored copy: four consecutive entries of row j
-            if constexpr (ESZ == 2) {
+            // mirrored copy: four consecutive entries of row j (staged
+            // through LDS below when kStageT)
+            if constexpr (kStageT) {
+            } else if constexpr (ESZ == 2) {
               St::put4(Cm, j * p.ldc + i0, p.pC, v);
               if (C2m) St::put4(C2m, j * p.ldc + i0, p.pC2, v);
             } else {
@@ -552,6 +599,13 @@ gemm_nt(GemmParams p) {
             }
           }
         }
+    if constexpr (kStageT) {
+      if (!diag_tile) {
+        stage_transposed();
+        store_transposed(Cm, p.ldc);
+        if (C2m) store_transposed(C2m, p.ldc);
+      }
+    }
   } else if (MODE == MODE_GEN) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *CTm = p.CT ? static_cast<S *>(p.CT) + static_cast<int64_t>(mat) * p.sCT : nullptr;
@@ -570,13 +624,21 @@ gemm_nt(GemmParams p) {
             St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
           }
           if (CTm) {
-            if constexpr (ESZ == 2) {
+            if constexpr (kStageT) {
+              // staged through LDS below
+            } else if constexpr (ESZ == 2) {
               St::put4(CTm, j * p.ldct + i0, p.pCT, v);
             } else {
               *reinterpret_cast<float4 *>(CTm + j * p.ldct + i0) = make_float4(v[0], v[1], v[2], v[3]);
             }
           }
         }
+    if constexpr (kStageT) {
+      if (CTm) {
+        stage_transposed();
+        store_transposed(CTm, p.ldct);
+      }
+    }
   } else {  // MODE_FINAL
     const int64_t *ridx = p.row_idx ? p.row_idx + static_cast<int64_t>(mat) * p.rows_eff : nullptr;
     const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
