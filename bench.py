@@ -52,10 +52,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def short_kernel(name):
+    """rocprofv3 kernel name -> the library's short name, e.g.
+    'gns::gemm_nt<gns::EBF16, 256, 0, 1>' -> 'gemm_nt<bf16,256,sym>' (the last
+    template argument is the plane count: 2 means split bf16, 'bf16x3')."""
     import re
-    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)>", name)
+    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)(?:, (\d))?>", name)
     if m:
-        return f"gemm_nt<{m.group(1).lower()},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
+        dt = m.group(1).lower()
+        if m.group(4) == "2":
+            dt = "bf16x3"
+        return f"gemm_nt<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
     for k in ("norm_partial", "scale_transpose", "check_rows"):
         if k in name:
             return k
