@@ -33,7 +33,11 @@ Reading of the pages taken here (each also listed in the design notes):
 * "restart after iteration s" means: before computing Z_{s+1}, replace X by
   Q_s X, re-form R from it and reset Q to I (X is not renormalised);
 * the coefficient triple of iteration t is (a_t, b_t, c_t) with
-  p_t(x) = a_t x + b_t x^3 + c_t x^5 and h_t(y) = a_t + b_t y + c_t y^2.
+  p_t(x) = a_t x + b_t x^3 + c_t x^5 and h_t(y) = a_t + b_t y + c_t y^2;
+* the pages take n <= m without loss of generality; a tall X (n > m) is
+  orthogonalised through its transpose: the iteration runs on X^T and the
+  result is transposed back (polar(X) = polar(X^T)^T, and each odd
+  polynomial step commutes with transposition).
 """
 from __future__ import annotations
 
@@ -126,8 +130,8 @@ def standard_ns(X, coeffs, eps=EPS) -> np.ndarray:
     """
     X = _as_work(X)
     n, m = X.shape
-    if n > m:
-        raise ValueError("Algorithm 1 assumes n <= m")
+    if n > m:                        # n <= m without loss of generality
+        return standard_ns(X.T, coeffs, eps).T
     exact = _is_exact(X)
     Y = frobenius_normalize(X, eps)
     for a, b, c in _coeff_list(coeffs, exact):
@@ -159,11 +163,14 @@ def gram_ns_trace(X, coeffs, restarts: Iterable[int] = (2,),
 
     Returns (output, trace) where trace is a list of dicts with the values of
     R, Z, Q after each iteration (and the restarted X when one happens).
+    A tall X (n > m) runs on X^T; the output is transposed back and the
+    trace holds the m x m iterates of the transposed problem.
     """
     X = _as_work(X)
     n, m = X.shape
-    if n > m:
-        raise ValueError("Gram Newton-Schulz assumes n <= m")
+    if n > m:                        # n <= m without loss of generality
+        out, trace = gram_ns_trace(X.T, coeffs, restarts, algebra, eps)
+        return out.T, trace
     exact = _is_exact(X)
     cl = _coeff_list(coeffs, exact)
     T = len(cl)

@@ -168,7 +168,9 @@ def pin_spectral(O):
     sched = load_schedules()
     ns5 = [tuple(float(v) for v in sched["muon_ns5"])] * 5
     mixed = [tuple(float(v) for v in row) for row in SCHED4] + [ns5[0]]
-    for seed, (n, m) in enumerate([(24, 60), (17, 17), (9, 40)]):
+    # wide, square, and tall shapes (a tall X goes through its transpose; the
+    # closed form uses the SVD of the tall matrix itself)
+    for seed, (n, m) in enumerate([(24, 60), (17, 17), (9, 40), (40, 9), (60, 24)]):
         X = 3.0 * _randn((n, m), seed)
         for co in (ns5, mixed):
             cf = _closed_form(X, co)
@@ -194,6 +196,9 @@ def pin_polar_limit(O):
     assert _rel(O.standard_ns(X, conv), polar) <= 1e-12
     assert _rel(O.gram_ns(X, conv, restarts=(5, 10, 15, 20, 25, 30, 35)), polar) <= 1e-12
     assert _rel(O.polar(X), polar) <= 1e-12
+    # the tall matrix X^T = V S U^T has polar factor V U^T
+    assert _rel(O.standard_ns(X.T, conv), polar.T) <= 1e-12
+    assert _rel(O.gram_ns(X.T, conv, restarts=(5, 10, 15, 20, 25, 30, 35)), polar.T) <= 1e-12
 
 
 # ---------------------------------------------------------------------------

@@ -35,6 +35,8 @@ MUTATIONS = {
     "flops restart": ("n_restarts * (3.0 * m * n * n - 3.0 * n ** 3)", "n_restarts * (3.0 * m * n * n)"),
     "dion3 keeps X rows": ("out[rows, :] = gram_ns(X[rows, :]", "out[rows, :] = gram_ns(X[sorted(rows), :]"),
     "identity wrong": ("return np.eye(n, dtype=np.float64)", "return 2.0 * np.eye(n, dtype=np.float64)"),
+    "tall standard not transposed back": ("return standard_ns(X.T, coeffs, eps).T", "return standard_ns(X.T, coeffs, eps)"),
+    "tall gram not transposed back": ("return out.T, trace", "return out, trace"),
 }
 
 
