@@ -31,9 +31,16 @@ bool valid_compute(int dt) { return valid_dtype(dt) || dt == GNS_BF16X3; }
 // --------------------------------------------------------------------------
 // problem plan: tile edge, padded sizes, workspace layout
 // --------------------------------------------------------------------------
+// The method works on Y with r <= c: Y = X_hat (r = rows, c = m) for a wide
+// or square problem, Y = X_hat^T (r = m, c = rows) for a tall one
+// (polar(X) = polar(X^T)^T; "Dion3" §2 assumes n <= m without loss of
+// generality).  Buffers: xh = Y row-major [Np][Mp], xt = Y^T row-major [Mp][Np].
 struct Plan {
   int tile = 128;
-  int64_t batch = 0, rows = 0, m = 0, Np = 0, Mp = 0;
+  int64_t batch = 0, rows = 0, m = 0;  // the caller's (selected) rows and columns
+  int64_t r = 0, c = 0;                // short and long side of Y
+  bool tall = false;                   // rows > m
+  int64_t Np = 0, Mp = 0;              // r and c padded to whole tiles
   int parts = 1;
   int esz = 2;
   int planes = 1;                      // 2: split hi/lo storage (GNS_BF16X3)
@@ -62,15 +69,18 @@ int choose_parts(int64_t batch, int64_t rows) {
 // for 256-padded buffers so that any tile choice fits.
 bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, int tile_request,
                Plan *pl) {
-  if (!valid_compute(cdt) || batch < 0 || rows < 1 || m < rows) return false;
-  pl->tile = tile_request ? tile_request : choose_tile(cdt, batch, rows);
+  if (!valid_compute(cdt) || batch < 0 || rows < 1 || m < 1) return false;
+  pl->tall = rows > m;
+  pl->r = std::min(rows, m);
+  pl->c = std::max(rows, m);
+  pl->tile = tile_request ? tile_request : choose_tile(cdt, batch, pl->r);
   // the fp32 and split-plane kernels exist for 128-edge tiles only
   if (cdt == GNS_F32 || cdt == GNS_BF16X3) pl->tile = 128;
   pl->batch = batch;
   pl->rows = rows;
   pl->m = m;
-  pl->Np = round_up(rows, pl->tile);
-  pl->Mp = round_up(m, pl->tile);
+  pl->Np = round_up(pl->r, pl->tile);
+  pl->Mp = round_up(pl->c, pl->tile);
   // per-matrix element offsets stay within int range of the kernels' math
   if (pl->Np * pl->Mp > (int64_t(1) << 31)) return false;
   // operand panels (256 rows of a padded buffer) are addressed with 32-bit
@@ -201,7 +211,7 @@ GemmParams base_params(const Ctx &c) {
   std::memset(&p, 0, sizeof(p));
   p.batch = static_cast<int>(c.batch);
   p.alpha = 1.0f;
-  p.n_real = static_cast<int>(c.pl->rows);
+  p.n_real = static_cast<int>(c.pl->r);
   return p;
 }
 
@@ -223,7 +233,7 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.C2 = C2; p.sC2 = c.sq_stride();
   p.pA = p.pB = p.pDT = p.pC = p.pC2 = c.plane_sq();
   p.diag1 = diag1; p.diag2 = diag2;
-  const double n = static_cast<double>(c.pl->rows);
+  const double n = static_cast<double>(c.pl->r);
   const double bytes = c.batch * n * n * c.pl->esz * (3.0 + (D ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
   LaunchScope ls(c.s, what, gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), flops * c.batch,
                  bytes);
@@ -247,7 +257,7 @@ gns_status syrk(const Ctx &c, void *R) {
   p.C = R; p.ldc = N; p.sC = c.sq_stride();
   p.pA = p.pB = c.plane_rect();
   p.pC = c.plane_sq();
-  const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
+  const double n = static_cast<double>(c.pl->r), m = static_cast<double>(c.pl->c);
   LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), n * n * m * c.batch,
                  c.batch * (n * m + n * n) * c.pl->esz);
   hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, gns::MODE_SYM, p, c.s);
@@ -276,9 +286,20 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   if (beta != 0.0f) { p.DT = XT_in; p.lddt = N; p.sDT = c.rect_stride(); }
   p.pA = c.plane_sq();
   p.pB = p.pDT = p.pC = p.pCT = c.plane_rect();
-  const double n = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
+  const double n = static_cast<double>(c.pl->r), m = static_cast<double>(c.pl->c);
   double bytes = c.batch * (n * n + n * m) * c.pl->esz;
   if (final) {
+    if (c.pl->tall) {
+      // out = (S Y + beta Y)^T = Y^T S + beta Y^T, written in the caller's
+      // layout: A = Y^T rows, B = S (symmetric), the beta term read through
+      // Y itself
+      p.A = XT_in; p.lda = N; p.sA = c.rect_stride();
+      p.B = S; p.ldb = N; p.sB = c.sq_stride();
+      p.tiles_m = tn; p.tiles_n = tm;
+      if (beta != 0.0f) { p.DT = Xh; p.lddt = M; p.sDT = c.rect_stride(); }
+      p.pA = p.pDT = c.plane_rect();
+      p.pB = c.plane_sq();
+    }
     p.out = out; p.out_dtype = io_dtype; p.out_rows = n_total; p.out_cols = c.pl->m;
     p.rows_eff = c.pl->rows; p.row_idx = row_idx;
     bytes += c.batch * n * m * gns::dtype_size(io_dtype);
@@ -311,9 +332,15 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
   {
     LaunchScope ls(c.s, "scale_transpose", "scale_transpose", rows * m * c.batch,
                    c.batch * rows * m * (gns::dtype_size(io) + 2.0 * c.pl->esz));
+    // X_hat row-major [rows][m] and its transpose; for a tall problem X_hat is
+    // Y^T (the xt buffer) and its transpose is Y (the xh buffer)
+    void *dst_rows = c.pl->tall ? c.xt(0) : c.xh();
+    void *dst_cols = c.pl->tall ? c.xh() : c.xt(0);
+    const int64_t rows_pad = c.pl->tall ? c.pl->Mp : c.pl->Np;
+    const int64_t cols_pad = c.pl->tall ? c.pl->Np : c.pl->Mp;
     hipError_t e = gns::launch_scale_transpose(io, c.cdt, X, c.batch, n_total, c.pl->m, c.pl->rows,
                                                row_idx, partials, c.pl->parts, kEps,
-                                               c.xh(), c.xt(0), c.pl->Np, c.pl->Mp,
+                                               dst_rows, dst_cols, rows_pad, cols_pad,
                                                c.plane_rect(), c.plane_rect(), c.s);
     ls.done();
     if (e != hipSuccess) return GNS_E_HIP;
@@ -345,7 +372,6 @@ gns_status common_checks(const void *X, void *out, int64_t batch, int64_t n, int
   } else {
     *rows = n;
   }
-  if (*rows > m) return GNS_E_SHAPE;
   if (!coeffs) return GNS_E_NULL;
   if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
   for (int i = 0; i < 3 * T; ++i)
@@ -372,7 +398,7 @@ gns_status enqueue_standard(const Ctx &c, const void *X, void *out, int io, int6
   void *A = c.sq(0), *B = c.sq(1);
   void *XT[2] = {c.xt(0), c.xt(1)};
   int xcur = 0;
-  const double nn = static_cast<double>(pl.rows);
+  const double nn = static_cast<double>(pl.r);
   gns_status st;
   if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
   for (int t = 1; t <= T; ++t) {
@@ -404,7 +430,7 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
   void *XT[2] = {c.xt(0), c.xt(1)};
   int qcur = 0, xcur = 0;
   bool q_is_identity = true;
-  const double nn = static_cast<double>(c.pl->rows);
+  const double nn = static_cast<double>(c.pl->r);
   const double n3 = nn * nn * nn;
 
   if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;

@@ -1,7 +1,7 @@
 /*
  * gns.h -- C ABI of the MI355X (gfx950) Gram Newton-Schulz library.
  *
- * The library orthogonalises batches of n x m matrices (n <= m) the way the
+ * The library orthogonalises batches of n x m matrices the way the
  * Muon family of optimisers does: it approximates polar(X) = U V^T
  * ("Dion3: Full-Stack Orthogonal Updates", §2.1 Definition 1) with a fixed
  * number T of odd quintic steps p_t(x) = a_t x + b_t x^3 + c_t x^5
@@ -75,7 +75,7 @@ typedef enum {
 typedef enum {
   GNS_OK = 0,
   GNS_E_NULL = 1,      /* a required pointer is NULL                          */
-  GNS_E_SHAPE = 2,     /* n < 1, m < rows, k not in [1, n], or too large      */
+  GNS_E_SHAPE = 2,     /* n < 1, m < 1, k not in [1, n], or too large        */
   GNS_E_DTYPE = 3,     /* unknown dtype                                       */
   GNS_E_COEFF = 4,     /* T < 1, T > GNS_MAX_ITERS, or a non-finite coeff.    */
   GNS_E_RESTART = 5,   /* restart list not strictly increasing in [1, T-1]    */
@@ -115,7 +115,7 @@ const char *gns_status_str(gns_status s);
 /*
  * Workspace bytes that gns_gram_batched needs for this problem.
  *   rows = k when a row subset is used, else n.  Returns 0 for invalid
- *   arguments (rows < 1, m < rows, unknown dtype) and for batch == 0.
+ *   arguments (rows < 1, m < 1, unknown dtype) and for batch == 0.
  */
 size_t gns_gram_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int64_t rows, int64_t m);
 
@@ -131,8 +131,12 @@ size_t gns_standard_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int6
  *              element is written.  With a row subset only the selected rows
  *              are written; the others keep what the caller put there.
  *   batch      number of matrices (>= 0).
- *   n, m       matrix shape; the orthogonalised matrix (all rows, or the k
- *              selected ones) must have rows <= m (the pages' n <= m).
+ *   n, m       matrix shape (n, m >= 1).  The pages take rows <= m without
+ *              loss of generality; a tall problem (rows > m, rows = n or k)
+ *              is orthogonalised through its transpose, polar(X) =
+ *              polar(X^T)^T: the iteration runs on m x m Gram matrices of
+ *              X_hat^T (the transposed copy the normalisation writes anyway)
+ *              and the last product X_hat Q writes the caller's layout.
  *   io_dtype   dtype of X and out.
  *   compute_dtype  dtype of the matrix products' operands (GNS_BF16 or
  *              GNS_F16: MFMA with fp32 accumulation; GNS_F32: fp32 MFMA;

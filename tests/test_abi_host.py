@@ -47,7 +47,13 @@ def test_workspace_sizes():
     # X_hat, two transposed copies and five n x n iterates, bf16
     assert b >= 8 * 2 * (3 * 4096 * 16384 + 5 * 4096 * 4096)
     assert gns.gram_workspace_bytes(gns.GNS_BF16, 0, 4096, 16384) == 0
-    assert gns.gram_workspace_bytes(gns.GNS_BF16, 1, 10, 5) == 0          # rows > m
+    assert gns.gram_workspace_bytes(gns.GNS_BF16, 1, 0, 5) == 0           # no rows
+    assert gns.gram_workspace_bytes(gns.GNS_BF16, 1, 10, 0) == 0          # no columns
+    # a tall problem needs what its transpose needs, up to the norm partials
+    # (which follow the caller's rows)
+    tall = gns.gram_workspace_bytes(gns.GNS_BF16, 2, 700, 300)
+    wide = gns.gram_workspace_bytes(gns.GNS_BF16, 2, 300, 700)
+    assert tall > 0 and abs(tall - wide) < 16384
     assert gns.gram_workspace_bytes(7, 1, 10, 20) == 0                     # bad dtype
     assert gns.standard_workspace_bytes(gns.GNS_F32, 1, 64, 256) > 0
     # split storage: two planes of every region, 128-edge tiles
@@ -84,7 +90,8 @@ def test_gram_argument_errors():
     assert _gram(cdt=9) == E["DTYPE"]
     assert _gram(io=gns.GNS_BF16X3) == E["DTYPE"]     # a compute type only
     assert _gram(n=0) == E["SHAPE"]
-    assert _gram(n=9, m=8) == E["SHAPE"]                  # n > m
+    assert _gram(m=0) == E["SHAPE"]
+    assert _gram(n=9, m=8, ws_bytes=100) == E["WORKSPACE"]   # tall: accepted, checked further
     assert _gram(row_idx=FAKE, k=0) == E["SHAPE"]
     assert _gram(row_idx=FAKE, k=5, n=4) == E["SHAPE"]    # k > n
     assert _gram(coeffs=[], T=0, restarts=()) == E["COEFF"]
@@ -115,7 +122,8 @@ def test_standard_argument_errors():
     ws = 0x7f0000000000
     need = L.gns_standard_workspace_bytes(1, 1, 4, 8)
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 0, None, 0, 0, ws, need, None) == E["COEFF"]
-    assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 8, 1, 1, carr, 5, None, 0, 0, ws, need, None) == E["SHAPE"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 0, 1, 1, carr, 5, None, 0, 0, ws, need, None) == E["SHAPE"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 8, 1, 1, carr, 5, None, 0, 0, ws, 16, None) == E["WORKSPACE"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0, ws, 16, None) == E["WORKSPACE"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 1, ws, need, None) == E["FLAGS"]
     assert L.gns_standard_batched(None, None, 0, 4, 8, 1, 1, carr, 5, None, 0, 0, None, 0, None) == E["OK"]

@@ -320,3 +320,69 @@ def test_split_planes_tighter_than_bf16():
     assert err["bf16x3"] <= 1e-3
     assert err["bf16x3"] < 0.25 * err["bf16"]
     assert err["f32"] <= TOL_F32
+
+
+@pytest.mark.parametrize("algo", ["gram", "standard"])
+@pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "bf16x3"), ("bf16", "f16")])
+def test_tall_parity(algo, io, cdt):
+    """n > m: the library orthogonalises X^T (its normalised copy is the
+    transposed layout it writes anyway) and writes the result back in the
+    caller's layout; several tiles and ragged tails on both sides."""
+    gns = need_gpu()
+    B, n, m = 3, 700, 300
+    X, X64 = _inputs(B, n, m, io, seed=26)
+    say(f"tall {algo} io={io} cdt={cdt} {B}x{n}x{m}")
+    out = _run(gns, algo, X.cuda(), cdt)
+    torch.cuda.synchronize()
+    ref = np.stack([(oracle_gram if algo == "gram" else oracle_standard)(X64[b]) for b in range(B)])
+    errs = per_matrix_rel(synth.as_f64(out), ref)
+    say("  rel errs", errs)
+    assert max(errs) <= _tol(cdt)
+    assert out.shape == X.shape
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_tall_matches_transposed_problem(tile):
+    """A tall batch and the wide batch of its transposes give the same
+    results, transposed, up to the order of the norm's partial sums."""
+    gns = need_gpu()
+    X, _ = _inputs(2, 600, 260, "f32", seed=27)
+    Xd = X.cuda()
+    say(f"tall vs transposed, tile {tile}")
+    a = gns.gram_ns_batched(Xd, NS5, tile=tile)
+    b = gns.gram_ns_batched(Xd.transpose(1, 2).contiguous(), NS5, tile=tile)
+    torch.cuda.synchronize()
+    assert max(per_matrix_rel(synth.as_f64(a), synth.as_f64(b.transpose(1, 2)))) <= 1e-5
+
+
+def test_tall_row_subset():
+    """Dion3 rows with more selected rows than columns (k > m)."""
+    gns = need_gpu()
+    B, n, m, k = 2, 400, 150, 230
+    X, X64 = _inputs(B, n, m, "bf16", seed=28)
+    rows = np.stack([synth.row_subset(n, k, seed=28, index=b) for b in range(B)])
+    init = torch.randn(B, n, m, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    out = init.clone().cuda()
+    say("tall row subset")
+    gns.gram_ns_batched(X.cuda(), NS5, row_idx=torch.from_numpy(rows).cuda(), out=out)
+    torch.cuda.synchronize()
+    got = synth.as_f64(out)
+    init64 = synth.as_f64(init)
+    for b in range(B):
+        sel = rows[b]
+        assert rel_err(got[b][sel], oracle_gram(X64[b][sel])) <= TOL_HALF
+        keep = np.setdiff1d(np.arange(n), sel)
+        assert np.array_equal(got[b][keep], init64[b][keep])
+
+
+def test_tall_mlp_down_projection():
+    """One 16384 x 4096 bf16 matrix (the shape of an MLP down-projection
+    weight), against the oracle."""
+    gns = need_gpu()
+    X = synth.batch(1, 16384, 4096, seed=29, dtype=torch.bfloat16)
+    say("tall 16384x4096")
+    g = gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,))
+    torch.cuda.synchronize()
+    e = rel_err(synth.as_f64(g)[0], oracle_gram(synth.as_f64(X)[0]))
+    say(f"  rel err {e:.4g}")
+    assert e <= TOL_HALF
