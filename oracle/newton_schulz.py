@@ -17,6 +17,8 @@ Every routine follows the written description in
 * ``composed_poly`` -- §2.2: the composed odd polynomial p_T o ... o p_1.
 * ``spectral_map``  -- §2.2: NS acts on the SVD as U (p_T o...o p_1)(S) V^T.
 * ``polar``         -- §2.1, Definition 1: polar(X) = U V^T.
+* ``dion3_select``  -- §6, Algorithm 4, selection: the k rows of largest l1
+                       norm.
 * ``dion3_rows``    -- §6, Algorithm 4: orthogonalise the selected rows M[S,:]
                        as one k x m matrix and write them back.
 * ``flops_*``       -- §2.2 and §4.1 FLOP models, §4.2 restart surcharge.
@@ -51,7 +53,7 @@ EPS = 1e-7
 
 __all__ = [
     "EPS", "frobenius_normalize", "standard_ns", "gram_ns", "theorem2_q",
-    "composed_poly", "spectral_map", "polar", "dion3_rows", "flops_standard",
+    "composed_poly", "spectral_map", "polar", "dion3_select", "dion3_rows", "flops_standard",
     "flops_gram", "gram_ns_trace",
 ]
 
@@ -256,6 +258,23 @@ def polar(X) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Dion3 fractional rows (Algorithm 4, orthogonalisation of M[S,:])
 # --------------------------------------------------------------------------
+def dion3_select(M, k: int) -> np.ndarray:
+    """Selection step of the Dion3 update (Dion3 §6, Algorithm 4): the
+    indices of the k rows of M with the largest l1 norm, in ascending order.
+
+    A row's norm is the exact sum of |M_ij| rounded once to float64
+    (math.fsum).  Rows with equal norms are taken in index order, the smaller
+    index first (the pages do not say how ties break).
+    """
+    M = np.asarray(M, dtype=np.float64)
+    n = M.shape[0]
+    if not 1 <= k <= n:
+        raise ValueError("need 1 <= k <= n")
+    keys = [math.fsum(np.abs(M[i])) for i in range(n)]
+    order = sorted(range(n), key=lambda i: (-keys[i], i))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
 def dion3_rows(X, out_init, rows: Sequence[int], coeffs, restarts=(2,),
                algebra="stabilized", eps=EPS) -> np.ndarray:
     """Orthogonalise rows ``rows`` of X as one k x m matrix (normalised by its

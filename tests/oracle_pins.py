@@ -282,6 +282,32 @@ def pin_dion3(O):
     assert _rel(part[rows], _closed_form(sub, ns5)) <= 1e-10   # own normalisation
 
 
+# ---------------------------------------------------------------------------
+# Dion3 selection: brute force over every k-subset on tiny integer matrices
+# ---------------------------------------------------------------------------
+def pin_dion3_select(O):
+    import itertools
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        n, m = int(rng.integers(1, 8)), int(rng.integers(1, 5))
+        # small integers (many exact ties), signs mixed
+        M = rng.integers(-3, 4, size=(n, m)).astype(np.float64)
+        for k in range(1, n + 1):
+            got = O.dion3_select(M, k)
+            norms = [sum(abs(int(v)) for v in M[i]) for i in range(n)]
+            # the subset with the largest total norm; among equals, the
+            # lexicographically smallest index tuple
+            best = max(itertools.combinations(range(n), k),
+                       key=lambda S: (sum(norms[i] for i in S), [-i for i in S]))
+            assert list(got) == list(best), (M, k, got, best)
+    # k = n takes every row; a row permutation permutes the selection
+    M = _randn((30, 12), 3)
+    assert list(O.dion3_select(M, 30)) == list(range(30))
+    perm = np.random.default_rng(2).permutation(30)
+    sel = set(O.dion3_select(M, 9))
+    assert set(O.dion3_select(M[perm], 9)) == {int(np.where(perm == i)[0][0]) for i in sel}
+
+
 FAST_PINS = [pin_exact_equivalence, pin_restart_semantics, pin_rank_one_exact, pin_theorem2, pin_spectral,
-             pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3]
+             pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3, pin_dion3_select]
 ALL_PINS = FAST_PINS + [pin_exact_equivalence_t4]

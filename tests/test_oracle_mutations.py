@@ -37,6 +37,9 @@ MUTATIONS = {
     "identity wrong": ("return np.eye(n, dtype=np.float64)", "return 2.0 * np.eye(n, dtype=np.float64)"),
     "tall standard not transposed back": ("return standard_ns(X.T, coeffs, eps).T", "return standard_ns(X.T, coeffs, eps)"),
     "tall gram not transposed back": ("return out.T, trace", "return out, trace"),
+    "select ties to larger index": ("key=lambda i: (-keys[i], i))", "key=lambda i: (-keys[i], -i))"),
+    "select smallest rows": ("key=lambda i: (-keys[i], i))", "key=lambda i: (keys[i], i))"),
+    "select l2 instead of l1": ("keys = [math.fsum(np.abs(M[i])) for i in range(n)]", "keys = [math.fsum(M[i] * M[i]) for i in range(n)]"),
 }
 
 
