@@ -324,6 +324,27 @@ def main():
                "alg_tflops_sym_count": round(std_flops / (ms_std / 1e3) / 1e12, 2),
                "gram_speedup": round(ms_std / ms_clean, 3)}
 
+    # Dion3 selection step (the k = n/4 rows of largest l1 norm) on the same
+    # batch: HBM-bound, one read of the input
+    sel = None
+    if not args.one_stream:
+        kk = gns.select_count(w.n, 0.25)
+        sel_ws = torch.empty(gns.lib().gns_select_workspace_bytes(w.batch, w.n), dtype=torch.uint8,
+                             device="cuda")
+        for _ in range(2):
+            gns.select_rows_l1(Xd, kk, workspace=sel_ws, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            gns.select_rows_l1(Xd, kk, workspace=sel_ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sel_ms = e0.elapsed_time(e1) / 10
+        sel_bytes = Xd.numel() * Xd.element_size()
+        sel = {"k": kk, "ms": round(sel_ms, 4), "gbs": round(sel_bytes / (sel_ms / 1e3) / 1e9, 1),
+               "frac_hbm": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 3)}
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -372,6 +393,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "standard_ns5": std,
+        "dion3_select_l1": sel,
     }
     print(json.dumps(line), flush=True)
 

@@ -36,6 +36,7 @@ EXPORTS = [
     "gns_abi_version", "gns_status_str", "gns_gram_workspace_bytes",
     "gns_standard_workspace_bytes", "gns_gram_batched", "gns_standard_batched",
     "gns_check_row_idx", "gns_timing_enable", "gns_timing_read", "gns_timing_reset",
+    "gns_select_workspace_bytes", "gns_select_rows_l1",
 ]
 
 
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
     L.gns_standard_batched.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                        vp, i64, ctypes.c_uint, vp, sz, vp]
+    L.gns_select_workspace_bytes.restype = sz
+    L.gns_select_workspace_bytes.argtypes = [i64, i64]
+    L.gns_select_rows_l1.restype = ctypes.c_int
+    L.gns_select_rows_l1.argtypes = [vp, i64, i64, i64, ctypes.c_int, i64, vp, vp, sz, vp]
     L.gns_check_row_idx.restype = ctypes.c_int
     L.gns_check_row_idx.argtypes = [vp, i64, i64, i64, vp, vp]
     L.gns_timing_enable.argtypes = [ctypes.c_int]
@@ -249,3 +254,38 @@ def timing_read():
     recs = (LaunchRecord * max(n, 1))()
     n = L.gns_timing_read(recs, n)
     return [(r.name.decode(), r.kernel.decode(), r.flops, r.bytes, r.ms) for r in recs[:n]]
+
+
+def select_rows_l1(M: torch.Tensor, k: int, *, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Indices of the k rows of largest l1 norm of every matrix in M
+    ([batch, n, m] or [n, m]), ascending, via gns_select_rows_l1 (the Dion3
+    selection step).  Returns an int64 [batch, k] (or [k]) device tensor."""
+    squeeze = M.dim() == 2
+    Mb = M.unsqueeze(0) if squeeze else M
+    if Mb.dim() != 3 or not Mb.is_contiguous():
+        raise GnsError(2, "M must be a contiguous [batch, n, m] tensor")
+    B, n, m = Mb.shape
+    out = torch.empty(B, k, dtype=torch.int64, device=Mb.device)
+    ws = _workspace(int(lib().gns_select_workspace_bytes(B, n)), Mb.device, workspace)
+    _check(lib().gns_select_rows_l1(_ptr(Mb), B, n, m, _dtype_code(Mb.dtype), k, _ptr(out),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return out.squeeze(0) if squeeze else out
+
+
+def select_count(n: int, fraction: float) -> int:
+    """k = ceil(f n) rows for a fraction f in (0, 1] (Dion3 Algorithm 4)."""
+    if not 0.0 < fraction <= 1.0:
+        raise ValueError("fraction must be in (0, 1]")
+    import math
+    return max(1, min(n, math.ceil(fraction * n)))
+
+
+def safety_scaled(coeffs: Sequence, s: float = 1.05) -> list:
+    """Coefficients of p_t(x / s) for every step: (a/s, b/s^3, c/s^5).  The
+    pages adjust the Polar Express polynomials this way so that singular
+    values up to s still converge (1.02 usual, 1.05 as the conservative
+    choice; Dion3 Appendix B.2.2)."""
+    if not s > 0:
+        raise ValueError("safety factor must be positive")
+    return [(float(a) / s, float(b) / s ** 3, float(c) / s ** 5) for a, b, c in coeffs]

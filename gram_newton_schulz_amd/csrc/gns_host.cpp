@@ -662,6 +662,37 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
                      });
 }
 
+size_t gns_select_workspace_bytes(int64_t batch, int64_t n) {
+  if (batch <= 0 || n < 1) return 0;
+  return align_up(sizeof(double) * static_cast<size_t>(batch) * static_cast<size_t>(n), kAlign);
+}
+
+gns_status gns_select_rows_l1(const void *M, int64_t batch, int64_t n, int64_t m, gns_dtype dtype,
+                              int64_t k, int64_t *row_idx, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (!valid_dtype(dtype)) return GNS_E_DTYPE;
+  if (batch < 0 || n < 1 || m < 1 || k < 1 || k > n || batch > 65535 ||
+      n > (int64_t(1) << 31) - 1024)
+    return GNS_E_SHAPE;
+  if (batch == 0) return GNS_OK;
+  if (!M || !row_idx) return GNS_E_NULL;
+  if (!workspace || workspace_bytes < gns_select_workspace_bytes(batch, n) ||
+      (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return GNS_E_WORKSPACE;
+  const size_t in_bytes = static_cast<size_t>(batch) * n * m * gns::dtype_size(dtype);
+  const size_t ws_used = gns_select_workspace_bytes(batch, n);
+  if (ranges_overlap(workspace, ws_used, M, in_bytes) ||
+      ranges_overlap(workspace, ws_used, row_idx, sizeof(int64_t) * batch * k))
+    return GNS_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const double bytes = static_cast<double>(in_bytes);
+  LaunchScope ls(s, "select_rows_l1", "row_l1+select_topk", 2.0 * batch * n * m, bytes);
+  hipError_t e = gns::launch_select_rows_l1(dtype, M, batch, n, m, k, static_cast<double *>(workspace),
+                                            row_idx, s);
+  ls.done();
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
 gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, void *stream) {
   if (!row_idx || !result) return GNS_E_NULL;

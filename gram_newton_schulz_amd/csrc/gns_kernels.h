@@ -75,6 +75,11 @@ hipError_t launch_scale_transpose(int io_dtype, int compute_dtype, const void *X
                                   int parts, double eps, void *Xh, void *XT, int64_t Np,
                                   int64_t Mp, int64_t plane_h, int64_t plane_t, hipStream_t s);
 
+// Dion3 selection: keys[b][i] = sum_j |M_b[i][j]| (fp64), then out[b][0..k) =
+// indices of the k largest keys in ascending order (ties: smaller index).
+hipError_t launch_select_rows_l1(int io_dtype, const void *M, int64_t batch, int64_t n, int64_t m,
+                                 int64_t k, double *keys, int64_t *out, hipStream_t s);
+
 hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, hipStream_t s);
 

@@ -895,6 +895,125 @@ check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
 }
 
 // ---------------------------------------------------------------------------
+// Row selection of the Dion3 update ("Dion3: Full-Stack Orthogonal Updates",
+// §6, Algorithm 4, selection step): the k rows of largest l1 norm
+// ---------------------------------------------------------------------------
+// Key of every row: sum_j |M_ij| in fp64, one wave per row, each lane over a
+// fixed set of 16-byte pieces, then a fixed-order wave tree.  For 16-bit
+// inputs whose values in a row span less than 2^31 in magnitude the sum is
+// exact, so the keys do not depend on the summation order.
+template <class TIn>
+__global__ void __launch_bounds__(256)
+row_l1(const void *M, int64_t n, int64_t m, double *keys) {
+  using S = typename TIn::S;
+  constexpr int VE = 16 / sizeof(S);
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const S *r = static_cast<const S *>(M) + (static_cast<int64_t>(b) * n + row) * m;
+  double acc = 0.0;
+  if ((m % VE) == 0 && (reinterpret_cast<uintptr_t>(M) & 15) == 0) {
+    const uint4 *rv = reinterpret_cast<const uint4 *>(r);
+    for (int64_t v = lane; v < m / VE; v += 64) {
+      const uint4 u = rv[v];
+      const S *e = reinterpret_cast<const S *>(&u);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) acc += fabs(static_cast<double>(TIn::ld(e[q])));
+    }
+  } else {
+    for (int64_t c = lane; c < m; c += 64) acc += fabs(static_cast<double>(TIn::ld(r[c])));
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
+  if (lane == 0) keys[static_cast<int64_t>(b) * n + row] = acc;
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup (16 waves);
+// *total receives the sum over all threads.
+__device__ __forceinline__ int block_scan_excl(int v, int *total, int *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int t = wsum[w];
+      wsum[w] = run;
+      run += t;
+    }
+    wsum[16] = run;
+  }
+  __syncthreads();
+  const int r = wsum[wave] + x - v;
+  *total = wsum[16];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per matrix.  The keys are non-negative doubles, so their bit
+// patterns order like the values: an MSB-first radix select (8 bits per
+// pass) finds the k-th largest key tau and how many keys equal to tau still
+// belong to the top k; a pass over the rows in index order then takes every
+// key above tau and the first of the keys equal to tau, writing the indices
+// in ascending order (equal keys: the smaller index wins).
+__global__ void __launch_bounds__(1024)
+select_topk(const double *keys, int64_t n, int64_t k, int64_t *out) {
+  const int b = blockIdx.x;
+  const uint64_t *K = reinterpret_cast<const uint64_t *>(keys) + static_cast<int64_t>(b) * n;
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int64_t s_need;
+  __shared__ int wsum[17];
+  uint64_t prefix = 0, mask = 0;
+  int64_t need = k;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += 1024) {
+      const uint64_t u = K[i];
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t above = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (above + hist[d] >= need) break;
+        above += hist[d];
+      }
+      s_prefix = prefix | (static_cast<uint64_t>(d) << shift);
+      s_need = need - above;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    mask |= static_cast<uint64_t>(255) << shift;
+  }
+  const uint64_t tau = prefix;
+  int64_t base = 0, eq_before = 0;
+  int64_t *o = out + static_cast<int64_t>(b) * k;
+  for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+    const int64_t i = c0 + threadIdx.x;
+    const uint64_t u = i < n ? K[i] : 0;
+    const int gt = (i < n && u > tau) ? 1 : 0;
+    const int eq = (i < n && u == tau) ? 1 : 0;
+    int eq_total = 0, take_total = 0;
+    const int eq_rank = block_scan_excl(eq, &eq_total, wsum);
+    const int take = (gt || (eq && eq_before + eq_rank < need)) ? 1 : 0;
+    const int pos = block_scan_excl(take, &take_total, wsum);
+    if (take && base + pos < k) o[base + pos] = i;
+    base += take_total;
+    eq_before += eq_total;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <class E, int TILE, int PL = 1>
@@ -980,6 +1099,18 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
   if (io == DT_BF16) st_dispatch<EBF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   else if (io == DT_F16) st_dispatch<EF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   else st_dispatch<EF32>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_rows_l1(int io, const void *M, int64_t batch, int64_t n, int64_t m,
+                                 int64_t k, double *keys, int64_t *out, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(batch));
+  if (io == DT_BF16) row_l1<EBF16><<<grid, 256, 0, s>>>(M, n, m, keys);
+  else if (io == DT_F16) row_l1<EF16><<<grid, 256, 0, s>>>(M, n, m, keys);
+  else row_l1<EF32><<<grid, 256, 0, s>>>(M, n, m, keys);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_topk<<<static_cast<unsigned>(batch), 1024, 0, s>>>(keys, n, k, out);
   return hipGetLastError();
 }
 

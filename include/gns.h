@@ -191,6 +191,26 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Row selection of the Dion3 update ("Dion3: Full-Stack Orthogonal Updates",
+ * §6, Algorithm 4, selection step): for every matrix M_b, the indices of the
+ * k rows with the largest l1 norm sum_j |M_b[i][j]|, written to
+ * row_idx[b][0..k) in ascending order, ready for gns_gram_batched's row
+ * subset.  The pages take k = ceil(f n) for a fraction f in (0, 1].
+ *   M          (device) [batch][n][m] in dtype (GNS_F32, GNS_BF16, GNS_F16).
+ *   row_idx    (device) [batch][k] int64, written.
+ *   workspace  (device) >= gns_select_workspace_bytes(batch, n) bytes,
+ *              256-byte aligned (the fp64 row norms); clobbered.
+ * The row norms are fp64 sums in a fixed order; for 16-bit inputs whose
+ * values in a row span less than 2^31 in magnitude they are exact.  Rows
+ * with equal norms are taken in index order (the smaller index first), so
+ * the selection is deterministic.  Needs 1 <= k <= n, batch <= 65535.
+ */
+size_t gns_select_workspace_bytes(int64_t batch, int64_t n);
+gns_status gns_select_rows_l1(const void *M, int64_t batch, int64_t n, int64_t m, gns_dtype dtype,
+                              int64_t k, int64_t *row_idx, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * Enqueue a check of a row subset: writes to *result (device int32) 0 when
  * every row_idx[b][i] is in [0, n) and the k indices of each matrix are
  * distinct, 1 when an index is out of range, 2 when an index repeats.

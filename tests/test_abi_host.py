@@ -23,7 +23,7 @@ E = {"OK": 0, "NULL": 1, "SHAPE": 2, "DTYPE": 3, "COEFF": 4, "RESTART": 5, "ROWI
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(gns_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(gns_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_symbol():
@@ -141,3 +141,35 @@ def test_binding_errors_are_raised():
     X = torch.zeros(2, 3, 8)
     with pytest.raises(gns.GnsError):
         gns.gram_ns_batched(X, [(1, 0, 0)], restarts=(), compute_dtype=torch.int32)
+
+
+def test_select_argument_errors():
+    L = gns.lib()
+    ws = 0x7f0000000000
+    need = L.gns_select_workspace_bytes(2, 64)
+    assert need >= 8 * 2 * 64 and L.gns_select_workspace_bytes(0, 64) == 0
+    sel = lambda **kw: L.gns_select_rows_l1(kw.get("M", FAKE), kw.get("batch", 2), kw.get("n", 64),
+                                            kw.get("m", 32), kw.get("dt", 1), kw.get("k", 16),
+                                            kw.get("out", FAKE + (1 << 24)), kw.get("ws", ws),
+                                            kw.get("ws_bytes", need), None)
+    assert sel(dt=gns.GNS_BF16X3) == E["DTYPE"]
+    assert sel(k=0) == E["SHAPE"] and sel(k=65) == E["SHAPE"] and sel(m=0) == E["SHAPE"]
+    assert sel(batch=70000) == E["SHAPE"]
+    assert sel(M=None) == E["NULL"] and sel(out=None) == E["NULL"]
+    assert sel(ws_bytes=8) == E["WORKSPACE"] and sel(ws=ws + 8) == E["WORKSPACE"]
+    assert sel(M=ws + 512) == E["ALIAS"]                  # input overlaps the workspace
+    assert sel(batch=0, M=None, out=None, ws=None, ws_bytes=0) == E["OK"]
+
+
+def test_safety_factor_helper():
+    """p_t(x / s) has coefficients (a/s, b/s^3, c/s^5): one step of the scaled
+    schedule at s*x equals one step of the original at x."""
+    import numpy as np
+    import oracle
+    co = [(3.4445, -4.7750, 2.0315), (1.875, -1.25, 0.375)]
+    sc = gns.safety_scaled(co, 1.05)
+    xs = np.linspace(0.0, 1.0, 11)
+    for t in range(2):
+        assert np.allclose(oracle.composed_poly([sc[t]], 1.05 * xs), oracle.composed_poly([co[t]], xs),
+                           rtol=1e-13, atol=1e-15)
+    assert gns.select_count(4096, 0.25) == 1024 and gns.select_count(10, 0.01) == 1
