@@ -386,3 +386,43 @@ def test_tall_mlp_down_projection():
     e = rel_err(synth.as_f64(g)[0], oracle_gram(synth.as_f64(X)[0]))
     say(f"  rel err {e:.4g}")
     assert e <= TOL_HALF
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_graph_capture_replays(split):
+    """The whole call captured into a HIP graph (the pages replay the full
+    optimizer step as a graph) and replayed several times, with eager work
+    and synchronisations between replays: every replay equals the eager
+    result bit for bit.  The library enqueues no memset and no allocation,
+    and its two-stream fan-out is captured through its fork/join events."""
+    gns = need_gpu()
+    B, n, m = 4, 300, 700
+    X, _ = _inputs(B, n, m, "bf16", seed=33)
+    X2, _ = _inputs(B, n, m, "bf16", seed=34)
+    Xd = X.cuda()
+    static_in = Xd.clone()
+    static_out = torch.empty_like(Xd)
+    ws = torch.empty(gns.gram_workspace_bytes(torch.bfloat16, B, n, m), dtype=torch.uint8, device="cuda")
+    eager = gns.gram_ns_batched(Xd, NS5, split_batch=split)
+    eager2 = gns.gram_ns_batched(X2.cuda(), NS5, split_batch=split)
+    torch.cuda.synchronize()
+    say(f"graph capture split={split}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):      # warm up on the capture stream
+        gns.gram_ns_batched(static_in, NS5, out=static_out, workspace=ws, split_batch=split)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gns.gram_ns_batched(static_in, NS5, out=static_out, workspace=ws, split_batch=split,
+                            stream=torch.cuda.current_stream())
+    for rep in range(4):
+        static_in.copy_(Xd if rep % 2 == 0 else X2.cuda())
+        static_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = eager if rep % 2 == 0 else eager2
+        assert torch.equal(static_out, want), f"replay {rep}"
+        _ = (static_out.float() * 2).sum().item()   # eager work between replays
