@@ -321,6 +321,8 @@ gemm_nt(GemmParams p) {
   // Accumulators start at (beta/alpha) * D so that the epilogue is a plain
   // scale-and-store.  D is read through its transposed copy DT (D itself
   // for symmetric D), where the four rows held by a lane are contiguous.
+  // The raw loads are issued first and converted only after the main loop's
+  // first DMA stages are in flight, so that the two latencies overlap.
   f32x16_t acc[NBI][NBJ];
 #pragma unroll
   for (int i = 0; i < NBI; ++i)
@@ -328,7 +330,10 @@ gemm_nt(GemmParams p) {
     for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  if (p.DT) {
+  using RawD = typename std::conditional<ESZ == 2, uint2, float4>::type;
+  RawD draw[PL][NBI][NBJ][4];
+  const bool has_d = p.DT != nullptr;
+  auto load_d = [&]() {
     const S *DTm = static_cast<const S *>(p.DT) + static_cast<int64_t>(mat) * p.sDT;
     const int64_t i_base = static_cast<int64_t>(ti) * TILE + wr + 4 * lh;
     const int64_t j_base = static_cast<int64_t>(tj) * TILE + wc + lr;
@@ -339,24 +344,35 @@ gemm_nt(GemmParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const S *src = DTm + (j_base + j * 32) * p.lddt + i_base + i * 32 + 8 * g;
+#pragma unroll
+          for (int pl = 0; pl < PL; ++pl) draw[pl][i][j][g] = *reinterpret_cast<const RawD *>(src + pl * p.pDT);
+        }
+  };
+  auto init_from_d = [&]() {
+#pragma unroll
+    for (int i = 0; i < NBI; ++i)
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
           float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int pl = 0; pl < PL; ++pl) {
+            const RawD u = draw[pl][i][j][g];
             if constexpr (ESZ == 2) {
-              const uint2 u = *reinterpret_cast<const uint2 *>(src + pl * p.pDT);
               v[0] += E::ld(static_cast<S>(u.x & 0xffffu));
               v[1] += E::ld(static_cast<S>(u.x >> 16));
               v[2] += E::ld(static_cast<S>(u.y & 0xffffu));
               v[3] += E::ld(static_cast<S>(u.y >> 16));
             } else {
-              const float4 u = *reinterpret_cast<const float4 *>(src);
               v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
             }
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = p.init_scale * v[q];
         }
-  }
+  };
+  if (has_d) load_d();
 
   // Main loop over K stages of 64 bytes per row in an NST-deep LDS ring.
   // The loads bypass the compiler's wait bookkeeping (inline assembly), so
@@ -430,6 +446,7 @@ gemm_nt(GemmParams p) {
       static_assert(kWait < 64, "wait count out of range");
 #pragma unroll
       for (int j = 0; j < NST - 1; ++j) dma_stage(j);
+      if (has_d) init_from_d();
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
       __syncthreads();
       if (g1) __syncthreads();
@@ -457,6 +474,7 @@ gemm_nt(GemmParams p) {
       // prologue: all NST stages in flight; wait for stages 0 and 1
 #pragma unroll
       for (int j = 0; j < NST; ++j) dma_stage(j);
+      if (has_d) init_from_d();
       static_assert(LPS * (NST - 2) < 64, "wait count out of range");
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 2)) : "memory");
       __syncthreads();
@@ -495,6 +513,8 @@ gemm_nt(GemmParams p) {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (has_d) {
+    init_from_d();
   }
 
   // ---------------------------------------------------------------- epilogue
