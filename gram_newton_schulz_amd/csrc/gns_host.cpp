@@ -44,7 +44,8 @@ struct Plan {
   int parts = 1;
   int esz = 2;
   int planes = 1;                      // 2: split hi/lo storage (GNS_BF16X3)
-  size_t off_partials = 0, off_xh = 0, off_xt0 = 0, off_xt1 = 0;
+  size_t off_partials = 0, off_inv = 0, off_xh = 0, off_xt0 = 0, off_xt1 = 0;
+  int64_t tile_parts = 0;              // 64x64 tiles per matrix (direct input path)
   size_t off_sq[5] = {0, 0, 0, 0, 0};  // R, Z, RZ, Q0, Q1 (standard NS: A, B)
   size_t bytes = 0;
 };
@@ -91,7 +92,12 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
   pl->planes = gns::dtype_planes(cdt);
   size_t off = 0;
   pl->off_partials = off;
-  off = align_up(off + sizeof(double) * batch * pl->parts, kAlign);
+  // norm partials: per row block (normalised-copy path) or per 64x64 tile
+  // (direct path), whichever needs more
+  pl->tile_parts = (pl->Np / 64) * (pl->Mp / 64);
+  off = align_up(off + sizeof(double) * batch * std::max<int64_t>(pl->parts, pl->tile_parts), kAlign);
+  pl->off_inv = off;                   // 1/(||X||+eps) and its square, per matrix
+  off = align_up(off + 2 * sizeof(float) * batch, kAlign);
   // every region holds `planes` planes of `batch` matrices, lo after hi
   const size_t rect = static_cast<size_t>(pl->planes) * batch * pl->Np * pl->Mp * pl->esz;
   const size_t sq = static_cast<size_t>(pl->planes) * batch * pl->Np * pl->Np * pl->esz;
@@ -166,6 +172,11 @@ struct Ctx {
   int64_t b0;
   unsigned char *ws;
   hipStream_t s;
+  // Direct input path: X (already in the compute type, whole tiles, no row
+  // subset) is read in place instead of through a normalised copy; products
+  // that read it apply 1/(||X||_F + eps) per matrix in their epilogues.
+  bool direct = false;
+  const void *xin = nullptr;           // this sub-batch's X
   int64_t sq_stride() const { return pl->Np * pl->Np; }
   int64_t rect_stride() const { return pl->Np * pl->Mp; }
   void *sq(int i) const { return ws + pl->off_sq[i] + b0 * sq_stride() * pl->esz; }
@@ -174,6 +185,11 @@ struct Ctx {
   double *partials() const {
     return reinterpret_cast<double *>(ws + pl->off_partials) + b0 * pl->parts;
   }
+  double *tile_partials() const {
+    return reinterpret_cast<double *>(ws + pl->off_partials) + b0 * pl->tile_parts;
+  }
+  float *inv() const { return reinterpret_cast<float *>(ws + pl->off_inv) + b0; }
+  float *inv2() const { return reinterpret_cast<float *>(ws + pl->off_inv) + pl->batch + b0; }
   // element offset from a hi plane to its lo plane (split storage only)
   int64_t plane_sq() const { return pl->planes == 2 ? pl->batch * sq_stride() : 0; }
   int64_t plane_rect() const { return pl->planes == 2 ? pl->batch * rect_stride() : 0; }
@@ -242,12 +258,15 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
 
-// R = X X^T from the row-layout buffer.
-gns_status syrk(const Ctx &c, void *R) {
+// R = X X^T from the row-layout buffer, or (from_input on the direct path)
+// from the caller's X with 1/(||X||+eps)^2 applied in the epilogue.
+gns_status syrk(const Ctx &c, void *R, bool from_input = false) {
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int nt = static_cast<int>(N / c.pl->tile);
-  const void *Xh = c.xh();
+  const bool direct = from_input && c.direct;
+  const void *Xh = direct ? c.xin : c.xh();
+  if (direct) p.alpha_vec = c.inv2();
   p.A = Xh; p.lda = M; p.sA = c.rect_stride();
   p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
   p.K = static_cast<int>(M);
@@ -270,8 +289,9 @@ gns_status syrk(const Ctx &c, void *R) {
 // transposed copy XT_out, or (final) the caller's output.
 gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, float beta,
                  bool final, void *out, int io_dtype, int64_t n_total, const int64_t *row_idx,
-                 const char *what) {
+                 const char *what, const float *alpha_vec = nullptr) {
   GemmParams p = base_params(c);
+  p.alpha_vec = alpha_vec;           // 1/(||X||+eps) when X^T is the unscaled input
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int tm = static_cast<int>(N / c.pl->tile), tn = static_cast<int>(M / c.pl->tile);
   void *Xh = c.xh();
@@ -317,10 +337,27 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
 
-// Norm + scale + cast + transpose of the (row-selected) input.
+// Norm + scale + cast + transpose of the (row-selected) input.  On the
+// direct path: the unscaled transpose X^T and the per-matrix scale factors.
 gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const int64_t *row_idx) {
   double *partials = c.partials();
   const double rows = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
+  if (c.direct) {
+    {
+      LaunchScope ls(c.s, "transpose_sumsq", "transpose_sumsq", 2.0 * rows * m * c.batch,
+                     c.batch * rows * m * 2.0 * gns::dtype_size(io));
+      hipError_t e = gns::launch_transpose_sumsq(io, X, c.batch, c.pl->rows, c.pl->m, c.xt(0),
+                                                 c.tile_partials(), c.s);
+      ls.done();
+      if (e != hipSuccess) return GNS_E_HIP;
+    }
+    LaunchScope ls(c.s, "norm_finish", "norm_finish", 1.0 * c.batch * c.pl->tile_parts,
+                   8.0 * c.batch * c.pl->tile_parts);
+    hipError_t e = gns::launch_norm_finish(c.tile_partials(), c.batch, c.pl->tile_parts, kEps, c.inv(),
+                                           c.inv2(), c.s);
+    ls.done();
+    return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+  }
   {
     LaunchScope ls(c.s, "norm_partial", "norm_partial", 2.0 * rows * m * c.batch,
                    c.batch * rows * m * gns::dtype_size(io));
@@ -401,19 +438,23 @@ gns_status enqueue_standard(const Ctx &c, const void *X, void *out, int io, int6
   const double nn = static_cast<double>(pl.r);
   gns_status st;
   if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
+  // on the direct path the first iteration reads X itself (syrk) and its
+  // unscaled transpose (apply), both with the normalisation as a factor
+  const float *x_scale = c.direct ? c.inv() : nullptr;
   for (int t = 1; t <= T; ++t) {
     const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);
     const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
     const float cc = static_cast<float>(coeffs[3 * (t - 1) + 2]);
-    if ((st = syrk(c, A)) != GNS_OK) return st;                                   // A = X X^T
+    if ((st = syrk(c, A, t == 1)) != GNS_OK) return st;                           // A = X X^T
     st = symm(c, A, A, cc, b, A, B, nullptr, 0.0f, 0.0f, "std_poly", nn * nn * nn);  // B = bA + cA^2
     if (st != GNS_OK) return st;
     if (t < T) {
-      st = apply(c, B, XT[xcur], XT[xcur ^ 1], a, false, nullptr, io, n, nullptr, "std_apply");
+      st = apply(c, B, XT[xcur], XT[xcur ^ 1], a, false, nullptr, io, n, nullptr, "std_apply", x_scale);
       xcur ^= 1;
     } else {
-      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, n, row_idx, "std_final_apply");
+      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, n, row_idx, "std_final_apply", x_scale);
     }
+    x_scale = nullptr;
     if (st != GNS_OK) return st;
   }
   return GNS_OK;
@@ -434,7 +475,9 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
   const double n3 = nn * nn * nn;
 
   if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
-  if ((st = syrk(c, R)) != GNS_OK) return st;                        // R_0 = X X^T
+  if ((st = syrk(c, R, true)) != GNS_OK) return st;                  // R_0 = X X^T
+  // the unscaled input transpose carries the normalisation as a factor
+  const float *x_scale = c.direct ? c.inv() : nullptr;
   for (int t = 1; t <= T; ++t) {
     const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);
     const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
@@ -442,7 +485,9 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     if (t > 1 && restart_at[t - 1]) {
       // restart: X <- Q X (row layout in place, transposed copy swapped),
       // R <- X X^T, Q <- I
-      st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], 0.0f, false, nullptr, io, n, nullptr, "restart_apply");
+      st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], 0.0f, false, nullptr, io, n, nullptr, "restart_apply",
+                 x_scale);
+      x_scale = nullptr;
       if (st != GNS_OK) return st;
       xcur ^= 1;
       if ((st = syrk(c, R)) != GNS_OK) return st;
@@ -487,7 +532,16 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     }
   }
   // out = Q_T X
-  return apply(c, Qb[qcur], XT[xcur], nullptr, 0.0f, true, out, io, n, row_idx, "final_apply");
+  return apply(c, Qb[qcur], XT[xcur], nullptr, 0.0f, true, out, io, n, row_idx, "final_apply", x_scale);
+}
+
+// The direct input path applies when X can stand in for its normalised copy:
+// X is already in the (16-bit, unsplit) compute type, every matrix is used
+// whole and fills whole tiles, and X is 16-byte aligned.
+bool direct_input(const Plan &pl, const void *X, int io, int cdt, const int64_t *row_idx) {
+  return io == cdt && (cdt == GNS_BF16 || cdt == GNS_F16) && pl.planes == 1 && !row_idx &&
+         !pl.tall && pl.rows % pl.tile == 0 && pl.m % pl.tile == 0 &&
+         (reinterpret_cast<uintptr_t>(X) & 15) == 0;
 }
 
 // --------------------------------------------------------------------------
@@ -624,16 +678,23 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   // matrix, so the pages fall back to it (Dion3 §4.1, last paragraph).
   const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  const bool direct = direct_input(pl, X, io, cdt, row_idx);
   if (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK))
-    return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c) {
-      return enqueue_standard(c, static_cast<const unsigned char *>(X) + c.b0 * io_mat,
-                              static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
+    return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c0) {
+      const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
+      Ctx c = c0;
+      c.direct = direct;
+      c.xin = Xs;
+      return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
                               row_idx ? row_idx + c.b0 * k : nullptr);
     });
   const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
-  return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c) {
-    return enqueue_gram(c, static_cast<const unsigned char *>(X) + c.b0 * io_mat,
-                        static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
+  return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c0) {
+    const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
+    Ctx c = c0;
+    c.direct = direct;
+    c.xin = Xs;
+    return enqueue_gram(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
                         restart_at, row_idx ? row_idx + c.b0 * k : nullptr, naive);
   });
 }
@@ -654,10 +715,14 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
   st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
   if (st != GNS_OK) return st;
   const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
+  const bool direct = direct_input(pl, X, io, cdt, row_idx);
   return run_batches(pl, cdt, batch, workspace, static_cast<hipStream_t>(stream), split,
-                     [&](const Ctx &c) {
-                       return enqueue_standard(c, static_cast<const unsigned char *>(X) + c.b0 * io_mat,
-                                               static_cast<unsigned char *>(out) + c.b0 * io_mat, io,
+                     [&](const Ctx &c0) {
+                       const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
+                       Ctx c = c0;
+                       c.direct = direct;
+                       c.xin = Xs;
+                       return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io,
                                                n, coeffs, T, row_idx ? row_idx + c.b0 * k : nullptr);
                      });
 }

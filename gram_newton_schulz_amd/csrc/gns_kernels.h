@@ -41,6 +41,7 @@ struct GemmParams {
   int xcd_chunk;                    // tiles per run dealt to one XCD (see gemm_nt);
                                     // must divide (grid & ~7) / 8
   float alpha;                      // C = alpha * (acc)
+  const float *alpha_vec;           // optional per-matrix factor on alpha (device, [batch])
   float init_scale;                 // acc starts at init_scale * D
   const void *DT; int64_t lddt, sDT;  // D read transposed: D(i,j) = DT[j*lddt + i];
                                       // may be null (D = 0)
@@ -79,6 +80,15 @@ hipError_t launch_scale_transpose(int io_dtype, int compute_dtype, const void *X
 // indices of the k largest keys in ascending order (ties: smaller index).
 hipError_t launch_select_rows_l1(int io_dtype, const void *M, int64_t batch, int64_t n, int64_t m,
                                  int64_t k, double *keys, int64_t *out, hipStream_t s);
+
+// Unscaled transpose of 16-bit X (n, m multiples of 64, 16-byte aligned) into
+// XT [m][n] per matrix, and the sum of squares of every 64x64 tile into
+// partials[b][tile] (fp64).
+hipError_t launch_transpose_sumsq(int dtype, const void *X, int64_t batch, int64_t n, int64_t m,
+                                  void *XT, double *partials, hipStream_t s);
+// inv[b] = 1 / (sqrt(sum_i partials[b][i]) + eps) and inv2[b] = inv[b]^2 (fixed-order sums).
+hipError_t launch_norm_finish(const double *partials, int64_t batch, int64_t parts, double eps,
+                              float *inv, float *inv2, hipStream_t s);
 
 hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, hipStream_t s);

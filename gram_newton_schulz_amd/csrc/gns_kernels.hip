@@ -522,6 +522,7 @@ gemm_nt(GemmParams p) {
   // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its block.
   const int64_t row_base = static_cast<int64_t>(ti) * TILE + wr;
   const int64_t col_base = static_cast<int64_t>(tj) * TILE + wc;
+  const float alpha = p.alpha_vec ? p.alpha * p.alpha_vec[mat] : p.alpha;
 
   // Transposed outputs (the mirrored half of a symmetric result, the
   // transposed copy of a general one) take four consecutive rows per lane,
@@ -547,7 +548,7 @@ gemm_nt(GemmParams p) {
           const int r0 = wr + ib * 32 + 8 * g + 4 * lh;
           uint32_t h[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = E::st(p.alpha * acc[ib][jb][4 * g + q]);
+          for (int q = 0; q < 4; ++q) h[q] = E::st(alpha * acc[ib][jb][4 * g + q]);
           uint2 pk;
           pk.x = h[0] | (h[1] << 16);
           pk.y = h[2] | (h[3] << 16);
@@ -582,7 +583,7 @@ gemm_nt(GemmParams p) {
           const int64_t j = col_base + jb * 32 + lr;
           float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = p.alpha * acc[ib][jb][4 * g + q];
+          for (int q = 0; q < 4; ++q) v[q] = alpha * acc[ib][jb][4 * g + q];
           if (!diag_tile) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -640,7 +641,7 @@ gemm_nt(GemmParams p) {
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            v[q] = p.alpha * acc[ib][jb][4 * g + q];
+            v[q] = alpha * acc[ib][jb][4 * g + q];
             St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
           }
           if (CTm) {
@@ -676,7 +677,7 @@ gemm_nt(GemmParams p) {
             const int64_t i0 = row_base + ib * 32 + 8 * g + 4 * lh;
             const int64_t j = col_base + jb * 32 + lr;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) O[(i0 + q) * p.out_cols + j] = E::st(p.alpha * acc[ib][jb][4 * g + q]);
+            for (int q = 0; q < 4; ++q) O[(i0 + q) * p.out_cols + j] = E::st(alpha * acc[ib][jb][4 * g + q]);
           }
       return;
     }
@@ -693,7 +694,7 @@ gemm_nt(GemmParams p) {
           for (int q = 0; q < 4; ++q) {
             const int64_t i = i0 + q;
             if (i >= p.rows_eff) continue;
-            const float v = p.alpha * acc[ib][jb][4 * g + q];
+            const float v = alpha * acc[ib][jb][4 * g + q];
             const int64_t row = ridx ? ridx[i] : i;
             if (row < 0 || row >= p.out_rows) continue;
             store_out(p.out, obase + row * p.out_cols + j, p.out_dtype, v);
@@ -915,6 +916,77 @@ check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
 }
 
 // ---------------------------------------------------------------------------
+// Input path without a normalised copy (16-bit input in the compute type,
+// whole tiles): the products read X itself and take 1/(||X||_F + eps) as a
+// per-matrix factor in their epilogues, so only X^T is materialised.
+// ---------------------------------------------------------------------------
+// One 64x64 tile per workgroup: X^T tile through a padded LDS tile (16-byte
+// loads and stores), and the tile's sum of squares (fp32 per thread over 16
+// elements, then a fixed-order fp64 combination).
+template <class T>
+__global__ void __launch_bounds__(256)
+transpose_sumsq(const void *X, int64_t n, int64_t m, void *XT, double *partials) {
+  const int b = blockIdx.z;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  __shared__ double wsum[4];
+  const uint16_t *Xb = static_cast<const uint16_t *>(X) + static_cast<int64_t>(b) * n * m;
+  uint16_t *XTb = static_cast<uint16_t *>(XT) + static_cast<int64_t>(b) * m * n;
+  float sq = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    const int row = v >> 3;
+    const int cv = (v & 7) * 8;
+    const u32x4 in = *reinterpret_cast<const u32x4 *>(Xb + (r0 + row) * m + c0 + cv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float f0 = T::ld(static_cast<uint16_t>(in[q] & 0xffffu));
+      const float f1 = T::ld(static_cast<uint16_t>(in[q] >> 16));
+      sq += f0 * f0 + f1 * f1;
+    }
+    *reinterpret_cast<u32x4 *>(&tile[row][cv]) = in;
+  }
+  double d = static_cast<double>(sq);
+  for (int off = 32; off > 0; off >>= 1) d += __shfl_down(d, off, 64);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = d;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t tile_id = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    partials[static_cast<int64_t>(b) * gridDim.x * gridDim.y + tile_id] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = threadIdx.x & 63;
+    const int k = (threadIdx.x >> 6) + 4 * h;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = static_cast<uint32_t>(tile[8 * k + 2 * q][c]) | (static_cast<uint32_t>(tile[8 * k + 2 * q + 1][c]) << 16);
+    *reinterpret_cast<u32x4 *>(XTb + (c0 + c) * n + r0 + 8 * k) = o;
+  }
+}
+
+// One workgroup per matrix: fixed-order sum of the partials, then the
+// scale factors of the normalisation X / (||X||_F + eps).
+__global__ void __launch_bounds__(256)
+norm_finish(const double *partials, int64_t parts, double eps, float *inv, float *inv2) {
+  const int b = blockIdx.x;
+  __shared__ double wsum[4];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < parts; i += 256) s += partials[static_cast<int64_t>(b) * parts + i];
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off, 64);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double r = 1.0 / (sqrt(((wsum[0] + wsum[1]) + wsum[2]) + wsum[3]) + eps);
+    inv[b] = static_cast<float>(r);
+    inv2[b] = static_cast<float>(r * r);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row selection of the Dion3 update ("Dion3: Full-Stack Orthogonal Updates",
 // §6, Algorithm 4, selection step): the k rows of largest l1 norm
 // ---------------------------------------------------------------------------
@@ -1119,6 +1191,20 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
   if (io == DT_BF16) st_dispatch<EBF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   else if (io == DT_F16) st_dispatch<EF16>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
   else st_dispatch<EF32>(cdt, grid, s, X, n, m, rows_eff, row_idx, partials, parts, eps, Xh, XT, Np, Mp, ph, pt);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_sumsq(int dt, const void *X, int64_t batch, int64_t n, int64_t m,
+                                  void *XT, double *partials, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(m / 64), static_cast<unsigned>(n / 64), static_cast<unsigned>(batch));
+  if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, partials);
+  else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finish(const double *partials, int64_t batch, int64_t parts, double eps,
+                              float *inv, float *inv2, hipStream_t s) {
+  norm_finish<<<static_cast<unsigned>(batch), 256, 0, s>>>(partials, parts, eps, inv, inv2);
   return hipGetLastError();
 }
 

@@ -426,3 +426,27 @@ def test_graph_capture_replays(split):
         want = eager if rep % 2 == 0 else eager2
         assert torch.equal(static_out, want), f"replay {rep}"
         _ = (static_out.float() * 2).sum().item()   # eager work between replays
+
+
+@pytest.mark.parametrize("algo,restarts", [("gram", (2,)), ("gram", ()), ("gram", (1, 3)), ("standard", ())])
+@pytest.mark.parametrize("io,tile", [("bf16", 128), ("bf16", 256), ("f16", 256)])
+def test_direct_input_path(algo, restarts, io, tile):
+    """Whole-tile shapes with the input already in the compute type: the
+    products read X itself and apply the normalisation in their epilogues
+    (no normalised copy).  Against the oracle, T = 1 and T = 5."""
+    gns = need_gpu()
+    B, n, m = 3, 512, 1536
+    X, X64 = _inputs(B, n, m, io, seed=35)
+    say(f"direct {algo} restarts={restarts} io={io} tile={tile}")
+    for co in (NS5, NS5[:1]):
+        rs = tuple(r for r in restarts if r < len(co))
+        if algo == "gram":
+            out = gns.gram_ns_batched(X.cuda(), co, restarts=rs, tile=tile)
+        else:
+            out = gns.standard_ns_batched(X.cuda(), co, tile=tile)
+        torch.cuda.synchronize()
+        ref = np.stack([oracle.gram_ns(X64[b], co, restarts=rs) if algo == "gram"
+                        else oracle.standard_ns(X64[b], co) for b in range(B)])
+        errs = per_matrix_rel(synth.as_f64(out), ref)
+        say("  T", len(co), "rel errs", errs)
+        assert max(errs) <= TOL_HALF
