@@ -211,7 +211,10 @@ void set_scale(GemmParams *p, float alpha, float beta) {
 // Runs of tiles dealt to one XCD (the kernel's xcd_chunk): one matrix per
 // run with xpm = 1, else 1/xpm of a matrix so that xpm XCDs share each
 // matrix.  Falls back to one contiguous run per XCD when the sizes do not
-// divide.
+// divide.  Every product uses xpm = 4 (a quarter matrix per run): measured
+// on 8 x 4096x16384 bf16 against 1, 2 and 8 per product kind, it keeps the
+// matrices in flight within the shared last-level cache while each XCD's L2
+// still sees a compact block of tiles.
 int xcd_chunk(int64_t tiles_per_mat, int64_t batch, int xpm) {
   const int64_t S = ((tiles_per_mat * batch) & ~int64_t(7)) / 8;
   if (S == 0) return 1;
@@ -272,7 +275,7 @@ gns_status syrk(const Ctx &c, void *R, bool from_input = false) {
   p.K = static_cast<int>(M);
   p.tiles_m = p.tiles_n = nt;
   p.tiles_per_mat = nt * (nt + 1) / 2;
-  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 1);
+  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
   p.C = R; p.ldc = N; p.sC = c.sq_stride();
   p.pA = p.pB = c.plane_rect();
   p.pC = c.plane_sq();

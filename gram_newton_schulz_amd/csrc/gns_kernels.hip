@@ -240,7 +240,7 @@ gemm_nt(GemmParams p) {
   // Long runs keep one matrix per XCD (most L2 reuse); runs of a fraction of
   // a matrix let several XCDs work on the same matrix at once, which keeps
   // the set of matrices in flight small enough for the shared last-level
-  // cache.
+  // cache (the host uses a quarter matrix per run).
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int G8 = G & ~7;
