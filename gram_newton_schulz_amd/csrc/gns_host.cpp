@@ -234,9 +234,11 @@ GemmParams base_params(const Ctx &c) {
   return p;
 }
 
-// C = alpha * A B + beta * D for n x n iterates (B symmetric), mirrored.
+// C = alpha * A B + beta * D (+ beta2 * D2) for n x n iterates (B
+// symmetric), mirrored.
 gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float beta, const void *D,
-                void *C, void *C2, float diag1, float diag2, const char *what, double flops) {
+                void *C, void *C2, float diag1, float diag2, const char *what, double flops,
+                const void *D2 = nullptr, float beta2 = 0.0f) {
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np;
   const int nt = static_cast<int>(N / c.pl->tile);
@@ -248,12 +250,17 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
   set_scale(&p, alpha, beta);
   if (D) { p.DT = D; p.lddt = N; p.sDT = c.sq_stride(); }   // D is symmetric
+  if (D && D2) {
+    p.DT2 = D2;
+    p.init_scale2 = alpha != 0.0f ? beta2 / alpha : beta2;
+    p.pDT2 = c.plane_sq();
+  }
   p.C = C; p.ldc = N; p.sC = c.sq_stride();
   p.C2 = C2; p.sC2 = c.sq_stride();
   p.pA = p.pB = p.pDT = p.pC = p.pC2 = c.plane_sq();
   p.diag1 = diag1; p.diag2 = diag2;
   const double n = static_cast<double>(c.pl->r);
-  const double bytes = c.batch * n * n * c.pl->esz * (3.0 + (D ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
+  const double bytes = c.batch * n * n * c.pl->esz * (3.0 + (D ? 1.0 : 0.0) + (D2 ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
   LaunchScope ls(c.s, what, gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), flops * c.batch,
                  bytes);
   hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, gns::MODE_SYM, p, c.s);
@@ -474,6 +481,7 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
   void *XT[2] = {c.xt(0), c.xt(1)};
   int qcur = 0, xcur = 0;
   bool q_is_identity = true;
+  float q_shift = 0.0f;   // Q is Qb[qcur] + q_shift I (nonzero right after an identity Q)
   const double nn = static_cast<double>(c.pl->r);
   const double n3 = nn * nn * nn;
 
@@ -488,9 +496,10 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     if (t > 1 && restart_at[t - 1]) {
       // restart: X <- Q X (row layout in place, transposed copy swapped),
       // R <- X X^T, Q <- I
-      st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], 0.0f, false, nullptr, io, n, nullptr, "restart_apply",
+      st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], q_shift, false, nullptr, io, n, nullptr, "restart_apply",
                  x_scale);
       x_scale = nullptr;
+      q_shift = 0.0f;
       if (st != GNS_OK) return st;
       xcur ^= 1;
       if ((st = syrk(c, R)) != GNS_OK) return st;
@@ -498,22 +507,33 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     }
     const bool need_r = (t < T) && !restart_at[t];
     if (!naive) {
-      // Z = b R + c R^2; with Q = I the Q update is Z + a I, written by the
-      // same kernel as a second output
+      // Z = b R + c R^2.  With Q = I the Q update is Z + a I (Dion3 §4.1:
+      // the first product is free); it stays implicit: Z goes into the Q
+      // buffer and the next product that uses Q adds the a I term itself.
+      const void *Zt = Z;
       if (q_is_identity) {
-        st = symm(c, R, R, cc, b, R, Z, Qb[qcur], 0.0f, a, "poly_q", n3);
+        st = symm(c, R, R, cc, b, R, Qb[qcur], nullptr, 0.0f, 0.0f, "poly_q", n3);
+        Zt = Qb[qcur];
+        q_shift = a;                   // Q = Qb[qcur] + q_shift I
         q_is_identity = false;
       } else {
         st = symm(c, R, R, cc, b, R, Z, nullptr, 0.0f, 0.0f, "poly", n3);
         if (st == GNS_OK) {
-          st = symm(c, Qb[qcur], Z, 1.0f, a, Qb[qcur], Qb[qcur ^ 1], nullptr, 0.0f, 0.0f, "q_update", n3);
+          if (q_shift != 0.0f) {
+            // (Zq + s I) Z + a (Zq + s I) = Zq Z + a Zq + s Z + a s I
+            st = symm(c, Qb[qcur], Z, 1.0f, a, Qb[qcur], Qb[qcur ^ 1], nullptr, a * q_shift, 0.0f,
+                      "q_update", n3, Z, q_shift);
+            q_shift = 0.0f;
+          } else {
+            st = symm(c, Qb[qcur], Z, 1.0f, a, Qb[qcur], Qb[qcur ^ 1], nullptr, 0.0f, 0.0f, "q_update", n3);
+          }
           qcur ^= 1;
         }
       }
       if (st != GNS_OK) return st;
       if (need_r) {
-        if ((st = symm(c, R, Z, 1.0f, a, R, RZ, nullptr, 0.0f, 0.0f, "rz", n3)) != GNS_OK) return st;
-        if ((st = symm(c, Z, RZ, 1.0f, a, RZ, R, nullptr, 0.0f, 0.0f, "r_update", n3)) != GNS_OK) return st;
+        if ((st = symm(c, R, Zt, 1.0f, a, R, RZ, nullptr, 0.0f, 0.0f, "rz", n3)) != GNS_OK) return st;
+        if ((st = symm(c, Zt, RZ, 1.0f, a, RZ, R, nullptr, 0.0f, 0.0f, "r_update", n3)) != GNS_OK) return st;
       }
     } else {
       // Algorithm 2 algebra: Z = a I + b R + c R^2, Q <- Q Z, R <- Z R Z
@@ -535,7 +555,7 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     }
   }
   // out = Q_T X
-  return apply(c, Qb[qcur], XT[xcur], nullptr, 0.0f, true, out, io, n, row_idx, "final_apply", x_scale);
+  return apply(c, Qb[qcur], XT[xcur], nullptr, q_shift, true, out, io, n, row_idx, "final_apply", x_scale);
 }
 
 // The direct input path applies when X can stand in for its normalised copy:

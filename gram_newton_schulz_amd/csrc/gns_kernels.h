@@ -45,6 +45,9 @@ struct GemmParams {
   float init_scale;                 // acc starts at init_scale * D
   const void *DT; int64_t lddt, sDT;  // D read transposed: D(i,j) = DT[j*lddt + i];
                                       // may be null (D = 0)
+  const void *DT2;                  // optional second term init_scale2 * D2, same
+  float init_scale2;                //   layout as DT (needs DT)
+  int64_t pDT2;
   void *C; int64_t ldc, sC;
   void *C2; int64_t sC2;            // MODE_SYM second output (ld = ldc); may be null
   float diag1, diag2;               // MODE_SYM: added to C / C2 on the diagonal

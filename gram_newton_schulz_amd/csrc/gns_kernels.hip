@@ -371,6 +371,36 @@ gemm_nt(GemmParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = p.init_scale * v[q];
         }
+    if (p.DT2) {
+      // second term (only the Q update that follows an identity Q has one):
+      // loaded and added here
+      const S *D2m = static_cast<const S *>(p.DT2) + static_cast<int64_t>(mat) * p.sDT;
+      const int64_t i_base = static_cast<int64_t>(ti) * TILE + wr + 4 * lh;
+      const int64_t j_base = static_cast<int64_t>(tj) * TILE + wc + lr;
+#pragma unroll
+      for (int i = 0; i < NBI; ++i)
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const S *src = D2m + (j_base + j * 32) * p.lddt + i_base + i * 32 + 8 * g;
+#pragma unroll
+            for (int pl = 0; pl < PL; ++pl) {
+              const RawD u = *reinterpret_cast<const RawD *>(src + pl * p.pDT2);
+              float v[4];
+              if constexpr (ESZ == 2) {
+                v[0] = E::ld(static_cast<S>(u.x & 0xffffu));
+                v[1] = E::ld(static_cast<S>(u.x >> 16));
+                v[2] = E::ld(static_cast<S>(u.y & 0xffffu));
+                v[3] = E::ld(static_cast<S>(u.y >> 16));
+              } else {
+                v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] += p.init_scale2 * v[q];
+            }
+          }
+    }
   };
   if (has_d) load_d();
 
