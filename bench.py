@@ -62,7 +62,8 @@ def short_kernel(name):
         if m.group(4) == "2":
             dt = "bf16x3"
         return f"gemm_nt<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
-    for k in ("norm_partial", "scale_transpose", "check_rows"):
+    for k in ("norm_partial", "scale_transpose", "transpose_sumsq", "norm_finish", "row_l1",
+              "select_topk", "check_rows"):
         if k in name:
             return k
     return name.split("(")[0][:60]
@@ -130,7 +131,8 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib):
     for src, key, scale in ((fetch, "fetch", fs), (write, "write", ws)):
         for d in src.values():
             name = short_kernel(d["kernel"])
-            if not (name.startswith("gemm_nt") or name in ("norm_partial", "scale_transpose")):
+            if not (name.startswith("gemm_nt") or name in ("norm_partial", "scale_transpose",
+                                                             "transpose_sumsq", "norm_finish")):
                 continue
             a = agg.setdefault(name, {"fetch": [], "write": []})
             a[key].append(d["v"] * 1024.0 * scale)
