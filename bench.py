@@ -109,7 +109,7 @@ def _pmc_per_dispatch(dirname, counter):
     return out
 
 
-def summarize_pmc(fetch_dir, write_dir, calib_mib):
+def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
     """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scaled by the
     reading of the calibration copy (a device copy of calib_mib MiB, which
     reads and writes exactly that many bytes)."""
@@ -145,12 +145,14 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib):
         print(f"{name:34s} {nf:8d} {f_avg / 2 ** 20:17.1f} {w_avg / 2 ** 20:17.1f}")
         print("TRAFFIC " + json.dumps({"kernel": name, "bytes_per_launch": f_avg + w_avg,
                                         "fetch_bytes": f_avg, "write_bytes": w_avg,
+                                        "workload": workload,
                                         "source_sha256_16": kernel_source_hash()}))
 
 
-def traffic_from_profile(kernel):
-    """HBM bytes per launch of `kernel` recorded in profiles/ by
-    --summarize-pmc, or None when absent or taken on a different kernel source."""
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` recorded in profiles/ by
+    --summarize-pmc, or None when absent, taken on another workload or taken
+    on a different kernel source."""
     try:
         names = [n for n in os.listdir(PROFILES) if n.endswith(".txt")]
     except FileNotFoundError:
@@ -161,7 +163,8 @@ def traffic_from_profile(kernel):
             for line in f:
                 if line.startswith("TRAFFIC "):
                     rec = json.loads(line[len("TRAFFIC "):])
-                    if rec.get("kernel") == kernel and rec.get("source_sha256_16") == h:
+                    if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                            and rec.get("source_sha256_16") == h):
                         return round(rec["bytes_per_launch"])
     return None
 
@@ -191,7 +194,7 @@ def main():
         summarize_stats(args.summarize_stats)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, calib_mib=args.calib_copy_mib)
+        summarize_pmc(*args.summarize_pmc, calib_mib=args.calib_copy_mib, workload=args.workload)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -302,7 +305,7 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(dom_tflops / peak, 4),
-        "traffic": traffic_from_profile(dom_name),
+        "traffic": traffic_from_profile(dom_name, args.workload),
         "avg_launch_ms": round(dom_avg_ms, 4),
         "launches_per_step": dom["launches"] / args.steps,
         "share_of_step": round(dom["ms"] / args.steps / ms, 4),
