@@ -21,6 +21,10 @@ Every routine follows the written description in
                        norm.
 * ``dion3_rows``    -- §6, Algorithm 4: orthogonalise the selected rows M[S,:]
                        as one k x m matrix and write them back.
+* ``dion3_step``    -- §6, Algorithm 4 in full (momentum sum, selection,
+                       orthogonalisation, the optional NorMuon steps of §2.1
+                       eq. (2), weight decay, update of the selected rows,
+                       error feedback).
 * ``flops_*``       -- §2.2 and §4.1 FLOP models, §4.2 restart surcharge.
 
 Arithmetic is float64 numpy (BLAS matmul) for float inputs.  For inputs of
@@ -36,6 +40,14 @@ Reading of the pages taken here (each also listed in the design notes):
   Q_s X, re-form R from it and reset Q to I (X is not renormalised);
 * the coefficient triple of iteration t is (a_t, b_t, c_t) with
   p_t(x) = a_t x + b_t x^3 + c_t x^5 and h_t(y) = a_t + b_t y + c_t y^2;
+* NorMuon divides each selected row by the square root of its second moment
+  plus eps (the root sign is lost in the extracted text of Algorithm 4 and
+  eq. (2); the recap describes an Adam-style second moment); weight decay
+  scales every row of W, the update and the error feedback touch the
+  selected rows only (Algorithm 4 marks those two lines "for i in S");
+* the one stored value the selection reads, the momentum sum M + G, is
+  formed as an fp32 addition, as the caller's fp32 buffer holds it; all
+  later steps are fp64;
 * the pages take n <= m without loss of generality; a tall X (n > m) is
   orthogonalised through its transpose: the iteration runs on X^T and the
   result is transposed back (polar(X) = polar(X^T)^T, and each odd
@@ -53,8 +65,8 @@ EPS = 1e-7
 
 __all__ = [
     "EPS", "frobenius_normalize", "standard_ns", "gram_ns", "theorem2_q",
-    "composed_poly", "spectral_map", "polar", "dion3_select", "dion3_rows", "flops_standard",
-    "flops_gram", "gram_ns_trace",
+    "composed_poly", "spectral_map", "polar", "dion3_select", "dion3_rows", "dion3_step",
+    "flops_standard", "flops_gram", "gram_ns_trace",
 ]
 
 
@@ -287,6 +299,44 @@ def dion3_rows(X, out_init, rows: Sequence[int], coeffs, restarts=(2,),
     out = np.array(out_init, dtype=np.float64, copy=True)
     out[rows, :] = gram_ns(X[rows, :], coeffs, restarts, algebra, eps)
     return out
+
+
+def dion3_step(W, G, M, v, k: int, coeffs, restarts=(2,), lr=0.02, weight_decay=0.0,
+               momentum=0.95, beta2=0.95, eps=1e-8, normuon=True, algebra="stabilized"):
+    """One Dion3 update of one weight matrix (Dion3 §6, Algorithm 4), with
+    Gram Newton-Schulz as its polar step and, when ``normuon``, the NorMuon
+    steps of §2.1 eq. (2).  In order:
+
+    1. the momentum takes the gradient: M + G (an fp32 addition: the caller's
+       momentum buffer is fp32, and the selection reads the stored sum);
+    2. S = the k rows of that sum with the largest l1 norm (dion3_select);
+    3. O = Gram Newton-Schulz of the k x m submatrix of those rows;
+    4. NorMuon: v_i <- beta2 v_i + (1 - beta2) mean_j O_ij^2 for i in S,
+       O_ij <- O_ij / (sqrt(v_i) + eps), then O is rescaled to the Frobenius
+       norm it had before that division;
+    5. weight decay on every row: W <- (1 - lr * weight_decay) W;
+    6. the selected rows move: W[S] <- W[S] - lr * O;
+    7. error feedback on the selected rows: M[S] <- momentum * M[S].
+
+    Returns a dict with W, M, v (fp64 arrays; v untouched without NorMuon),
+    S (int64, ascending) and O (the k x m update direction after step 4).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    Msum = (np.asarray(M, dtype=np.float32) + np.asarray(G, dtype=np.float32)).astype(np.float64)
+    n, m = Msum.shape
+    S = dion3_select(Msum, k)
+    O = gram_ns(Msum[S, :], coeffs, restarts, algebra)
+    v_new = np.array(v, dtype=np.float64, copy=True) if v is not None else None
+    if normuon:
+        second = beta2 * v_new[S] + (1.0 - beta2) * np.mean(O * O, axis=1)
+        v_new[S] = second
+        On = O / (np.sqrt(second) + eps)[:, None]
+        O = On * (np.linalg.norm(O) / np.linalg.norm(On))
+    W_new = (1.0 - lr * weight_decay) * W
+    W_new[S, :] -= lr * O
+    M_new = Msum.copy()
+    M_new[S, :] *= momentum
+    return {"W": W_new, "M": M_new, "v": v_new, "S": S, "O": O}
 
 
 # --------------------------------------------------------------------------

@@ -308,6 +308,71 @@ def pin_dion3_select(O):
     assert set(O.dion3_select(M[perm], 9)) == {int(np.where(perm == i)[0][0]) for i in sel}
 
 
+# ---------------------------------------------------------------------------
+# The whole Dion3 update (Algorithm 4 with the NorMuon steps of eq. (2))
+# ---------------------------------------------------------------------------
+def pin_dion3_step(O):
+    from fractions import Fraction
+    sched = load_schedules()
+    ns5 = [tuple(float(v) for v in sched["muon_ns5"])] * 5
+    n, m, lr = 12, 40, 0.03
+    W, G, M = _randn((n, m), 21), _randn((n, m), 22), _randn((n, m), 23)
+    Msum32 = np.float32(M) + np.float32(G)          # the stored fp32 momentum sum
+    Msum = Msum32.astype(np.float64)
+    v0 = np.abs(_randn(n, 24)) + 0.1
+
+    # k = n, no NorMuon, no decay: W moves by -lr times the closed form of
+    # the finite iteration on M + G (thin SVD), M becomes momentum * (M + G)
+    r = O.dion3_step(W, G, M, v0, n, ns5, lr=lr, weight_decay=0.0, momentum=0.5, normuon=False)
+    assert list(r["S"]) == list(range(n))
+    assert _rel(W - r["W"], lr * _closed_form(Msum, ns5)) <= 1e-10
+    assert np.array_equal(r["M"], 0.5 * Msum) and np.array_equal(r["v"], v0)
+
+    # selection on the momentum sum: exact rational l1 norms of the fp32 values
+    k = 5
+    r = O.dion3_step(W, G, M, v0, k, ns5, lr=lr, weight_decay=0.1, momentum=0.25, normuon=False)
+    exact = [sum(abs(Fraction(float(x))) for x in Msum32[i]) for i in range(n)]
+    top = sorted(sorted(range(n), key=lambda i: -exact[i])[:k])
+    assert list(r["S"]) == top
+    rest = [i for i in range(n) if i not in top]
+    decay = 1.0 - lr * 0.1
+    assert np.array_equal(r["W"][rest], decay * W[rest])          # decay only
+    assert np.array_equal(r["M"][rest], Msum[rest])                # momentum sum kept
+    assert np.array_equal(r["M"][top], 0.25 * Msum[top])           # error feedback
+    cf = _closed_form(Msum[top], ns5)
+    assert _rel(decay * W[top] - r["W"][top], lr * cf) <= 1e-10   # own normalisation of M[S]
+
+    # lr * weight_decay = 1 zeroes the unselected rows; momentum 0 zeroes the
+    # selected momentum rows
+    r = O.dion3_step(W, G, M, v0, k, ns5, lr=lr, weight_decay=1.0 / lr, momentum=0.0, normuon=False)
+    assert not r["W"][rest].any() and not r["M"][top].any()
+    assert _rel(-r["W"][top], lr * cf) <= 1e-10
+
+    # NorMuon, beta2 = 0: the second moment is this step's row mean square, so
+    # every row ends with the same norm, and the rescale keeps ||O||_F
+    r = O.dion3_step(W, G, M, v0, k, ns5, lr=lr, momentum=0.9, beta2=0.0, eps=1e-12, normuon=True)
+    rn = np.linalg.norm(r["O"], axis=1)
+    assert np.max(np.abs(rn / rn[0] - 1.0)) <= 1e-9
+    assert abs(np.linalg.norm(r["O"]) / np.linalg.norm(cf) - 1.0) <= 1e-10
+    assert np.allclose(r["v"][top], np.mean(cf * cf, axis=1), rtol=1e-10, atol=0)
+    assert np.array_equal(r["v"][rest], v0[rest])
+
+    # NorMuon, beta2 = 1: v stays as given and row i is divided by
+    # sqrt(v_i) + eps before the common rescale
+    v1 = v0.copy()
+    v1[top] = [1.0, 4.0, 9.0, 16.0, 25.0]
+    r = O.dion3_step(W, G, M, v1, k, ns5, lr=lr, beta2=1.0, eps=0.0, normuon=True)
+    assert np.array_equal(r["v"], v1)
+    ratio = np.linalg.norm(r["O"], axis=1) / np.linalg.norm(cf, axis=1)
+    assert np.allclose(ratio * np.array([1.0, 2.0, 3.0, 4.0, 5.0]), ratio[0], rtol=1e-10, atol=0)
+    assert abs(np.linalg.norm(r["O"]) / np.linalg.norm(cf) - 1.0) <= 1e-10
+
+    # NorMuon, beta2 = 1/2: the new second moment averages the old one and
+    # the row mean square of the orthogonalised rows
+    r = O.dion3_step(W, G, M, v1, k, ns5, lr=lr, beta2=0.5, eps=1e-8, normuon=True)
+    assert np.allclose(r["v"][top], 0.5 * v1[top] + 0.5 * np.mean(cf * cf, axis=1), rtol=1e-10, atol=0)
+
+
 FAST_PINS = [pin_exact_equivalence, pin_restart_semantics, pin_rank_one_exact, pin_theorem2, pin_spectral,
-             pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3, pin_dion3_select]
+             pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3, pin_dion3_select, pin_dion3_step]
 ALL_PINS = FAST_PINS + [pin_exact_equivalence_t4]

@@ -40,6 +40,18 @@ MUTATIONS = {
     "select ties to larger index": ("key=lambda i: (-keys[i], i))", "key=lambda i: (-keys[i], -i))"),
     "select smallest rows": ("key=lambda i: (-keys[i], i))", "key=lambda i: (keys[i], i))"),
     "select l2 instead of l1": ("keys = [math.fsum(np.abs(M[i])) for i in range(n)]", "keys = [math.fsum(M[i] * M[i]) for i in range(n)]"),
+    "step momentum not added": ("np.asarray(M, dtype=np.float32) + np.asarray(G, dtype=np.float32)",
+                                "np.asarray(M, dtype=np.float32) + 0 * np.asarray(G, dtype=np.float32)"),
+    "step selects before the sum": ("S = dion3_select(Msum, k)", "S = dion3_select(np.asarray(M, dtype=np.float64), k)"),
+    "normuon root dropped": ("On = O / (np.sqrt(second) + eps)[:, None]", "On = O / (second + eps)[:, None]"),
+    "normuon no rescale": ("O = On * (np.linalg.norm(O) / np.linalg.norm(On))", "O = On"),
+    "normuon sum not mean": ("np.mean(O * O, axis=1)", "np.sum(O * O, axis=1)"),
+    "normuon beta swapped": ("second = beta2 * v_new[S] + (1.0 - beta2) * np.mean",
+                             "second = (1.0 - beta2) * v_new[S] + beta2 * np.mean"),
+    "decay on selected rows only": ("W_new = (1.0 - lr * weight_decay) * W\n",
+                                    "W_new = W.copy()\n    W_new[S, :] *= 1.0 - lr * weight_decay\n"),
+    "update sign": ("W_new[S, :] -= lr * O", "W_new[S, :] += lr * O"),
+    "error feedback on every row": ("M_new[S, :] *= momentum", "M_new *= momentum"),
 }
 
 
