@@ -313,7 +313,8 @@ def dion3_step(W, G, M, v, k: int, coeffs, restarts=(2,), lr=0.02, weight_decay=
     3. O = Gram Newton-Schulz of the k x m submatrix of those rows;
     4. NorMuon: v_i <- beta2 v_i + (1 - beta2) mean_j O_ij^2 for i in S,
        O_ij <- O_ij / (sqrt(v_i) + eps), then O is rescaled to the Frobenius
-       norm it had before that division;
+       norm it had before that division (a zero O stays zero: the pages'
+       ratio is 0/0 there);
     5. weight decay on every row: W <- (1 - lr * weight_decay) W;
     6. the selected rows move: W[S] <- W[S] - lr * O;
     7. error feedback on the selected rows: M[S] <- momentum * M[S].
@@ -331,7 +332,10 @@ def dion3_step(W, G, M, v, k: int, coeffs, restarts=(2,), lr=0.02, weight_decay=
         second = beta2 * v_new[S] + (1.0 - beta2) * np.mean(O * O, axis=1)
         v_new[S] = second
         On = O / (np.sqrt(second) + eps)[:, None]
-        O = On * (np.linalg.norm(O) / np.linalg.norm(On))
+        # the rescale to ||O||_F is 0/0 when the selected rows orthogonalise
+        # to zero (a zero momentum sum); the update then stays zero
+        norm_on = np.linalg.norm(On)
+        O = On * (np.linalg.norm(O) / norm_on) if norm_on > 0 else On
     W_new = (1.0 - lr * weight_decay) * W
     W_new[S, :] -= lr * O
     M_new = Msum.copy()

@@ -372,6 +372,17 @@ def pin_dion3_step(O):
     r = O.dion3_step(W, G, M, v1, k, ns5, lr=lr, beta2=0.5, eps=1e-8, normuon=True)
     assert np.allclose(r["v"][top], 0.5 * v1[top] + 0.5 * np.mean(cf * cf, axis=1), rtol=1e-10, atol=0)
 
+    # a zero momentum sum: every key ties at 0, so the first k rows are
+    # taken; Newton-Schulz of zero is zero, NorMuon leaves it zero (the
+    # Frobenius rescale is 0/0 there), W only decays and v only decays
+    Z = np.zeros((n, m))
+    r = O.dion3_step(W, Z, Z, v1, k, ns5, lr=lr, weight_decay=0.5, beta2=0.5, eps=1e-8, normuon=True)
+    assert list(r["S"]) == list(range(k))
+    assert np.all(np.isfinite(r["O"])) and not r["O"].any()
+    assert np.array_equal(r["W"], (1.0 - lr * 0.5) * W)
+    assert np.array_equal(r["v"][:k], 0.5 * v1[:k]) and np.array_equal(r["v"][k:], v1[k:])
+    assert not r["M"].any()
+
 
 FAST_PINS = [pin_exact_equivalence, pin_restart_semantics, pin_rank_one_exact, pin_theorem2, pin_spectral,
              pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3, pin_dion3_select, pin_dion3_step]

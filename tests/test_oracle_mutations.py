@@ -44,7 +44,9 @@ MUTATIONS = {
                                 "np.asarray(M, dtype=np.float32) + 0 * np.asarray(G, dtype=np.float32)"),
     "step selects before the sum": ("S = dion3_select(Msum, k)", "S = dion3_select(np.asarray(M, dtype=np.float64), k)"),
     "normuon root dropped": ("On = O / (np.sqrt(second) + eps)[:, None]", "On = O / (second + eps)[:, None]"),
-    "normuon no rescale": ("O = On * (np.linalg.norm(O) / np.linalg.norm(On))", "O = On"),
+    "normuon no rescale": ("O = On * (np.linalg.norm(O) / norm_on) if norm_on > 0 else On", "O = On"),
+    "normuon zero rescale gives nan": ("O = On * (np.linalg.norm(O) / norm_on) if norm_on > 0 else On",
+                                       "O = On * (np.linalg.norm(O) / norm_on) if norm_on >= 0 else On"),
     "normuon sum not mean": ("np.mean(O * O, axis=1)", "np.sum(O * O, axis=1)"),
     "normuon beta swapped": ("second = beta2 * v_new[S] + (1.0 - beta2) * np.mean",
                              "second = (1.0 - beta2) * v_new[S] + beta2 * np.mean"),
