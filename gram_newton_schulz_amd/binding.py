@@ -28,7 +28,7 @@ _DT = {torch.float32: GNS_F32, torch.bfloat16: GNS_BF16, torch.float16: GNS_F16}
 _STATUS = {
     0: "GNS_OK", 1: "GNS_E_NULL", 2: "GNS_E_SHAPE", 3: "GNS_E_DTYPE", 4: "GNS_E_COEFF",
     5: "GNS_E_RESTART", 6: "GNS_E_ROWIDX", 7: "GNS_E_ALIAS", 8: "GNS_E_WORKSPACE",
-    9: "GNS_E_HIP", 10: "GNS_E_FLAGS",
+    9: "GNS_E_HIP", 10: "GNS_E_FLAGS", 11: "GNS_E_PARAM",
 }
 
 #: every symbol include/gns.h declares
@@ -37,6 +37,7 @@ EXPORTS = [
     "gns_standard_workspace_bytes", "gns_gram_batched", "gns_standard_batched",
     "gns_check_row_idx", "gns_timing_enable", "gns_timing_read", "gns_timing_reset",
     "gns_select_workspace_bytes", "gns_select_rows_l1",
+    "gns_dion3_workspace_bytes", "gns_dion3_step",
 ]
 
 
@@ -85,6 +86,14 @@ def lib() -> ctypes.CDLL:
     L.gns_select_workspace_bytes.argtypes = [i64, i64]
     L.gns_select_rows_l1.restype = ctypes.c_int
     L.gns_select_rows_l1.argtypes = [vp, i64, i64, i64, ctypes.c_int, i64, vp, vp, sz, vp]
+    L.gns_dion3_workspace_bytes.restype = sz
+    L.gns_dion3_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+    dbl = ctypes.c_double
+    L.gns_dion3_step.restype = ctypes.c_int
+    L.gns_dion3_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                 dbl, dbl, dbl, dbl, dbl, ctypes.c_int, vp, ctypes.c_uint, vp, sz, vp]
     L.gns_check_row_idx.restype = ctypes.c_int
     L.gns_check_row_idx.argtypes = [vp, i64, i64, i64, vp, vp]
     L.gns_timing_enable.argtypes = [ctypes.c_int]
@@ -289,3 +298,49 @@ def safety_scaled(coeffs: Sequence, s: float = 1.05) -> list:
     if not s > 0:
         raise ValueError("safety factor must be positive")
     return [(float(a) / s, float(b) / s ** 3, float(c) / s ** 5) for a, b, c in coeffs]
+
+
+def dion3_workspace_bytes(compute_dtype, batch: int, n: int, m: int, k: int) -> int:
+    return int(lib().gns_dion3_workspace_bytes(_dtype_code(compute_dtype), batch, n, m, k))
+
+
+def dion3_step(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, v: Optional[torch.Tensor],
+               k: int, coeffs: Sequence, restarts: Sequence[int] = (2,), *, lr: float = 0.02,
+               weight_decay: float = 0.0, mu: float = 0.95, beta2: float = 0.95, eps: float = 1e-8,
+               normuon: bool = True, compute_dtype=torch.bfloat16, naive_algebra: bool = False,
+               square_fallback: bool = True, tile: Optional[int] = None, split_batch: bool = True,
+               row_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """One Dion3 update (Algorithm 4) of every matrix in W ([batch, n, m] or
+    [n, m], fp32) via gns_dion3_step: W, M (fp32) and v (fp32 [batch, n], or
+    None without NorMuon) are updated in place; G is fp32, bf16 or fp16.
+    Returns the selected rows S (int64 [batch, k], ascending)."""
+    squeeze = W.dim() == 2
+    Wb, Gb, Mb = (t.unsqueeze(0) if squeeze else t for t in (W, G, M))
+    vb = None if v is None else (v.unsqueeze(0) if v.dim() == 1 else v)
+    for name, t in (("W", Wb), ("G", Gb), ("M", Mb)):
+        if t.dim() != 3 or not t.is_contiguous():
+            raise GnsError(2, f"{name} must be a contiguous [batch, n, m] tensor")
+    if Wb.dtype != torch.float32 or Mb.dtype != torch.float32:
+        raise GnsError(3, "W and M must be float32")
+    B, n, m = Wb.shape
+    if Gb.shape != Wb.shape or Mb.shape != Wb.shape:
+        raise GnsError(2, "W, G and M must have the same shape")
+    if vb is not None and (vb.dtype != torch.float32 or vb.shape != (B, n) or not vb.is_contiguous()):
+        raise GnsError(2, "v must be a contiguous float32 [batch, n] tensor")
+    cdt = _dtype_code(compute_dtype)
+    if row_idx is None:
+        row_idx = torch.empty(B, k, dtype=torch.int64, device=Wb.device)
+    ws = _workspace(dion3_workspace_bytes(cdt, B, n, m, k), Wb.device, workspace)
+    carr, T = _coeff_array(coeffs)
+    rs = list(restarts)
+    rarr = (ctypes.c_int * max(len(rs), 1))(*rs)
+    _check(lib().gns_dion3_step(
+        _ptr(Wb), _ptr(Gb), _ptr(Mb), _ptr(vb), B, n, m, _dtype_code(Gb.dtype), cdt, k, carr, T,
+        rarr, len(rs), float(lr), float(weight_decay), float(mu), float(beta2), float(eps),
+        1 if normuon else 0, _ptr(row_idx),
+        (GNS_OPT_NAIVE_ALGEBRA if naive_algebra else 0)
+        | (0 if square_fallback else GNS_OPT_NO_SQUARE_FALLBACK) | _tile_opts(tile)
+        | (0 if split_batch else GNS_OPT_ONE_STREAM),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return row_idx.squeeze(0) if squeeze else row_idx

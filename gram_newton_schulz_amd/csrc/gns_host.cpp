@@ -439,8 +439,12 @@ gns_status workspace_checks(const void *X, const void *out, int64_t batch, int64
 
 // Standard Newton-Schulz (Dion3 §2.2, Algorithm 1) on a validated problem;
 // the symmetric products go through the mirrored kernel (Appendix C.3).
+// Rows row_idx of X (all rows when null) are orthogonalised; row i of the
+// result goes to row out_idx[i] of out (row i when null), out having
+// out_rows rows per matrix.
 gns_status enqueue_standard(const Ctx &c, const void *X, void *out, int io, int64_t n,
-                            const double *coeffs, int T, const int64_t *row_idx) {
+                            const double *coeffs, int T, const int64_t *row_idx,
+                            const int64_t *out_idx, int64_t out_rows) {
   const Plan &pl = *c.pl;
   void *A = c.sq(0), *B = c.sq(1);
   void *XT[2] = {c.xt(0), c.xt(1)};
@@ -462,7 +466,7 @@ gns_status enqueue_standard(const Ctx &c, const void *X, void *out, int io, int6
       st = apply(c, B, XT[xcur], XT[xcur ^ 1], a, false, nullptr, io, n, nullptr, "std_apply", x_scale);
       xcur ^= 1;
     } else {
-      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, n, row_idx, "std_final_apply", x_scale);
+      st = apply(c, B, XT[xcur], nullptr, a, true, out, io, out_rows, out_idx, "std_final_apply", x_scale);
     }
     x_scale = nullptr;
     if (st != GNS_OK) return st;
@@ -471,10 +475,11 @@ gns_status enqueue_standard(const Ctx &c, const void *X, void *out, int io, int6
 }
 
 // Gram Newton-Schulz (Dion3 §4.2, Algorithm 3; Algorithm 2 algebra when
-// `naive`) on one sub-batch of a validated problem.
+// `naive`) on one sub-batch of a validated problem; rows, out_idx and
+// out_rows as for enqueue_standard.
 gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t n,
                         const double *coeffs, int T, const std::vector<char> &restart_at,
-                        const int64_t *row_idx, bool naive) {
+                        const int64_t *row_idx, const int64_t *out_idx, int64_t out_rows, bool naive) {
   gns_status st;
   void *R = c.sq(0), *Z = c.sq(1), *RZ = c.sq(2);
   void *Qb[2] = {c.sq(3), c.sq(4)};
@@ -555,7 +560,8 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     }
   }
   // out = Q_T X
-  return apply(c, Qb[qcur], XT[xcur], nullptr, q_shift, true, out, io, n, row_idx, "final_apply", x_scale);
+  return apply(c, Qb[qcur], XT[xcur], nullptr, q_shift, true, out, io, out_rows, out_idx, "final_apply",
+               x_scale);
 }
 
 // The direct input path applies when X can stand in for its normalised copy:
@@ -634,6 +640,50 @@ gns_status run_batches(const Plan &pl, int cdt, int64_t batch, void *workspace,
   return st;
 }
 
+// --------------------------------------------------------------------------
+// Dion3 update: workspace layout after the orthogonalisation's own workspace
+// --------------------------------------------------------------------------
+struct Dion3Layout {
+  size_t off_keys = 0, off_o = 0, off_rowsq = 0, off_factor = 0, bytes = 0;
+};
+
+// The orthogonalisation's region is sized for 256-padded buffers (any tile
+// choice fits), so the regions after it do not depend on the tile.
+bool dion3_layout(int cdt, int64_t batch, int64_t n, int64_t m, int64_t k, Dion3Layout *d) {
+  Plan pl;
+  if (batch <= 0 || n < 1 || k < 1 || k > n || !make_plan(cdt, batch, k, m, 5, 256, &pl)) return false;
+  size_t off = align_up(pl.bytes, kAlign);
+  d->off_keys = off;                                  // fp64 row keys [batch][n]
+  off = align_up(off + sizeof(double) * batch * n, kAlign);
+  d->off_o = off;                                     // fp32 update O [batch][k][m]
+  off = align_up(off + sizeof(float) * batch * k * m, kAlign);
+  d->off_rowsq = off;                                 // fp64 row sums of O^2 [batch][k]
+  off = align_up(off + sizeof(double) * batch * k, kAlign);
+  d->off_factor = off;                                // fp64 row factors [batch][k]
+  off = align_up(off + sizeof(double) * batch * k, kAlign);
+  d->bytes = off;
+  return true;
+}
+
+gns_status check_coeffs(const double *coeffs, int T) {
+  if (!coeffs) return GNS_E_NULL;
+  if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
+  for (int i = 0; i < 3 * T; ++i)
+    if (!std::isfinite(coeffs[i])) return GNS_E_COEFF;
+  return GNS_OK;
+}
+
+gns_status parse_restarts(const int *restart_after, int n_restart, int T, std::vector<char> *at) {
+  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
+  at->assign(T + 2, 0);
+  for (int i = 0; i < n_restart; ++i) {
+    const int r = restart_after[i];
+    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
+    (*at)[r] = 1;
+  }
+  return GNS_OK;
+}
+
 }  // namespace
 
 // ==========================================================================
@@ -656,6 +706,7 @@ const char *gns_status_str(gns_status s) {
     case GNS_E_WORKSPACE: return "workspace missing, misaligned or too small";
     case GNS_E_HIP: return "HIP launch failed";
     case GNS_E_FLAGS: return "unknown option bits";
+    case GNS_E_PARAM: return "invalid update hyperparameter";
   }
   return "unknown status";
 }
@@ -708,8 +759,9 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
       Ctx c = c0;
       c.direct = direct;
       c.xin = Xs;
+      const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
       return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
-                              row_idx ? row_idx + c.b0 * k : nullptr);
+                              ri, ri, n);
     });
   const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
   return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c0) {
@@ -717,8 +769,9 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
     Ctx c = c0;
     c.direct = direct;
     c.xin = Xs;
+    const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
     return enqueue_gram(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
-                        restart_at, row_idx ? row_idx + c.b0 * k : nullptr, naive);
+                        restart_at, ri, ri, n, naive);
   });
 }
 
@@ -745,8 +798,9 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
                        Ctx c = c0;
                        c.direct = direct;
                        c.xin = Xs;
+                       const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
                        return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io,
-                                               n, coeffs, T, row_idx ? row_idx + c.b0 * k : nullptr);
+                                               n, coeffs, T, ri, ri, n);
                      });
 }
 
@@ -779,6 +833,106 @@ gns_status gns_select_rows_l1(const void *M, int64_t batch, int64_t n, int64_t m
                                             row_idx, s);
   ls.done();
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+size_t gns_dion3_workspace_bytes(gns_dtype cdt, int64_t batch, int64_t n, int64_t m, int64_t k) {
+  Dion3Layout d;
+  if (!dion3_layout(cdt, batch, n, m, k, &d)) return 0;
+  return d.bytes;
+}
+
+gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t batch, int64_t n,
+                          int64_t m, gns_dtype grad_dtype, gns_dtype cdt, int64_t k,
+                          const double *coeffs, int T, const int *restart_after, int n_restart,
+                          double lr, double weight_decay, double mu, double beta2, double eps,
+                          int normuon, int64_t *row_idx, unsigned opts, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (!valid_dtype(grad_dtype) || !valid_compute(cdt)) return GNS_E_DTYPE;
+  if (batch < 0 || n < 1 || m < 1 || k < 1 || k > n || batch > 65535 || n > (int64_t(1) << 30))
+    return GNS_E_SHAPE;
+  gns_status st = check_coeffs(coeffs, T);
+  if (st != GNS_OK) return st;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu) || !std::isfinite(beta2) ||
+      !std::isfinite(eps) || (normuon && !(eps > 0.0)))
+    return GNS_E_PARAM;
+  int tile_req = 0;
+  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
+    return st;
+  std::vector<char> restart_at;
+  if ((st = parse_restarts(restart_after, n_restart, T, &restart_at)) != GNS_OK) return st;
+  if (batch == 0) return GNS_OK;
+  if (!W || !G || !M || !row_idx || (normuon && !v)) return GNS_E_NULL;
+  Plan pl;
+  Dion3Layout d;
+  if (!make_plan(cdt, batch, k, m, 5, tile_req, &pl) || !dion3_layout(cdt, batch, n, m, k, &d))
+    return GNS_E_SHAPE;
+  if (!workspace || workspace_bytes < d.bytes || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return GNS_E_WORKSPACE;
+  const size_t elems = static_cast<size_t>(batch) * n * m;
+  struct Range { const void *p; size_t bytes; };
+  const Range user[] = {{W, elems * 4}, {M, elems * 4}, {G, elems * gns::dtype_size(grad_dtype)},
+                        {row_idx, sizeof(int64_t) * batch * k},
+                        {normuon ? v : nullptr, sizeof(float) * batch * n}};
+  for (const Range &r : user)
+    if (r.p && ranges_overlap(workspace, d.bytes, r.p, r.bytes)) return GNS_E_ALIAS;
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (user[i].p && user[j].p && ranges_overlap(user[i].p, user[i].bytes, user[j].p, user[j].bytes))
+        return GNS_E_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  double *keys = reinterpret_cast<double *>(ws + d.off_keys);
+  float *O = reinterpret_cast<float *>(ws + d.off_o);
+  double *rowsq = reinterpret_cast<double *>(ws + d.off_rowsq);
+  double *factor = reinterpret_cast<double *>(ws + d.off_factor);
+  const double bn = static_cast<double>(batch) * n, bk = static_cast<double>(batch) * k;
+  const double gsz = gns::dtype_size(grad_dtype);
+  // Algorithm 4, first two steps: M <- M + G, then the k rows of largest l1 norm
+  {
+    LaunchScope ls(s, "momentum_l1", "momentum_l1", 2.0 * bn * m, bn * m * (8.0 + gsz));
+    hipError_t e = gns::launch_momentum_l1(grad_dtype, M, G, batch, n, m, keys, s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  {
+    LaunchScope ls(s, "select_topk", "select_topk", bn, 8.0 * bn * 8.0 + 8.0 * bk);
+    hipError_t e = gns::launch_select_topk(keys, batch, n, k, row_idx, s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  // orthogonalise M[S,:] into the k x m update O (fp32, not scattered)
+  const size_t in_mat = static_cast<size_t>(n) * m;
+  const size_t o_mat = static_cast<size_t>(k) * m;
+  const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
+  const bool square = (k == m) && !(opts & GNS_OPT_NO_SQUARE_FALLBACK);
+  st = run_batches(pl, cdt, batch, workspace, s, !(opts & GNS_OPT_ONE_STREAM), [&](const Ctx &c) {
+    const float *Xs = M + c.b0 * in_mat;
+    float *Os = O + c.b0 * o_mat;
+    const int64_t *ri = row_idx + c.b0 * k;
+    if (square) return enqueue_standard(c, Xs, Os, GNS_F32, n, coeffs, T, ri, nullptr, k);
+    return enqueue_gram(c, Xs, Os, GNS_F32, n, coeffs, T, restart_at, ri, nullptr, k, naive);
+  });
+  if (st != GNS_OK) return st;
+  // NorMuon row factors (second moment v at the selected rows), then the
+  // decay, the update of the selected rows and the error feedback
+  {
+    LaunchScope ls(s, "normuon", "row_sumsq+normuon_factors", normuon ? 2.0 * bk * m : 0.0,
+                   normuon ? bk * m * 4.0 + bk * 16.0 : bk * 8.0);
+    hipError_t e = gns::launch_normuon(O, batch, k, m, v, row_idx, n, beta2, eps, normuon, rowsq, factor, s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  {
+    const float decay = static_cast<float>(1.0 - lr * weight_decay);
+    const double rows_w = decay != 1.0f ? bn : bk;
+    LaunchScope ls(s, "dion3_update", "dion3_update", 3.0 * bk * m, rows_w * m * 8.0 + bk * m * 12.0);
+    hipError_t e = gns::launch_dion3_update(W, M, O, row_idx, factor, batch, n, m, k, decay, lr,
+                                            static_cast<float>(mu), s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  return GNS_OK;
 }
 
 gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,

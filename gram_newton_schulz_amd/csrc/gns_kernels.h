@@ -96,4 +96,21 @@ hipError_t launch_norm_finish(const double *partials, int64_t batch, int64_t par
 hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, hipStream_t s);
 
+// Dion3 update (Algorithm 4 around the orthogonalisation).
+// M <- M + G (fp32) and keys[b][i] = sum_j |M_b[i][j]| (fp64).
+hipError_t launch_momentum_l1(int grad_dtype, float *M, const void *G, int64_t batch, int64_t n,
+                              int64_t m, double *keys, hipStream_t s);
+// out[b][0..k) = indices of the k largest keys, ascending (ties: smaller index).
+hipError_t launch_select_topk(const double *keys, int64_t batch, int64_t n, int64_t k, int64_t *out,
+                              hipStream_t s);
+// Row factors of the k x m update O: NorMuon (v updated in place at rows S)
+// with the Frobenius rescale, or all ones without NorMuon.
+hipError_t launch_normuon(const float *O, int64_t batch, int64_t k, int64_t m, float *v,
+                          const int64_t *S, int64_t n, double beta2, double eps, int normuon,
+                          double *rowsq, double *factor, hipStream_t s);
+// W <- decay W everywhere, W[S_i] -= lr factor_i O_i, M[S_i] *= mu (S ascending).
+hipError_t launch_dion3_update(float *W, float *M, const float *O, const int64_t *S,
+                               const double *factor, int64_t batch, int64_t n, int64_t m, int64_t k,
+                               float decay, double lr, float mu, hipStream_t s);
+
 }  // namespace gns

@@ -1136,6 +1136,197 @@ select_topk(const double *keys, int64_t n, int64_t k, int64_t *out) {
 }
 
 // ---------------------------------------------------------------------------
+// Dion3 update around the orthogonalisation ("Dion3: Full-Stack Orthogonal
+// Updates", §6, Algorithm 4, with the optional NorMuon steps of §2.1, eq. (2))
+// ---------------------------------------------------------------------------
+// The momentum takes the gradient, M <- M + G (one fp32 addition per
+// element, stored), and every row of the sum gets its l1 key sum_j |M_ij|
+// (fp64; lane-strided 16-byte pieces, then the wave tree: a fixed order for
+// a given shape).  One wave per row.
+template <class TG>
+__global__ void __launch_bounds__(256)
+momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *keys) {
+  using SG = typename TG::S;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int64_t base = (static_cast<int64_t>(b) * n + row) * m;
+  float *mr = M + base;
+  const SG *gr = static_cast<const SG *>(G) + base;
+  double acc = 0.0;
+  if (vec) {
+    // four elements per piece: 16 bytes of M, 16 (fp32) or 8 (16-bit) of G
+    for (int64_t v = lane; v < m / 4; v += 64) {
+      float4 mv = reinterpret_cast<const float4 *>(mr)[v];
+      float g[4];
+      if constexpr (sizeof(SG) == 4) {
+        const float4 gv = reinterpret_cast<const float4 *>(gr)[v];
+        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+      } else {
+        const uint2 gv = reinterpret_cast<const uint2 *>(gr)[v];
+        g[0] = TG::ld(static_cast<SG>(gv.x & 0xffffu));
+        g[1] = TG::ld(static_cast<SG>(gv.x >> 16));
+        g[2] = TG::ld(static_cast<SG>(gv.y & 0xffffu));
+        g[3] = TG::ld(static_cast<SG>(gv.y >> 16));
+      }
+      mv.x += g[0];
+      mv.y += g[1];
+      mv.z += g[2];
+      mv.w += g[3];
+      reinterpret_cast<float4 *>(mr)[v] = mv;
+      acc += fabs(static_cast<double>(mv.x));
+      acc += fabs(static_cast<double>(mv.y));
+      acc += fabs(static_cast<double>(mv.z));
+      acc += fabs(static_cast<double>(mv.w));
+    }
+  } else {
+    for (int64_t c = lane; c < m; c += 64) {
+      const float s = mr[c] + TG::ld(gr[c]);
+      mr[c] = s;
+      acc += fabs(static_cast<double>(s));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
+  if (lane == 0) keys[static_cast<int64_t>(b) * n + row] = acc;
+}
+
+// Sum of squares of every row of the k x m update O (fp32 values, fp64
+// sums in a fixed order), one wave per row: the row means of O^2 that the
+// NorMuon second moment takes, and the squared Frobenius norm of O.
+__global__ void __launch_bounds__(256)
+row_sumsq(const float *O, int64_t k, int64_t m, bool vec, double *rowsq) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= k) return;
+  const float *orow = O + (static_cast<int64_t>(b) * k + row) * m;
+  double acc = 0.0;
+  if (vec) {
+    for (int64_t v = lane; v < m / 4; v += 64) {
+      const float4 o = reinterpret_cast<const float4 *>(orow)[v];
+      acc += static_cast<double>(o.x) * o.x;
+      acc += static_cast<double>(o.y) * o.y;
+      acc += static_cast<double>(o.z) * o.z;
+      acc += static_cast<double>(o.w) * o.w;
+    }
+  } else {
+    for (int64_t c = lane; c < m; c += 64) acc += static_cast<double>(orow[c]) * orow[c];
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
+  if (lane == 0) rowsq[static_cast<int64_t>(b) * k + row] = acc;
+}
+
+// Row factors of the update, one workgroup per matrix.  With NorMuon, for
+// every selected row i (index S_i):
+//   v_i <- beta2 v_i + (1 - beta2) mean_j O_ij^2      (stored, fp32 buffer)
+//   s_i = 1 / (sqrt(v_i) + eps)
+// and O_hat = diag(s) O is brought back to the Frobenius norm of O, so the
+// factor of row i is g s_i with g = ||O||_F / ||O_hat||_F (g = 0 when O_hat
+// is zero).  Without NorMuon every factor is 1.  fp64 throughout, with
+// fixed-order reductions.
+__global__ void __launch_bounds__(256)
+normuon_factors(const double *rowsq, float *v, const int64_t *S, int64_t n, int64_t k, int64_t m,
+                double beta2, double eps, int normuon, double *factor) {
+  const int b = blockIdx.x;
+  const double *rs = rowsq + static_cast<int64_t>(b) * k;
+  const int64_t *Sb = S + static_cast<int64_t>(b) * k;
+  double *f = factor + static_cast<int64_t>(b) * k;
+  if (!normuon) {
+    for (int64_t i = threadIdx.x; i < k; i += blockDim.x) f[i] = 1.0;
+    return;
+  }
+  float *vb = v + static_cast<int64_t>(b) * n;
+  double a = 0.0, h = 0.0;   // ||O||^2 and ||O_hat||^2, this thread's share
+  for (int64_t i = threadIdx.x; i < k; i += blockDim.x) {
+    const int64_t row = Sb[i];
+    const double sq = rs[i];
+    const double vi = beta2 * static_cast<double>(vb[row]) + (1.0 - beta2) * (sq / static_cast<double>(m));
+    vb[row] = static_cast<float>(vi);
+    const double s = 1.0 / (sqrt(vi) + eps);
+    f[i] = s;
+    a += sq;
+    h += sq * s * s;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_down(a, off, 64);
+    h += __shfl_down(h, off, 64);
+  }
+  __shared__ double wa[4], wh[4];
+  __shared__ double g_s;
+  if ((threadIdx.x & 63) == 0) {
+    wa[threadIdx.x >> 6] = a;
+    wh[threadIdx.x >> 6] = h;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double A = ((wa[0] + wa[1]) + wa[2]) + wa[3];
+    const double H = ((wh[0] + wh[1]) + wh[2]) + wh[3];
+    g_s = H > 0.0 ? sqrt(A / H) : 0.0;
+  }
+  __syncthreads();
+  const double g = g_s;
+  for (int64_t i = threadIdx.x; i < k; i += blockDim.x) f[i] *= g;
+}
+
+// Weight and momentum update, one workgroup per row of W:
+//   W <- (1 - lr wd) W                on every row (skipped when wd = 0),
+//   W[S_i] <- W[S_i] - lr f_i O_i     on the selected rows,
+//   M[S_i] <- mu M[S_i]               (error feedback, selected rows only).
+// The slot i of a row in the ascending index list S comes from a binary
+// search.  fp32 arithmetic on the caller's fp32 buffers.
+__global__ void __launch_bounds__(256)
+dion3_update(float *W, float *M, const float *O, const int64_t *S, const double *factor, int64_t n,
+             int64_t m, int64_t k, float decay, double lr, float mu, bool vec) {
+  const int b = blockIdx.y;
+  const int64_t row = blockIdx.x;
+  const int64_t *Sb = S + static_cast<int64_t>(b) * k;
+  int64_t lo = 0, hi = k;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (Sb[mid] < row) lo = mid + 1;
+    else hi = mid;
+  }
+  const int64_t slot = (lo < k && Sb[lo] == row) ? lo : -1;
+  if (slot < 0 && decay == 1.0f) return;
+  float *wr = W + (static_cast<int64_t>(b) * n + row) * m;
+  if (slot < 0) {
+    if (vec) {
+      for (int64_t v = threadIdx.x; v < m / 4; v += blockDim.x) {
+        float4 w = reinterpret_cast<const float4 *>(wr)[v];
+        w.x *= decay; w.y *= decay; w.z *= decay; w.w *= decay;
+        reinterpret_cast<float4 *>(wr)[v] = w;
+      }
+    } else {
+      for (int64_t c = threadIdx.x; c < m; c += blockDim.x) wr[c] *= decay;
+    }
+    return;
+  }
+  const float c = static_cast<float>(lr * factor[static_cast<int64_t>(b) * k + slot]);
+  const float *orow = O + (static_cast<int64_t>(b) * k + slot) * m;
+  float *mr = M + (static_cast<int64_t>(b) * n + row) * m;
+  if (vec) {
+    for (int64_t v = threadIdx.x; v < m / 4; v += blockDim.x) {
+      float4 w = reinterpret_cast<const float4 *>(wr)[v];
+      const float4 o = reinterpret_cast<const float4 *>(orow)[v];
+      float4 mm = reinterpret_cast<const float4 *>(mr)[v];
+      w.x = fmaf(-c, o.x, decay * w.x);
+      w.y = fmaf(-c, o.y, decay * w.y);
+      w.z = fmaf(-c, o.z, decay * w.z);
+      w.w = fmaf(-c, o.w, decay * w.w);
+      mm.x *= mu; mm.y *= mu; mm.z *= mu; mm.w *= mu;
+      reinterpret_cast<float4 *>(wr)[v] = w;
+      reinterpret_cast<float4 *>(mr)[v] = mm;
+    }
+  } else {
+    for (int64_t j = threadIdx.x; j < m; j += blockDim.x) {
+      wr[j] = fmaf(-c, orow[j], decay * wr[j]);
+      mr[j] *= mu;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <class E, int TILE, int PL = 1>
@@ -1256,6 +1447,48 @@ hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   check_rows<<<static_cast<unsigned>(batch), 256, 0, s>>>(row_idx, k, n, result);
+  return hipGetLastError();
+}
+
+hipError_t launch_momentum_l1(int grad_dtype, float *M, const void *G, int64_t batch, int64_t n,
+                              int64_t m, double *keys, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(batch));
+  const bool vec = (m % 4) == 0 && (reinterpret_cast<uintptr_t>(M) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(G) & (grad_dtype == DT_F32 ? 15 : 7)) == 0;
+  if (grad_dtype == DT_BF16) momentum_l1<EBF16><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys);
+  else if (grad_dtype == DT_F16) momentum_l1<EF16><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys);
+  else momentum_l1<EF32><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk(const double *keys, int64_t batch, int64_t n, int64_t k, int64_t *out,
+                              hipStream_t s) {
+  select_topk<<<static_cast<unsigned>(batch), 1024, 0, s>>>(keys, n, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_normuon(const float *O, int64_t batch, int64_t k, int64_t m, float *v,
+                          const int64_t *S, int64_t n, double beta2, double eps, int normuon,
+                          double *rowsq, double *factor, hipStream_t s) {
+  if (normuon) {
+    dim3 grid(static_cast<unsigned>((k + 3) / 4), static_cast<unsigned>(batch));
+    const bool vec = (m % 4) == 0 && (reinterpret_cast<uintptr_t>(O) & 15) == 0;
+    row_sumsq<<<grid, 256, 0, s>>>(O, k, m, vec, rowsq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  normuon_factors<<<static_cast<unsigned>(batch), 256, 0, s>>>(rowsq, v, S, n, k, m, beta2, eps, normuon,
+                                                               factor);
+  return hipGetLastError();
+}
+
+hipError_t launch_dion3_update(float *W, float *M, const float *O, const int64_t *S,
+                               const double *factor, int64_t batch, int64_t n, int64_t m, int64_t k,
+                               float decay, double lr, float mu, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(n), static_cast<unsigned>(batch));
+  const bool vec = (m % 4) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(M) & 15) == 0 && (reinterpret_cast<uintptr_t>(O) & 15) == 0;
+  dion3_update<<<grid, 256, 0, s>>>(W, M, O, S, factor, n, m, k, decay, lr, mu, vec);
   return hipGetLastError();
 }
 

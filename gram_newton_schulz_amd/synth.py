@@ -174,3 +174,26 @@ def as_f64(t: torch.Tensor) -> np.ndarray:
     """The exact values of a stored tensor as float64 (bf16/fp16/fp32 all
     embed exactly in float64)."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def dion3_state(count: int, n: int, m: int, *, seed: int, grad_dtype: torch.dtype = torch.bfloat16):
+    """Optimizer state for one Dion3 update of `count` n x m weights:
+    W ~ N(0, 0.02^2) fp32 weights, G ~ N(0, 1) gradient in grad_dtype,
+    M ~ N(0, 0.5^2) fp32 momentum and v ~ U[0.5, 1.5] / m fp32 row second
+    moments (the size of a mean square of an orthogonalised row).  Each
+    member b is drawn from default_rng([seed, b]) in float64 and rounded once.
+    Returns (W, G, M, v) on the CPU."""
+    W = torch.empty((count, n, m), dtype=torch.float32)
+    G = torch.empty((count, n, m), dtype=grad_dtype)
+    M = torch.empty((count, n, m), dtype=torch.float32)
+    v = torch.empty((count, n), dtype=torch.float32)
+
+    def one(b):
+        rng = _rng(seed, b)
+        W[b] = torch.from_numpy(0.02 * rng.standard_normal((n, m)))
+        G[b] = torch.from_numpy(rng.standard_normal((n, m))).to(grad_dtype)
+        M[b] = torch.from_numpy(0.5 * rng.standard_normal((n, m)))
+        v[b] = torch.from_numpy(rng.uniform(0.5, 1.5, size=n) / m)
+    with ThreadPoolExecutor(_workers(count)) as ex:
+        list(ex.map(one, range(count)))
+    return W, G, M, v

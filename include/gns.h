@@ -83,7 +83,9 @@ typedef enum {
   GNS_E_ALIAS = 7,     /* workspace overlaps X or out                         */
   GNS_E_WORKSPACE = 8, /* workspace NULL or smaller than gns_*_workspace_bytes */
   GNS_E_HIP = 9,       /* a HIP launch or runtime call failed                 */
-  GNS_E_FLAGS = 10     /* unknown option bit                                  */
+  GNS_E_FLAGS = 10,    /* unknown option bit                                  */
+  GNS_E_PARAM = 11     /* non-finite update hyperparameter, or eps <= 0 with
+                          NorMuon (gns_dion3_step)                            */
 } gns_status;
 
 #define GNS_MAX_ITERS 64
@@ -209,6 +211,58 @@ size_t gns_select_workspace_bytes(int64_t batch, int64_t n);
 gns_status gns_select_rows_l1(const void *M, int64_t batch, int64_t n, int64_t m, gns_dtype dtype,
                               int64_t k, int64_t *row_idx, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/*
+ * One Dion3 update of a batch of weight matrices ("Dion3: Full-Stack
+ * Orthogonal Updates", §6, Algorithm 4), with Gram Newton-Schulz as its
+ * orthogonalisation and, when `normuon` is set, the NorMuon steps of §2.1,
+ * eq. (2).  For every matrix b, in this order:
+ *   1. M <- M + G                              (fp32 additions, stored)
+ *   2. S = the k rows of M with the largest l1 norm, ascending (as
+ *      gns_select_rows_l1; written to row_idx[b][0..k))
+ *   3. O = Gram Newton-Schulz of the k x m matrix M[S,:], normalised by its
+ *      own Frobenius norm (as gns_gram_batched with that row subset; square
+ *      k = m falls back to standard NS unless GNS_OPT_NO_SQUARE_FALLBACK)
+ *   4. NorMuon (optional): v[S_i] <- beta2 v[S_i] + (1 - beta2) mean_j O_ij^2,
+ *      O_i <- O_i / (sqrt(v[S_i]) + eps), then O is rescaled to the Frobenius
+ *      norm it had before the division (left zero when that is zero)
+ *   5. W <- (1 - lr * weight_decay) W          (every row)
+ *   6. W[S_i] <- W[S_i] - lr O_i               (selected rows)
+ *   7. M[S_i] <- mu M[S_i]                     (error feedback, selected rows)
+ *
+ *   W          (device) [batch][n][m] fp32, updated in place.
+ *   G          (device) [batch][n][m] in grad_dtype (GNS_F32, GNS_BF16 or
+ *              GNS_F16), read only.
+ *   M          (device) [batch][n][m] fp32 momentum, updated in place.
+ *   v          (device) [batch][n] fp32 row second moments, updated at the
+ *              selected rows; may be NULL without NorMuon.
+ *   n, m, k    matrix shape and rows selected per matrix (1 <= k <= n; the
+ *              pages take k = ceil(f n) for a fraction f in (0, 1]).
+ *   compute_dtype, coeffs, T, restart_after, n_restart, opts
+ *              as for gns_gram_batched (opts: GNS_OPT_NAIVE_ALGEBRA,
+ *              GNS_OPT_NO_SQUARE_FALLBACK, GNS_OPT_ONE_STREAM, TILE bits).
+ *   lr, weight_decay, mu, beta2, eps
+ *              eta, wd, the error-feedback factor mu, and the NorMuon decay
+ *              and epsilon; all finite, eps > 0 with NorMuon.
+ *   row_idx    (device) [batch][k] int64, written (the selection S).
+ *   workspace  (device) >= gns_dion3_workspace_bytes(compute_dtype, batch, n,
+ *              m, k) bytes, 256-byte aligned, clobbered.
+ * W, G, M, v, row_idx and the workspace must not overlap (GNS_E_ALIAS).
+ * Needs batch <= 65535.  Row l1 norms are fp64 sums in a fixed order, so
+ * near-equal norms may order differently from an exactly rounded sum; equal
+ * norms take the smaller index first.  Everything is enqueued on `stream`
+ * (the orthogonalisation may fan out over the library's two streams, as in
+ * gns_gram_batched); nothing allocates and nothing synchronises, so the whole
+ * step can be captured in a HIP graph.
+ */
+size_t gns_dion3_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int64_t n, int64_t m,
+                                 int64_t k);
+gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t batch, int64_t n,
+                          int64_t m, gns_dtype grad_dtype, gns_dtype compute_dtype, int64_t k,
+                          const double *coeffs, int T, const int *restart_after, int n_restart,
+                          double lr, double weight_decay, double mu, double beta2, double eps,
+                          int normuon, int64_t *row_idx, unsigned opts, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * Enqueue a check of a row subset: writes to *result (device int32) 0 when

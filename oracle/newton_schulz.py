@@ -21,6 +21,7 @@ Every routine follows the written description in
                        norm.
 * ``dion3_rows``    -- §6, Algorithm 4: orthogonalise the selected rows M[S,:]
                        as one k x m matrix and write them back.
+* ``normuon_rows``  -- the NorMuon steps of Algorithm 4 (§2.1 eq. (2)).
 * ``dion3_step``    -- §6, Algorithm 4 in full (momentum sum, selection,
                        orthogonalisation, the optional NorMuon steps of §2.1
                        eq. (2), weight decay, update of the selected rows,
@@ -301,6 +302,22 @@ def dion3_rows(X, out_init, rows: Sequence[int], coeffs, restarts=(2,),
     return out
 
 
+def normuon_rows(O, v_rows, beta2=0.95, eps=1e-8):
+    """The optional NorMuon steps of Dion3 Algorithm 4 (from NorMuon, §2.1
+    eq. (2)) on the k x m update O, whose row i has second moment v_rows[i]:
+    v_i <- beta2 v_i + (1 - beta2) mean_j O_ij^2, O_ij <- O_ij / (sqrt(v_i)
+    + eps), then O is rescaled to the Frobenius norm it had before that
+    division.  Returns (O, v_rows), both new float64 arrays."""
+    O = np.asarray(O, dtype=np.float64)
+    second = beta2 * np.asarray(v_rows, dtype=np.float64) + (1.0 - beta2) * np.mean(O * O, axis=1)
+    On = O / (np.sqrt(second) + eps)[:, None]
+    # the rescale to ||O||_F is 0/0 when the selected rows orthogonalise to
+    # zero (a zero momentum sum); the update then stays zero
+    norm_on = np.linalg.norm(On)
+    O = On * (np.linalg.norm(O) / norm_on) if norm_on > 0 else On
+    return O, second
+
+
 def dion3_step(W, G, M, v, k: int, coeffs, restarts=(2,), lr=0.02, weight_decay=0.0,
                momentum=0.95, beta2=0.95, eps=1e-8, normuon=True, algebra="stabilized"):
     """One Dion3 update of one weight matrix (Dion3 §6, Algorithm 4), with
@@ -329,13 +346,7 @@ def dion3_step(W, G, M, v, k: int, coeffs, restarts=(2,), lr=0.02, weight_decay=
     O = gram_ns(Msum[S, :], coeffs, restarts, algebra)
     v_new = np.array(v, dtype=np.float64, copy=True) if v is not None else None
     if normuon:
-        second = beta2 * v_new[S] + (1.0 - beta2) * np.mean(O * O, axis=1)
-        v_new[S] = second
-        On = O / (np.sqrt(second) + eps)[:, None]
-        # the rescale to ||O||_F is 0/0 when the selected rows orthogonalise
-        # to zero (a zero momentum sum); the update then stays zero
-        norm_on = np.linalg.norm(On)
-        O = On * (np.linalg.norm(O) / norm_on) if norm_on > 0 else On
+        O, v_new[S] = normuon_rows(O, v_new[S], beta2, eps)
     W_new = (1.0 - lr * weight_decay) * W
     W_new[S, :] -= lr * O
     M_new = Msum.copy()

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(gns.LIB_PATH),
 
 FAKE = 0x10000000  # never dereferenced: every call below fails validation first
 E = {"OK": 0, "NULL": 1, "SHAPE": 2, "DTYPE": 3, "COEFF": 4, "RESTART": 5, "ROWIDX": 6,
-     "ALIAS": 7, "WORKSPACE": 8, "HIP": 9, "FLAGS": 10}
+     "ALIAS": 7, "WORKSPACE": 8, "HIP": 9, "FLAGS": 10, "PARAM": 11}
 
 
 def declared_functions():
@@ -38,8 +38,9 @@ def test_exports_every_declared_symbol():
 def test_version_and_strings():
     L = gns.lib()
     assert L.gns_abi_version() == 1
-    for code in range(0, 11):
+    for code in range(0, 12):
         assert L.gns_status_str(code)
+        assert L.gns_status_str(code) != b"unknown status"
 
 
 def test_workspace_sizes():
@@ -173,3 +174,55 @@ def test_safety_factor_helper():
         assert np.allclose(oracle.composed_poly([sc[t]], 1.05 * xs), oracle.composed_poly([co[t]], xs),
                            rtol=1e-13, atol=1e-15)
     assert gns.select_count(4096, 0.25) == 1024 and gns.select_count(10, 0.01) == 1
+
+
+def _dion3(W=FAKE, G=FAKE + (1 << 30), M=FAKE + (2 << 30), v=FAKE + (3 << 30), batch=2, n=64, m=96,
+           gdt=1, cdt=1, k=16, coeffs=None, T=None, restarts=(2,), lr=0.02, wd=0.0, mu=0.95,
+           beta2=0.95, eps=1e-8, normuon=1, rows=FAKE + (4 << 30), opts=0, ws=None, ws_bytes=None):
+    L = gns.lib()
+    if coeffs is None:
+        coeffs = [(3.4445, -4.7750, 2.0315)] * 5
+    flat = [float(x) for row in coeffs for x in row]
+    carr = (ctypes.c_double * max(len(flat), 1))(*flat)
+    T = len(coeffs) if T is None else T
+    rs = list(restarts)
+    rarr = (ctypes.c_int * max(len(rs), 1))(*rs) if rs else None
+    if ws is None:
+        ws = 0x7f0000000000
+    if ws_bytes is None:
+        ws_bytes = L.gns_dion3_workspace_bytes(cdt, batch, n, m, k)
+    return L.gns_dion3_step(W, G, M, v, batch, n, m, gdt, cdt, k, carr, T, rarr, len(rs), lr, wd, mu,
+                            beta2, eps, normuon, rows, opts, ws, ws_bytes, None)
+
+
+def test_dion3_workspace_size():
+    L = gns.lib()
+    b, n, m, k = 2, 64, 96, 16
+    need = L.gns_dion3_workspace_bytes(gns.GNS_BF16, b, n, m, k)
+    gram = L.gns_gram_workspace_bytes(gns.GNS_BF16, b, k, m)
+    # the orthogonalisation's workspace, then row keys, the fp32 update O and
+    # two fp64 values per selected row
+    assert need >= gram + 8 * b * n + 4 * b * k * m + 16 * b * k
+    assert L.gns_dion3_workspace_bytes(gns.GNS_BF16, 0, n, m, k) == 0
+    assert L.gns_dion3_workspace_bytes(gns.GNS_BF16, b, n, m, 0) == 0
+    assert L.gns_dion3_workspace_bytes(gns.GNS_BF16, b, n, m, n + 1) == 0
+    assert L.gns_dion3_workspace_bytes(9, b, n, m, k) == 0
+
+
+def test_dion3_argument_errors():
+    assert _dion3(gdt=gns.GNS_BF16X3) == E["DTYPE"]
+    assert _dion3(cdt=7) == E["DTYPE"]
+    assert _dion3(k=0) == E["SHAPE"] and _dion3(k=65) == E["SHAPE"] and _dion3(m=0) == E["SHAPE"]
+    assert _dion3(batch=70000) == E["SHAPE"]
+    assert _dion3(coeffs=[], T=0, restarts=()) == E["COEFF"]
+    assert _dion3(restarts=(5,)) == E["RESTART"]
+    assert _dion3(lr=float("nan")) == E["PARAM"]
+    assert _dion3(mu=float("inf")) == E["PARAM"]
+    assert _dion3(eps=0.0) == E["PARAM"]                   # NorMuon divides by sqrt(v) + eps
+    assert _dion3(opts=0x80) == E["FLAGS"]
+    assert _dion3(W=None) == E["NULL"] and _dion3(rows=None) == E["NULL"]
+    assert _dion3(v=None) == E["NULL"]                     # NorMuon needs v
+    assert _dion3(ws_bytes=64) == E["WORKSPACE"] and _dion3(ws=0x7f0000000008) == E["WORKSPACE"]
+    assert _dion3(M=FAKE + 4096) == E["ALIAS"]             # momentum overlaps the weights
+    assert _dion3(G=0x7f0000000000 + 256) == E["ALIAS"]    # gradient overlaps the workspace
+    assert _dion3(batch=0, W=None, G=None, M=None, v=None, rows=None, ws=None, ws_bytes=0) == E["OK"]

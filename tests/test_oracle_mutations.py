@@ -48,8 +48,8 @@ MUTATIONS = {
     "normuon zero rescale gives nan": ("O = On * (np.linalg.norm(O) / norm_on) if norm_on > 0 else On",
                                        "O = On * (np.linalg.norm(O) / norm_on) if norm_on >= 0 else On"),
     "normuon sum not mean": ("np.mean(O * O, axis=1)", "np.sum(O * O, axis=1)"),
-    "normuon beta swapped": ("second = beta2 * v_new[S] + (1.0 - beta2) * np.mean",
-                             "second = (1.0 - beta2) * v_new[S] + beta2 * np.mean"),
+    "normuon beta swapped": ("second = beta2 * np.asarray(v_rows, dtype=np.float64) + (1.0 - beta2) * np.mean",
+                             "second = (1.0 - beta2) * np.asarray(v_rows, dtype=np.float64) + beta2 * np.mean"),
     "decay on selected rows only": ("W_new = (1.0 - lr * weight_decay) * W\n",
                                     "W_new = W.copy()\n    W_new[S, :] *= 1.0 - lr * weight_decay\n"),
     "update sign": ("W_new[S, :] -= lr * O", "W_new[S, :] += lr * O"),
