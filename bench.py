@@ -169,6 +169,50 @@ def traffic_from_profile(kernel, workload):
     return None
 
 
+def bench_dion3_step(gns, synth, torch, w, coeffs, restarts, stream, steps=10):
+    """One whole Dion3 update (Algorithm 4: momentum sum, l1 selection of
+    k = n/4 rows, Gram NS of those rows, NorMuon, decay, row update, error
+    feedback) of the workload's batch shape with fp32 W and M and a bf16
+    gradient; per-kernel times from the library's launch events."""
+    log(f"timing the Dion3 update on {w.batch} x {w.n}x{w.m}, f = 1/4")
+    k = gns.select_count(w.n, 0.25)
+    W, G, M, v = (t.cuda() for t in synth.dion3_state(w.batch, w.n, w.m, seed=77))
+    ws = torch.empty(gns.dion3_workspace_bytes(torch.bfloat16, w.batch, w.n, w.m, k), dtype=torch.uint8,
+                     device="cuda")
+    S = torch.empty(w.batch, k, dtype=torch.int64, device="cuda")
+    kw = dict(lr=0.02, weight_decay=0.1, mu=0.95, beta2=0.95, eps=1e-8, normuon=True, row_idx=S,
+              workspace=ws, stream=stream)
+    for _ in range(2):
+        gns.dion3_step(W, G, M, v, k, coeffs, restarts, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        gns.dion3_step(W, G, M, v, k, coeffs, restarts, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gns.timing_reset()
+    gns.timing_enable(True)
+    for _ in range(steps):
+        gns.dion3_step(W, G, M, v, k, coeffs, restarts, split_batch=False, **kw)
+    torch.cuda.synchronize()
+    gns.timing_enable(False)
+    per = {}
+    for name, kernel, fl, by, kms in gns.timing_read():
+        if name in ("momentum_l1", "select_topk", "normuon", "dion3_update"):
+            d = per.setdefault(name, {"ms": 0.0, "bytes": 0.0})
+            d["ms"] += kms
+            d["bytes"] += by
+    kernels = {n: {"ms": round(d["ms"] / steps, 4),
+                   "gbs": round(d["bytes"] / (d["ms"] / 1e3) / 1e9, 1),
+                   "frac_hbm": round(d["bytes"] / (d["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 3)}
+               for n, d in per.items() if d["ms"] > 0}
+    del W, G, M, v, ws
+    return {"k": k, "ms_per_step": round(ms, 4), "updates_per_s": round(w.batch / (ms / 1e3), 2),
+            "hbm_kernels": kernels}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +226,8 @@ def main():
                     help="time every pass with the whole batch on one stream (no split over the "
                          "library's two streams); used for kernel-trace profiles")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dion3", action="store_true",
+                    help="skip the timing of the whole Dion3 update (f = 1/4) on the workload's shape")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size "
                          "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -350,6 +396,10 @@ def main():
         sel = {"k": kk, "ms": round(sel_ms, 4), "gbs": round(sel_bytes / (sel_ms / 1e3) / 1e9, 1),
                "frac_hbm": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 3)}
 
+    dion3 = None
+    if not args.one_stream and not args.no_dion3:
+        dion3 = bench_dion3_step(gns, synth, torch, w, coeffs, restarts, stream)
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -399,6 +449,7 @@ def main():
         "cpu_baseline": cpu,
         "standard_ns5": std,
         "dion3_select_l1": sel,
+        "dion3_step": dion3,
     }
     print(json.dumps(line), flush=True)
 

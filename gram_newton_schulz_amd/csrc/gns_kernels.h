@@ -37,6 +37,8 @@ struct GemmParams {
   int K;                            // contraction length, multiple of 128 bytes
   int tiles_m, tiles_n;             // output tiles per matrix along rows / cols
   int tiles_per_mat;                // sym: tiles_m*(tiles_m+1)/2
+  int sym_block, sym_half;          // sym: tile order (0 = column-major triangle;
+                                    // else blocks of sym_block, bands of sym_half rows)
   int batch;
   int xcd_chunk;                    // tiles per run dealt to one XCD (see gemm_nt);
                                     // must divide (grid & ~7) / 8
