@@ -591,20 +591,47 @@ gemm_nt(GemmParams p) {
   const int64_t col_base = static_cast<int64_t>(tj) * TILE + wc;
   const float alpha = p.alpha_vec ? p.alpha * p.alpha_vec[mat] : p.alpha;
 
-  // Transposed outputs (the mirrored half of a symmetric result, the
-  // transposed copy of a general one) take four consecutive rows per lane,
-  // i.e. 16-byte pieces of 32 different rows per store.  With 256-edge tiles
-  // and 16-bit types they are staged through LDS instead: each wave writes
-  // its accumulators transposed into a tile with 528-byte rows, and the whole
-  // workgroup then stores that tile as full 512-byte rows.
-  constexpr bool kStageT = (TILE == 256 && PL == 1 && ESZ == 2);
+  // Outputs of 256-edge tiles in 16-bit types go through LDS: the
+  // accumulator layout gives each lane scattered 2-byte elements (direct
+  // layout) or 8-byte pieces of 32 different rows (transposed layout), so
+  // the tile is first written into LDS (rows of 528 bytes, either layout) and
+  // the whole workgroup then stores it as full 512-byte rows, 16 bytes per
+  // lane.  Both layouts of every output are stored this way.
+  constexpr bool kStage = (TILE == 256 && PL == 1 && ESZ == 2);
   constexpr int TP = TILE + 8;                         // staged row pitch (elements)
-  static_assert(!kStageT || TILE * TP * 2 <= NST * STB, "staging tile fits the ring");
-  S *const Tt = reinterpret_cast<S *>(lds);
-  // Tt[c][r] = value of tile row r, tile column c
+  static_assert(!kStage || TILE * TP * 2 <= NST * STB, "staging tile fits the ring");
+  S *const Ts = reinterpret_cast<S *>(lds);
+  // The staged paths round every accumulator once into packed pairs:
+  // pk[ib][jb][2 g + h] holds rows 8 g + 4 lh + 2 h and + 1 (low half first)
+  // of column lr in block (ib, jb).  The fp32 accumulators then die, which
+  // keeps the epilogue within the register budget of two waves per SIMD.
+  // A diagonal symmetric tile also keeps, per row block ib, the unrounded
+  // diagonal entry this lane holds (dv[ib]; see fix_diag).
+  uint32_t pk[NBI][NBJ][8];
+  float dv[NBI];
+  auto pack = [&](bool keep_diag) {
+    const int dreg = 4 * (lr >> 3) + (lr & 3);
+#pragma unroll
+    for (int ib = 0; ib < NBI; ++ib) {
+      dv[ib] = 0.0f;
+#pragma unroll
+      for (int jb = 0; jb < NBJ; ++jb) {
+        if (keep_diag && wr + 32 * ib == wc + 32 * jb) {
+          float v = acc[ib][jb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) v = r == dreg ? acc[ib][jb][r] : v;
+          dv[ib] = alpha * v;
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          pk[ib][jb][h] = static_cast<uint32_t>(E::st(alpha * acc[ib][jb][2 * h])) |
+                          (static_cast<uint32_t>(E::st(alpha * acc[ib][jb][2 * h + 1])) << 16);
+      }
+    }
+  };
+  // Ts[c][r] = tile(r, c)
   auto stage_transposed = [&]() {
-    // every wave is past its last read of the ring and every DMA has landed
-    __syncthreads();
+    __syncthreads();   // the ring (or the previous staged tile) is no longer read
 #pragma unroll
     for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
@@ -613,33 +640,99 @@ gemm_nt(GemmParams p) {
         for (int g = 0; g < 4; ++g) {
           const int c = wc + jb * 32 + lr;
           const int r0 = wr + ib * 32 + 8 * g + 4 * lh;
-          uint32_t h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = E::st(alpha * acc[ib][jb][4 * g + q]);
-          uint2 pk;
-          pk.x = h[0] | (h[1] << 16);
-          pk.y = h[2] | (h[3] << 16);
-          *reinterpret_cast<uint2 *>(Tt + c * TP + r0) = pk;
+          uint2 v;
+          v.x = pk[ib][jb][2 * g];
+          v.y = pk[ib][jb][2 * g + 1];
+          *reinterpret_cast<uint2 *>(Ts + c * TP + r0) = v;
         }
     __syncthreads();
   };
-  // row c of the staged tile -> row (tj*TILE + c), columns ti*TILE .. of dst
-  auto store_transposed = [&](S *dst, int64_t ld) {
-    constexpr int CHUNKS = TILE * TILE / 8;            // 16-byte pieces
+  // Ts[r][c] = tile(r, c)
+  auto stage_direct = [&]() {
+    __syncthreads();
+    S *const base = Ts + (wr + 4 * lh) * TP + wc + lr;
+#pragma unroll
+    for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < NBJ; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            base[(ib * 32 + 8 * g + q) * TP + jb * 32] =
+                static_cast<S>(pk[ib][jb][2 * g + q / 2] >> (16 * (q & 1)));
+    __syncthreads();
+  };
+  // Diagonal tile: entry (r, r) of the staged direct tile becomes
+  // alpha * acc + diag, rounded once (rows r < n_real only).  In a 32 x 32
+  // block that lies on the diagonal, lane (lr, lh) holds entry (lr, lr) when
+  // bit 2 of lr equals lh (in register 4 (lr / 8) + lr % 4, kept as dv).
+  auto fix_diag = [&](float diag) {
+    __syncthreads();
+    if (((lr >> 2) & 1) == lh) {
+#pragma unroll
+      for (int ib = 0; ib < NBI; ++ib) {
+        const int rc = wr + 32 * ib + lr;
+        if (rc >= wc && rc < wc + WTN && static_cast<int64_t>(ti) * TILE + rc < p.n_real)
+          Ts[rc * TP + rc] = E::st(dv[ib] + diag);
+      }
+    }
+    __syncthreads();
+  };
+  // staged row k -> row (row0 + k) of dst, columns col0 .. col0 + TILE - 1;
+  // with `upper`, element (k, c) with k > c is taken from (c, k) instead
+  // (the stored form of a diagonal symmetric tile)
+  auto store_staged = [&](S *dst, int64_t ld, int64_t row0, int64_t col0, bool upper) {
+    constexpr int CPR = TILE / 8;                      // 16-byte pieces per row
 #pragma unroll 4
-    for (int k = tid; k < CHUNKS; k += NT) {
-      const int c = k / (TILE / 8);
-      const int r = (k % (TILE / 8)) * 8;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(Tt + c * TP + r);
-      *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(tj) * TILE + c) * ld +
-                                 static_cast<int64_t>(ti) * TILE + r) = v;
+    for (int k = tid; k < TILE * CPR; k += NT) {
+      const int rr = k / CPR;
+      const int cc = (k % CPR) * 8;
+      u32x4 v;
+      if (!upper || cc >= rr) {
+        v = *reinterpret_cast<const u32x4 *>(Ts + rr * TP + cc);
+      } else {
+        S e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int c = cc + q;
+          e[q] = c >= rr ? Ts[rr * TP + c] : Ts[c * TP + rr];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = static_cast<uint32_t>(e[2 * q]) | (static_cast<uint32_t>(e[2 * q + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4 *>(dst + (row0 + rr) * ld + col0 + cc) = v;
     }
   };
+  const int64_t tr0 = static_cast<int64_t>(ti) * TILE, tc0 = static_cast<int64_t>(tj) * TILE;
 
   if (MODE == MODE_SYM) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *C2m = p.C2 ? static_cast<S *>(p.C2) + static_cast<int64_t>(mat) * p.sC2 : nullptr;
     const bool diag_tile = (ti == tj);
+    if constexpr (kStage) {
+      pack(diag_tile);
+      if (!diag_tile) {
+        // C and its mirror; C2 equals C off the diagonal
+        stage_direct();
+        store_staged(Cm, p.ldc, tr0, tc0, false);
+        if (C2m) store_staged(C2m, p.ldc, tr0, tc0, false);
+        stage_transposed();
+        store_staged(Cm, p.ldc, tc0, tr0, false);
+        if (C2m) store_staged(C2m, p.ldc, tc0, tr0, false);
+      } else {
+        // diagonal tile: the upper-triangle value of every pair, written to
+        // both places, each entry exactly once
+        stage_direct();
+        if (p.diag1 != 0.0f) fix_diag(p.diag1);
+        store_staged(Cm, p.ldc, tr0, tc0, true);
+        if (C2m) {
+          if (p.diag2 != p.diag1) fix_diag(p.diag2);
+          store_staged(C2m, p.ldc, tr0, tc0, true);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
@@ -657,10 +750,8 @@ gemm_nt(GemmParams p) {
               St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
               if (C2m) St::put(C2m, (i0 + q) * p.ldc + j, p.pC2, v[q]);
             }
-            // mirrored copy: four consecutive entries of row j (staged
-            // through LDS below when kStageT)
-            if constexpr (kStageT) {
-            } else if constexpr (ESZ == 2) {
+            // mirrored copy: four consecutive entries of row j
+            if constexpr (ESZ == 2) {
               St::put4(Cm, j * p.ldc + i0, p.pC, v);
               if (C2m) St::put4(C2m, j * p.ldc + i0, p.pC2, v);
             } else {
@@ -687,16 +778,19 @@ gemm_nt(GemmParams p) {
             }
           }
         }
-    if constexpr (kStageT) {
-      if (!diag_tile) {
-        stage_transposed();
-        store_transposed(Cm, p.ldc);
-        if (C2m) store_transposed(C2m, p.ldc);
-      }
-    }
   } else if (MODE == MODE_GEN) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *CTm = p.CT ? static_cast<S *>(p.CT) + static_cast<int64_t>(mat) * p.sCT : nullptr;
+    if constexpr (kStage) {
+      pack(false);
+      stage_direct();
+      store_staged(Cm, p.ldc, tr0, tc0, false);
+      if (CTm) {
+        stage_transposed();
+        store_staged(CTm, p.ldct, tc0, tr0, false);
+      }
+      return;
+    }
 #pragma unroll
     for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
@@ -712,26 +806,29 @@ gemm_nt(GemmParams p) {
             St::put(Cm, (i0 + q) * p.ldc + j, p.pC, v[q]);
           }
           if (CTm) {
-            if constexpr (kStageT) {
-              // staged through LDS below
-            } else if constexpr (ESZ == 2) {
+            if constexpr (ESZ == 2) {
               St::put4(CTm, j * p.ldct + i0, p.pCT, v);
             } else {
               *reinterpret_cast<float4 *>(CTm + j * p.ldct + i0) = make_float4(v[0], v[1], v[2], v[3]);
             }
           }
         }
-    if constexpr (kStageT) {
-      if (CTm) {
-        stage_transposed();
-        store_transposed(CTm, p.ldct);
-      }
-    }
   } else {  // MODE_FINAL
     const int64_t *ridx = p.row_idx ? p.row_idx + static_cast<int64_t>(mat) * p.rows_eff : nullptr;
     const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
-    if (!ridx && p.out_dtype == E::code && row_base + WTM <= p.rows_eff &&
-        col_base + WTN <= p.out_cols) {
+    const bool plain = !ridx && p.out_dtype == E::code;
+    if constexpr (kStage) {
+      // the whole tile lies inside the caller's matrix, in the compute type,
+      // with 16-byte aligned rows: staged full-row stores
+      if (plain && tr0 + TILE <= p.rows_eff && tc0 + TILE <= p.out_cols && (p.out_cols & 7) == 0 &&
+          (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
+        pack(false);
+        stage_direct();
+        store_staged(static_cast<S *>(p.out) + obase, p.out_cols, tr0, tc0, false);
+        return;
+      }
+    }
+    if (plain && row_base + WTM <= p.rows_eff && col_base + WTN <= p.out_cols) {
       // the whole wave tile lies inside the caller's matrix and needs no
       // conversion: plain stores, consecutive lanes on consecutive columns
       S *O = static_cast<S *>(p.out) + obase;
