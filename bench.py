@@ -63,7 +63,8 @@ def short_kernel(name):
             dt = "bf16x3"
         return f"gemm_nt<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
     for k in ("norm_partial", "scale_transpose", "transpose_sumsq", "norm_finish", "row_l1",
-              "select_topk", "check_rows"):
+              "select_topk", "check_rows", "momentum_l1", "row_sumsq", "normuon_factors",
+              "dion3_update"):
         if k in name:
             return k
     return name.split("(")[0][:60]
@@ -131,8 +132,7 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
     for src, key, scale in ((fetch, "fetch", fs), (write, "write", ws)):
         for d in src.values():
             name = short_kernel(d["kernel"])
-            if not (name.startswith("gemm_nt") or name in ("norm_partial", "scale_transpose",
-                                                             "transpose_sumsq", "norm_finish")):
+            if not (name.startswith("gemm_nt") or name in HBM_KERNELS):
                 continue
             a = agg.setdefault(name, {"fetch": [], "write": []})
             a[key].append(d["v"] * 1024.0 * scale)
@@ -147,6 +147,10 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
                                         "fetch_bytes": f_avg, "write_bytes": w_avg,
                                         "workload": workload,
                                         "source_sha256_16": kernel_source_hash()}))
+
+
+HBM_KERNELS = ("norm_partial", "scale_transpose", "transpose_sumsq", "norm_finish", "momentum_l1",
+               "row_sumsq", "normuon_factors", "dion3_update", "select_topk")
 
 
 def traffic_from_profile(kernel, workload):
@@ -228,6 +232,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dion3", action="store_true",
                     help="skip the timing of the whole Dion3 update (f = 1/4) on the workload's shape")
+    ap.add_argument("--only-dion3", action="store_true",
+                    help="time only the whole Dion3 update on the workload's shape (for profiles)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size "
                          "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -240,7 +246,9 @@ def main():
         summarize_stats(args.summarize_stats)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, calib_mib=args.calib_copy_mib, workload=args.workload)
+        # records of the Dion3 update are tagged apart from the workload's own call
+        tag = f"dion3 update on workload {args.workload}'s shape" if args.only_dion3 else args.workload
+        summarize_pmc(*args.summarize_pmc, calib_mib=args.calib_copy_mib, workload=tag)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -267,6 +275,12 @@ def main():
     coeffs = synth.NS5_MUON
     T, restarts = 5, (2,)
     cdt = {"bf16": torch.bfloat16, "f16": torch.float16, "bf16x3": "bf16x3"}[args.compute]
+
+    if args.only_dion3:
+        print(json.dumps({"dion3_step": bench_dion3_step(gns, synth, torch, w, coeffs, restarts,
+                                                         torch.cuda.current_stream(), steps=args.steps)}),
+              flush=True)
+        return
 
     log(f"generating workload {args.workload}: {w.batch} x {w.n}x{w.m}")
     X = synth.workload_batch(args.workload)

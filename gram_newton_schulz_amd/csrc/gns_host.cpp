@@ -242,6 +242,19 @@ int xcd_chunk(int64_t tiles_per_mat, int64_t batch, int xpm) {
 constexpr int kSyrkBlock = 4, kSyrkBand = 2;
 constexpr int kSymmBlock = 0, kSymmBand = 1;
 
+// Launch layout of a symmetric product over nt x nt tiles.  (With 256-edge
+// 16-bit tiles a diagonal tile costs three quarters of a tile; running the
+// diagonal tiles last on every XCD, to fill the partial last round, measured
+// slower: 4.04 -> 4.79 ms for the two Gram matrices of an 8 x 4096x16384
+// call, as a diagonal tile shares no operand panel with the tiles around it.)
+void sym_layout(GemmParams *p, const Ctx &c, int nt, int xpm, int block, int band) {
+  p->tiles_m = p->tiles_n = nt;
+  p->tiles_per_mat = nt * (nt + 1) / 2;
+  p->sym_block = block;
+  p->sym_half = band;
+  p->xcd_chunk = xcd_chunk(p->tiles_per_mat, c.batch, xpm);
+}
+
 GemmParams base_params(const Ctx &c) {
   GemmParams p;
   std::memset(&p, 0, sizeof(p));
@@ -262,11 +275,7 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.A = A; p.lda = N; p.sA = c.sq_stride();
   p.B = B; p.ldb = N; p.sB = c.sq_stride();
   p.K = static_cast<int>(N);
-  p.tiles_m = p.tiles_n = nt;
-  p.tiles_per_mat = nt * (nt + 1) / 2;
-  p.sym_block = kSymmBlock;
-  p.sym_half = kSymmBand;
-  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
+  sym_layout(&p, c, nt, 4, kSymmBlock, kSymmBand);
   set_scale(&p, alpha, beta);
   if (D) { p.DT = D; p.lddt = N; p.sDT = c.sq_stride(); }   // D is symmetric
   if (D && D2) {
@@ -299,11 +308,7 @@ gns_status syrk(const Ctx &c, void *R, bool from_input = false) {
   p.A = Xh; p.lda = M; p.sA = c.rect_stride();
   p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
   p.K = static_cast<int>(M);
-  p.tiles_m = p.tiles_n = nt;
-  p.tiles_per_mat = nt * (nt + 1) / 2;
-  p.sym_block = kSyrkBlock;
-  p.sym_half = kSyrkBand;
-  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
+  sym_layout(&p, c, nt, 4, kSyrkBlock, kSyrkBand);
   p.C = R; p.ldc = N; p.sC = c.sq_stride();
   p.pA = p.pB = c.plane_rect();
   p.pC = c.plane_sq();

@@ -285,34 +285,44 @@ gemm_nt(GemmParams p) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int G8 = G & ~7;
-  int lw = w;
-  if (w < G8 && p.xcd_chunk > 0) {
-    const int c = p.xcd_chunk, slot = w >> 3;
-    lw = ((slot / c) * 8 + (w & 7)) * c + slot % c;
-    if (lw >= G8) lw = w;   // only when xcd_chunk does not divide G8 / 8 (a host error)
-  }
-  const int mat = lw / p.tiles_per_mat;
-  const int t = lw - mat * p.tiles_per_mat;
-  int ti, tj;
-  if (MODE == MODE_SYM) {
-    sym_tile(t, p.tiles_m, p.sym_block, p.sym_half, &ti, &tj);
-  } else {
-    // grouped raster: runs of 32 consecutive tiles form 4 x 8 blocks, so the
-    // tiles that one XCD runs together touch 4 A panels and 8 B panels
-    constexpr int GM = 4;
-    const int group = t / (GM * p.tiles_n);
-    const int first = group * GM;
-    const int gm = (p.tiles_m - first) < GM ? (p.tiles_m - first) : GM;
-    const int r = t - group * GM * p.tiles_n;
-    ti = first + r % gm;
-    tj = r / gm;
+  int mat, ti, tj;
+  {
+    int lw = w;
+    if (w < G8 && p.xcd_chunk > 0) {
+      const int c = p.xcd_chunk, slot = w >> 3;
+      lw = ((slot / c) * 8 + (w & 7)) * c + slot % c;
+      if (lw >= G8) lw = w;   // only when xcd_chunk does not divide G8 / 8 (a host error)
+    }
+    mat = lw / p.tiles_per_mat;
+    const int t = lw - mat * p.tiles_per_mat;
+    if (MODE == MODE_SYM) {
+      sym_tile(t, p.tiles_m, p.sym_block, p.sym_half, &ti, &tj);
+    } else {
+      // grouped raster: runs of 32 consecutive tiles form 4 x 8 blocks, so
+      // the tiles that one XCD runs together touch 4 A panels and 8 B panels
+      constexpr int GM = 4;
+      const int group = t / (GM * p.tiles_n);
+      const int first = group * GM;
+      const int gm = (p.tiles_m - first) < GM ? (p.tiles_m - first) : GM;
+      const int r = t - group * GM * p.tiles_n;
+      ti = first + r % gm;
+      tj = r / gm;
+    }
   }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // A diagonal tile of a symmetric result needs only its upper triangle.
+  // With 256-edge tiles and 8 waves, waves 0-3 keep their 64 x 128 tiles
+  // (rows 0-127, every column) and waves 4-7 take 64 x 64 tiles of the
+  // lower-right quadrant (rows 128-255, columns 128-255); the lower-left
+  // quadrant is never computed.  Wave w runs on SIMD w % 4, so every SIMD
+  // does 12 of its usual 16 blocks: the tile costs three quarters of a tile.
+  constexpr bool kHalfDiag = (MODE == MODE_SYM && TILE == 256 && NW == 8 && PL == 1);
+  const bool half = kHalfDiag && ti == tj && wave >= 4;
   const int wr = (wave / WGN) * WTM;
-  const int wc = (wave % WGN) * WTN;
+  const int wc = half ? 128 + (wave % 2) * 64 : (wave % WGN) * WTN;
 
   const int64_t ldaB = p.lda * ESZ;
   const int64_t ldbB = p.ldb * ESZ;
@@ -377,19 +387,22 @@ gemm_nt(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < NBI; ++i)
 #pragma unroll
-      for (int j = 0; j < NBJ; ++j)
+      for (int j = 0; j < NBJ; ++j) {
+        if (half && j >= 2) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const S *src = DTm + (j_base + j * 32) * p.lddt + i_base + i * 32 + 8 * g;
 #pragma unroll
           for (int pl = 0; pl < PL; ++pl) draw[pl][i][j][g] = *reinterpret_cast<const RawD *>(src + pl * p.pDT);
         }
+      }
   };
   auto init_from_d = [&]() {
 #pragma unroll
     for (int i = 0; i < NBI; ++i)
 #pragma unroll
-      for (int j = 0; j < NBJ; ++j)
+      for (int j = 0; j < NBJ; ++j) {
+        if (half && j >= 2) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -408,6 +421,7 @@ gemm_nt(GemmParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = p.init_scale * v[q];
         }
+      }
     if (p.DT2) {
       // second term (only the Q update that follows an identity Q has one):
       // loaded and added here
@@ -417,7 +431,8 @@ gemm_nt(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < NBI; ++i)
 #pragma unroll
-        for (int j = 0; j < NBJ; ++j)
+        for (int j = 0; j < NBJ; ++j) {
+          if (half && j >= 2) continue;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const S *src = D2m + (j_base + j * 32) * p.lddt + i_base + i * 32 + 8 * g;
@@ -437,6 +452,7 @@ gemm_nt(GemmParams p) {
               for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] += p.init_scale2 * v[q];
             }
           }
+        }
     }
   };
   if (has_d) load_d();
@@ -469,7 +485,10 @@ gemm_nt(GemmParams p) {
       }
     };
     Frag fa[2][PL][NBI], fb[2][PL][NBJ];
-    auto fload = [&](int slot, int buf, int sub) {
+    // NJ: column blocks this wave computes (NBJ, or 2 for a half wave of a
+    // diagonal tile)
+    auto fload = [&](int slot, int buf, int sub, auto nj) {
+      constexpr int NJ = decltype(nj)::value;
       const unsigned char *la = lds + buf * STB;
 #pragma unroll
       for (int pl = 0; pl < PL; ++pl) {
@@ -477,15 +496,16 @@ gemm_nt(GemmParams p) {
         for (int b = 0; b < NBI; ++b)
           fa[slot][pl][b] = Mma<E>::load(la + pl * OPB + (wr + b * 32 + lr) * SB, sub, lh, fsw);
 #pragma unroll
-        for (int b = 0; b < NBJ; ++b)
+        for (int b = 0; b < NJ; ++b)
           fb[slot][pl][b] = Mma<E>::load(la + (PL + pl) * OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
       }
     };
-    auto mma = [&](int slot) {
+    auto mma = [&](int slot, auto nj) {
+      constexpr int NJ = decltype(nj)::value;
 #pragma unroll
       for (int ii = 0; ii < NBI; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < NBJ; ++jj) {
+        for (int jj = 0; jj < NJ; ++jj) {
           if constexpr (PL == 2) {
             // small terms first
             acc[ii][jj] = Mma<E>::run(fa[slot][1][ii], fb[slot][0][jj], acc[ii][jj]);
@@ -517,17 +537,27 @@ gemm_nt(GemmParams p) {
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
       __syncthreads();
       if (g1) __syncthreads();
-      int buf = 0;                          // buffer of stage i
-      for (int i = 0; i < nk; ++i) {
-        static_for<0, SUB>([&](auto sc) { fload(decltype(sc)::value, buf, decltype(sc)::value); });
-        dma_stage(i + NST - 1);             // into the buffer of stage i-1
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
-        __syncthreads();
-        __builtin_amdgcn_s_setprio(1);
-        static_for<0, SUB>([&](auto sc) { mma(decltype(sc)::value); });
-        __builtin_amdgcn_s_setprio(0);
-        __syncthreads();
-        buf = buf == NST - 1 ? 0 : buf + 1;
+      // the same barrier sequence in both versions of the loop: the half
+      // waves of a diagonal tile run the one that skips column blocks 2, 3
+      auto loop = [&](auto nj) {
+        int buf = 0;                        // buffer of stage i
+        for (int i = 0; i < nk; ++i) {
+          static_for<0, SUB>([&](auto sc) { fload(decltype(sc)::value, buf, decltype(sc)::value, nj); });
+          dma_stage(i + NST - 1);           // into the buffer of stage i-1
+          asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
+          __syncthreads();
+          __builtin_amdgcn_s_setprio(1);
+          static_for<0, SUB>([&](auto sc) { mma(decltype(sc)::value, nj); });
+          __builtin_amdgcn_s_setprio(0);
+          __syncthreads();
+          buf = buf == NST - 1 ? 0 : buf + 1;
+        }
+      };
+      if constexpr (kHalfDiag) {
+        if (half) loop(std::integral_constant<int, 2>{});
+        else loop(std::integral_constant<int, NBJ>{});
+      } else {
+        loop(std::integral_constant<int, NBJ>{});
       }
       if (!g1) __syncthreads();
     } else {
@@ -545,7 +575,7 @@ gemm_nt(GemmParams p) {
       static_assert(LPS * (NST - 2) < 64, "wait count out of range");
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 2)) : "memory");
       __syncthreads();
-      fload(0, 0, 0);
+      fload(0, 0, 0, std::integral_constant<int, NBJ>{});
 
       int buf = 0;                            // buffer of stage i
       for (int i = 0; i < nk; ++i) {
@@ -554,12 +584,12 @@ gemm_nt(GemmParams p) {
           constexpr int s = decltype(sc)::value;
           constexpr int cur = s & 1;
           if constexpr (s + 1 < SUB) {
-            fload(cur ^ 1, buf, s + 1);
+            fload(cur ^ 1, buf, s + 1, std::integral_constant<int, NBJ>{});
           } else {
-            fload(cur ^ 1, bnext, 0);
+            fload(cur ^ 1, bnext, 0, std::integral_constant<int, NBJ>{});
           }
           __builtin_amdgcn_sched_barrier(0);
-          mma(cur);
+          mma(cur, std::integral_constant<int, NBJ>{});
           __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr ((SUB & 1) == 1) {
@@ -616,6 +646,7 @@ gemm_nt(GemmParams p) {
       dv[ib] = 0.0f;
 #pragma unroll
       for (int jb = 0; jb < NBJ; ++jb) {
+        if (half && jb >= 2) continue;
         if (keep_diag && wr + 32 * ib == wc + 32 * jb) {
           float v = acc[ib][jb][0];
 #pragma unroll
@@ -654,13 +685,15 @@ gemm_nt(GemmParams p) {
 #pragma unroll
     for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < NBJ; ++jb)
+      for (int jb = 0; jb < NBJ; ++jb) {
+        if (half && jb >= 2) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             base[(ib * 32 + 8 * g + q) * TP + jb * 32] =
                 static_cast<S>(pk[ib][jb][2 * g + q / 2] >> (16 * (q & 1)));
+      }
     __syncthreads();
   };
   // Diagonal tile: entry (r, r) of the staged direct tile becomes
@@ -673,7 +706,7 @@ gemm_nt(GemmParams p) {
 #pragma unroll
       for (int ib = 0; ib < NBI; ++ib) {
         const int rc = wr + 32 * ib + lr;
-        if (rc >= wc && rc < wc + WTN && static_cast<int64_t>(ti) * TILE + rc < p.n_real)
+        if (rc >= wc && rc < wc + (half ? 64 : WTN) && static_cast<int64_t>(ti) * TILE + rc < p.n_real)
           Ts[rc * TP + rc] = E::st(dv[ib] + diag);
       }
     }
@@ -701,7 +734,9 @@ gemm_nt(GemmParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = static_cast<uint32_t>(e[2 * q]) | (static_cast<uint32_t>(e[2 * q + 1]) << 16);
       }
-      *reinterpret_cast<u32x4 *>(dst + (row0 + rr) * ld + col0 + cc) = v;
+      // streaming (non-temporal) store: the output is not read again by this
+      // launch, so it should not displace operand panels from the L2
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + (row0 + rr) * ld + col0 + cc));
     }
   };
   const int64_t tr0 = static_cast<int64_t>(ti) * TILE, tc0 = static_cast<int64_t>(tj) * TILE;
