@@ -45,7 +45,7 @@ struct Plan {
   int esz = 2;
   int planes = 1;                      // 2: split hi/lo storage (GNS_BF16X3)
   size_t off_partials = 0, off_inv = 0, off_xh = 0, off_xt0 = 0, off_xt1 = 0;
-  int64_t tile_parts = 0;              // 64x64 tiles per matrix (direct input path)
+  int64_t tile_parts = 0;              // 128x128 tiles per matrix (direct input path)
   size_t off_sq[5] = {0, 0, 0, 0, 0};  // R, Z, RZ, Q0, Q1 (standard NS: A, B)
   size_t bytes = 0;
 };
@@ -92,9 +92,9 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
   pl->planes = gns::dtype_planes(cdt);
   size_t off = 0;
   pl->off_partials = off;
-  // norm partials: per row block (normalised-copy path) or per 64x64 tile
+  // norm partials: per row block (normalised-copy path) or per 128x128 tile
   // (direct path), whichever needs more
-  pl->tile_parts = (pl->Np / 64) * (pl->Mp / 64);
+  pl->tile_parts = (pl->Np / 128) * (pl->Mp / 128);
   off = align_up(off + sizeof(double) * batch * std::max<int64_t>(pl->parts, pl->tile_parts), kAlign);
   pl->off_inv = off;                   // 1/(||X||+eps) and its square, per matrix
   off = align_up(off + 2 * sizeof(float) * batch, kAlign);

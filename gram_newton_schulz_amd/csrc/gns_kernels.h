@@ -86,8 +86,8 @@ hipError_t launch_scale_transpose(int io_dtype, int compute_dtype, const void *X
 hipError_t launch_select_rows_l1(int io_dtype, const void *M, int64_t batch, int64_t n, int64_t m,
                                  int64_t k, double *keys, int64_t *out, hipStream_t s);
 
-// Unscaled transpose of 16-bit X (n, m multiples of 64, 16-byte aligned) into
-// XT [m][n] per matrix, and the sum of squares of every 64x64 tile into
+// Unscaled transpose of 16-bit X (n, m multiples of 128, 16-byte aligned) into
+// XT [m][n] per matrix, and the sum of squares of every 128x128 tile into
 // partials[b][tile] (fp64).
 hipError_t launch_transpose_sumsq(int dtype, const void *X, int64_t batch, int64_t n, int64_t m,
                                   void *XT, double *partials, hipStream_t s);

@@ -1119,33 +1119,41 @@ check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
 // whole tiles): the products read X itself and take 1/(||X||_F + eps) as a
 // per-matrix factor in their epilogues, so only X^T is materialised.
 // ---------------------------------------------------------------------------
-// One 64x64 tile per workgroup: X^T tile through a padded LDS tile (16-byte
-// loads and stores), and the tile's sum of squares (fp32 per thread over 16
-// elements, then a fixed-order fp64 combination).
+// One 128x128 tile per workgroup: X^T tile through a padded LDS tile (16-byte
+// loads and stores, all eight loads of a thread in flight together), and the
+// tile's sum of squares (fp32 per thread over 64 elements, then a fixed-order
+// fp64 combination).
 template <class T>
 __global__ void __launch_bounds__(256)
-transpose_sumsq(const void *X, int64_t n, int64_t m, void *XT, double *partials) {
+transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restrict__ XT,
+                double *partials) {
+  constexpr int TT = 128;                 // tile edge
+  constexpr int PR = TT / 8;              // 16-byte pieces per tile row
+  constexpr int NP = TT * PR / 256;       // pieces per thread
   const int b = blockIdx.z;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * TT;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * TT;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
   __shared__ double wsum[4];
   const uint16_t *Xb = static_cast<const uint16_t *>(X) + static_cast<int64_t>(b) * n * m;
   uint16_t *XTb = static_cast<uint16_t *>(XT) + static_cast<int64_t>(b) * m * n;
+  u32x4 in[NP];
+#pragma unroll
+  for (int h = 0; h < NP; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    in[h] = *reinterpret_cast<const u32x4 *>(Xb + (r0 + v / PR) * m + c0 + (v % PR) * 8);
+  }
   float sq = 0.0f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NP; ++h) {
     const int v = threadIdx.x + 256 * h;
-    const int row = v >> 3;
-    const int cv = (v & 7) * 8;
-    const u32x4 in = *reinterpret_cast<const u32x4 *>(Xb + (r0 + row) * m + c0 + cv);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float f0 = T::ld(static_cast<uint16_t>(in[q] & 0xffffu));
-      const float f1 = T::ld(static_cast<uint16_t>(in[q] >> 16));
+      const float f0 = T::ld(static_cast<uint16_t>(in[h][q] & 0xffffu));
+      const float f1 = T::ld(static_cast<uint16_t>(in[h][q] >> 16));
       sq += f0 * f0 + f1 * f1;
     }
-    *reinterpret_cast<u32x4 *>(&tile[row][cv]) = in;
+    *reinterpret_cast<u32x4 *>(&tile[v / PR][(v % PR) * 8]) = in[h];
   }
   double d = static_cast<double>(sq);
   for (int off = 32; off > 0; off >>= 1) d += __shfl_down(d, off, 64);
@@ -1155,10 +1163,12 @@ transpose_sumsq(const void *X, int64_t n, int64_t m, void *XT, double *partials)
     const int64_t tile_id = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
     partials[static_cast<int64_t>(b) * gridDim.x * gridDim.y + tile_id] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   }
+  // X^T row c0 + c takes the 8-row run 8 k .. 8 k + 7 of tile column c
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = threadIdx.x & 63;
-    const int k = (threadIdx.x >> 6) + 4 * h;
+  for (int h = 0; h < NP; ++h) {
+    const int v = threadIdx.x + 256 * h;
+    const int c = v % TT;
+    const int k = v / TT;
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -1586,7 +1596,7 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
 
 hipError_t launch_transpose_sumsq(int dt, const void *X, int64_t batch, int64_t n, int64_t m,
                                   void *XT, double *partials, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(m / 64), static_cast<unsigned>(n / 64), static_cast<unsigned>(batch));
+  dim3 grid(static_cast<unsigned>(m / 128), static_cast<unsigned>(n / 128), static_cast<unsigned>(batch));
   if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, partials);
   else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, partials);
   return hipGetLastError();
