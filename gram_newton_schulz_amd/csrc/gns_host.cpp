@@ -434,6 +434,25 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+gns_status check_coeffs(const double *coeffs, int T) {
+  if (!coeffs) return GNS_E_NULL;
+  if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
+  for (int i = 0; i < 3 * T; ++i)
+    if (!std::isfinite(coeffs[i])) return GNS_E_COEFF;
+  return GNS_OK;
+}
+
+gns_status parse_restarts(const int *restart_after, int n_restart, int T, std::vector<char> *at) {
+  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
+  at->assign(T + 2, 0);
+  for (int i = 0; i < n_restart; ++i) {
+    const int r = restart_after[i];
+    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
+    (*at)[r] = 1;
+  }
+  return GNS_OK;
+}
+
 gns_status common_checks(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
                          gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
                          const int64_t *row_idx, int64_t k, int64_t *rows) {
@@ -445,10 +464,8 @@ gns_status common_checks(const void *X, void *out, int64_t batch, int64_t n, int
   } else {
     *rows = n;
   }
-  if (!coeffs) return GNS_E_NULL;
-  if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
-  for (int i = 0; i < 3 * T; ++i)
-    if (!std::isfinite(coeffs[i])) return GNS_E_COEFF;
+  const gns_status cs = check_coeffs(coeffs, T);
+  if (cs != GNS_OK) return cs;
   if (batch > 0 && (!X || !out)) return GNS_E_NULL;
   if (batch > (int64_t(1) << 24)) return GNS_E_SHAPE;
   return GNS_OK;
@@ -708,25 +725,6 @@ bool dion3_layout(int cdt, int64_t batch, int64_t n, int64_t m, int64_t k, Dion3
   return true;
 }
 
-gns_status check_coeffs(const double *coeffs, int T) {
-  if (!coeffs) return GNS_E_NULL;
-  if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
-  for (int i = 0; i < 3 * T; ++i)
-    if (!std::isfinite(coeffs[i])) return GNS_E_COEFF;
-  return GNS_OK;
-}
-
-gns_status parse_restarts(const int *restart_after, int n_restart, int T, std::vector<char> *at) {
-  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
-  at->assign(T + 2, 0);
-  for (int i = 0; i < n_restart; ++i) {
-    const int r = restart_after[i];
-    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
-    (*at)[r] = 1;
-  }
-  return GNS_OK;
-}
-
 }  // namespace
 
 // ==========================================================================
@@ -778,13 +776,8 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
     return st;
   const bool split = !(opts & GNS_OPT_ONE_STREAM);
-  if (n_restart < 0 || (n_restart > 0 && !restart_after)) return GNS_E_RESTART;
-  std::vector<char> restart_at(T + 2, 0);
-  for (int i = 0; i < n_restart; ++i) {
-    const int r = restart_after[i];
-    if (r < 1 || r > T - 1 || (i > 0 && r <= restart_after[i - 1])) return GNS_E_RESTART;
-    restart_at[r] = 1;
-  }
+  std::vector<char> restart_at;
+  if ((st = parse_restarts(restart_after, n_restart, T, &restart_at)) != GNS_OK) return st;
   if (batch == 0) return GNS_OK;
   Plan pl;
   if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;

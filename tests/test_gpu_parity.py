@@ -79,6 +79,23 @@ def test_restart_sets_fp32(restarts):
     assert max(per_matrix_rel(synth.as_f64(out), ref)) <= TOL_F32
 
 
+@pytest.mark.parametrize("cdt", ["bf16", "f16"])
+@pytest.mark.parametrize("restarts", [(1,), (2,), (3,), (4,), (1, 3)])
+def test_restart_location_sweep_half(cdt, restarts):
+    """Where the restart goes (the pages sweep it in half precision): every
+    location of a single restart, and two restarts, on 256-edge tiles, against
+    the oracle with the same restart set."""
+    gns = need_gpu()
+    X, X64 = _inputs(2, 512, 1536, "bf16", seed=29)
+    say(f"restart sweep {cdt} {restarts}")
+    out = gns.gram_ns_batched(X.cuda(), NS5, restarts=restarts, compute_dtype=DT[cdt], tile=256)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle_gram(X64[b], restarts=restarts) for b in range(2)])
+    errs = per_matrix_rel(synth.as_f64(out), ref)
+    say("  rel errs", errs)
+    assert max(errs) <= TOL_HALF
+
+
 @pytest.mark.parametrize("cdt,tile", [("f32", None), ("bf16", None), ("bf16", 256), ("f16", 256)])
 def test_naive_algebra(cdt, tile):
     """Algorithm 2's algebra puts a_t on the diagonal of Z and, after an
