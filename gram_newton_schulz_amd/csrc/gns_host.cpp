@@ -177,6 +177,9 @@ struct Ctx {
   // that read it apply 1/(||X||_F + eps) per matrix in their epilogues.
   bool direct = false;
   const void *xin = nullptr;           // this sub-batch's X
+  // The rectangular products of Gram NS read X row-major (K-major B operand,
+  // LDS transpose reads), so no transposed copy of X is written.
+  bool nn = false;
   // Fan-out stagger: recorded on `s` once the input is normalised; the next
   // part's stream waits for it (see run_batches).  Null when unused.
   hipEvent_t stagger = nullptr;
@@ -298,12 +301,14 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
 
 // R = X X^T from the row-layout buffer, or (from_input on the direct path)
 // from the caller's X with 1/(||X||+eps)^2 applied in the epilogue.
-gns_status syrk(const Ctx &c, void *R, bool from_input = false) {
+// xrow: the row-layout X to use instead of the normalised copy (the restarted
+// X of a K-major-B call lives in one of two row buffers).
+gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow = nullptr) {
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int nt = static_cast<int>(N / c.pl->tile);
   const bool direct = from_input && c.direct;
-  const void *Xh = direct ? c.xin : c.xh();
+  const void *Xh = direct ? c.xin : (xrow ? xrow : c.xh());
   if (direct) p.alpha_vec = c.inv2();
   p.A = Xh; p.lda = M; p.sA = c.rect_stride();
   p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
@@ -373,6 +378,45 @@ gns_status apply(const Ctx &c, const void *S, const void *XT_in, void *XT_out, f
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
 
+// Y = S X (+ beta * X) with S an n x n iterate and X row-major [rows][m]
+// (pitch ld_in): the K-major-B form of the product, whose kernel reads X
+// through LDS transpose loads.  Writes the row layout Y into Xrow_out, or
+// (final) the caller's output.
+gns_status apply_nn(const Ctx &c, const void *S, const void *Xrow_in, int64_t ld_in, void *Xrow_out,
+                    float beta, bool final, void *out, int io_dtype, int64_t n_total,
+                    const int64_t *row_idx, const char *what, const float *alpha_vec = nullptr) {
+  GemmParams p = base_params(c);
+  p.alpha_vec = alpha_vec;           // 1/(||X||+eps) when X is the unscaled input
+  const int64_t N = c.pl->Np, M = c.pl->Mp;
+  const int tm = static_cast<int>(N / c.pl->tile), tn = static_cast<int>(M / c.pl->tile);
+  p.A = S; p.lda = N; p.sA = c.sq_stride();
+  p.B = Xrow_in; p.ldb = ld_in; p.sB = c.rect_stride();
+  p.b_kmajor = 1;
+  p.K = static_cast<int>(N);
+  p.tiles_m = tm; p.tiles_n = tn;
+  p.tiles_per_mat = tm * tn;
+  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch, 4);
+  set_scale(&p, 1.0f, beta);
+  if (beta != 0.0f) { p.DT = Xrow_in; p.lddt = ld_in; p.sDT = c.rect_stride(); p.d_rows = 1; }
+  const double n = static_cast<double>(c.pl->r), m = static_cast<double>(c.pl->c);
+  double bytes = c.batch * (n * n + n * m) * c.pl->esz;
+  if (final) {
+    p.out = out; p.out_dtype = io_dtype; p.out_rows = n_total; p.out_cols = c.pl->m;
+    p.rows_eff = c.pl->rows; p.row_idx = row_idx;
+    bytes += c.batch * n * m * gns::dtype_size(io_dtype);
+  } else {
+    p.C = Xrow_out; p.ldc = M; p.sC = c.rect_stride();
+    bytes += c.batch * n * m * c.pl->esz;
+  }
+  if (beta != 0.0f) bytes += c.batch * n * m * c.pl->esz;
+  const int mode = final ? gns::MODE_FINAL : gns::MODE_GEN;
+  LaunchScope ls(c.s, what, gns::gemm_kernel_name(c.cdt, c.pl->tile, mode, true), 2.0 * n * n * m * c.batch,
+                 bytes);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, mode, p, c.s);
+  ls.done();
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
 // Norm + scale + cast + transpose of the (row-selected) input.  On the
 // direct path: the unscaled transpose X^T and the per-matrix scale factors.
 gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const int64_t *row_idx) {
@@ -382,8 +426,8 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
     {
       LaunchScope ls(c.s, "transpose_sumsq", "transpose_sumsq", 2.0 * rows * m * c.batch,
                      c.batch * rows * m * 2.0 * gns::dtype_size(io));
-      hipError_t e = gns::launch_transpose_sumsq(io, X, c.batch, c.pl->rows, c.pl->m, c.xt(0),
-                                                 c.tile_partials(), c.s);
+      hipError_t e = gns::launch_transpose_sumsq(io, X, c.batch, c.pl->rows, c.pl->m,
+                                                 c.nn ? nullptr : c.xt(0), c.tile_partials(), c.s);
       ls.done();
       if (e != hipSuccess) return GNS_E_HIP;
     }
@@ -408,7 +452,7 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
     // X_hat row-major [rows][m] and its transpose; for a tall problem X_hat is
     // Y^T (the xt buffer) and its transpose is Y (the xh buffer)
     void *dst_rows = c.pl->tall ? c.xt(0) : c.xh();
-    void *dst_cols = c.pl->tall ? c.xh() : c.xt(0);
+    void *dst_cols = c.nn ? nullptr : (c.pl->tall ? c.xh() : c.xt(0));
     const int64_t rows_pad = c.pl->tall ? c.pl->Mp : c.pl->Np;
     const int64_t cols_pad = c.pl->tall ? c.pl->Np : c.pl->Mp;
     hipError_t e = gns::launch_scale_transpose(io, c.cdt, X, c.batch, n_total, c.pl->m, c.pl->rows,
@@ -537,6 +581,13 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
   if ((st = normalize(c, X, io, n, row_idx)) != GNS_OK) return st;
   if ((st = c.mark_stagger()) != GNS_OK) return st;
   if ((st = syrk(c, R, true)) != GNS_OK) return st;                  // R_0 = X X^T
+  // K-major form: X in row layout, the caller's X on the direct path, else
+  // the normalised copy; restarts alternate between two row buffers (the
+  // transposed-copy buffers, unused in this form, hold the second one)
+  void *rows[2] = {c.xh(), c.xt(0)};
+  const void *xrow = c.direct ? c.xin : c.xh();
+  int64_t xrow_ld = c.direct ? c.pl->m : c.pl->Mp;
+  int rcur = c.direct ? 0 : 1;
   // the unscaled input transpose carries the normalisation as a factor
   const float *x_scale = c.direct ? c.inv() : nullptr;
   for (int t = 1; t <= T; ++t) {
@@ -544,15 +595,24 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     const float b = static_cast<float>(coeffs[3 * (t - 1) + 1]);
     const float cc = static_cast<float>(coeffs[3 * (t - 1) + 2]);
     if (t > 1 && restart_at[t - 1]) {
-      // restart: X <- Q X (row layout in place, transposed copy swapped),
-      // R <- X X^T, Q <- I
-      st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], q_shift, false, nullptr, io, n, nullptr, "restart_apply",
-                 x_scale);
+      // restart: X <- Q X, R <- X X^T, Q <- I.  Transposed form: the row
+      // layout is written in place and the transposed copy swapped; K-major
+      // form: the row layout goes to the other row buffer.
+      if (c.nn) {
+        st = apply_nn(c, Qb[qcur], xrow, xrow_ld, rows[rcur], q_shift, false, nullptr, io, n, nullptr,
+                      "restart_apply", x_scale);
+        xrow = rows[rcur];
+        xrow_ld = c.pl->Mp;
+        rcur ^= 1;
+      } else {
+        st = apply(c, Qb[qcur], XT[xcur], XT[xcur ^ 1], q_shift, false, nullptr, io, n, nullptr, "restart_apply",
+                   x_scale);
+        xcur ^= 1;
+      }
       x_scale = nullptr;
       q_shift = 0.0f;
       if (st != GNS_OK) return st;
-      xcur ^= 1;
-      if ((st = syrk(c, R)) != GNS_OK) return st;
+      if ((st = syrk(c, R, false, c.nn ? xrow : nullptr)) != GNS_OK) return st;
       q_is_identity = true;
     }
     const bool need_r = (t < T) && !restart_at[t];
@@ -605,8 +665,21 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
     }
   }
   // out = Q_T X
+  if (c.nn)
+    return apply_nn(c, Qb[qcur], xrow, xrow_ld, nullptr, q_shift, true, out, io, out_rows, out_idx, "final_apply",
+                    x_scale);
   return apply(c, Qb[qcur], XT[xcur], nullptr, q_shift, true, out, io, out_rows, out_idx, "final_apply",
                x_scale);
+}
+
+// Gram NS runs its rectangular products with X row-major (K-major B) for
+// unsplit 16-bit compute types on 256-edge tiles when the problem is wide and
+// a whole X fits the 32-bit range of a buffer descriptor.  Against the
+// transposed copies this drops two HBM writes of X per call (the input
+// transpose and the restart's second layout).
+bool kmajor_products(const Plan &pl, int cdt) {
+  return (cdt == GNS_BF16 || cdt == GNS_F16) && pl.planes == 1 && pl.tile == 256 && !pl.tall &&
+         pl.Np * pl.Mp * pl.esz < (int64_t(1) << 31);
 }
 
 // The direct input path applies when X can stand in for its normalised copy:
@@ -800,10 +873,12 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
                               ri, ri, n);
     });
   const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
+  const bool nn = kmajor_products(pl, cdt);
   return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c0) {
     const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
     Ctx c = c0;
     c.direct = direct;
+    c.nn = nn;
     c.xin = Xs;
     const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
     return enqueue_gram(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
@@ -947,7 +1022,9 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
     float *Os = O + c.b0 * o_mat;
     const int64_t *ri = row_idx + c.b0 * k;
     if (square) return enqueue_standard(c, Xs, Os, GNS_F32, n, coeffs, T, ri, nullptr, k);
-    return enqueue_gram(c, Xs, Os, GNS_F32, n, coeffs, T, restart_at, ri, nullptr, k, naive);
+    Ctx cg = c;
+    cg.nn = kmajor_products(pl, cdt);
+    return enqueue_gram(cg, Xs, Os, GNS_F32, n, coeffs, T, restart_at, ri, nullptr, k, naive);
   });
   if (st != GNS_OK) return st;
   // NorMuon row factors (second moment v at the selected rows), then the

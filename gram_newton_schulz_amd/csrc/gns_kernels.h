@@ -47,6 +47,10 @@ struct GemmParams {
   float init_scale;                 // acc starts at init_scale * D
   const void *DT; int64_t lddt, sDT;  // D read transposed: D(i,j) = DT[j*lddt + i];
                                       // may be null (D = 0)
+  int d_rows;                       // D read in row layout instead: D(i,j) = DT[i*lddt + j]
+                                    // (16-bit unsplit types)
+  int b_kmajor;                     // B stored K-major (B[k][n], n contiguous): C = A B
+                                    // (MODE_GEN / MODE_FINAL, 256-edge 16-bit tiles)
   const void *DT2;                  // optional second term init_scale2 * D2, same
   float init_scale2;                //   layout as DT (needs DT)
   int64_t pDT2;
@@ -66,15 +70,15 @@ struct GemmParams {
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_gemm(int compute_dtype, int tile, int mode, const GemmParams &p,
                        hipStream_t s);
-const char *gemm_kernel_name(int compute_dtype, int tile, int mode);
+const char *gemm_kernel_name(int compute_dtype, int tile, int mode, bool b_kmajor = false);
 
 hipError_t launch_norm_partial(int io_dtype, const void *X, int64_t batch, int64_t n,
                                int64_t m, int64_t rows_eff, const int64_t *row_idx,
                                int parts, double *partials, hipStream_t s);
 
 // X_hat = X / (||X||_F + eps) in the compute type, row-major into Xh and
-// transposed into XT; for DT_BF16X3 the lo planes sit plane_h / plane_t
-// elements after Xh / XT.
+// transposed into XT (skipped when XT is null); for DT_BF16X3 the lo planes
+// sit plane_h / plane_t elements after Xh / XT.
 hipError_t launch_scale_transpose(int io_dtype, int compute_dtype, const void *X,
                                   int64_t batch, int64_t n, int64_t m, int64_t rows_eff,
                                   const int64_t *row_idx, const double *partials,
@@ -87,8 +91,8 @@ hipError_t launch_select_rows_l1(int io_dtype, const void *M, int64_t batch, int
                                  int64_t k, double *keys, int64_t *out, hipStream_t s);
 
 // Unscaled transpose of 16-bit X (n, m multiples of 128, 16-byte aligned) into
-// XT [m][n] per matrix, and the sum of squares of every 128x128 tile into
-// partials[b][tile] (fp64).
+// XT [m][n] per matrix (skipped when XT is null), and the sum of squares of
+// every 128x128 tile into partials[b][tile] (fp64).
 hipError_t launch_transpose_sumsq(int dtype, const void *X, int64_t batch, int64_t n, int64_t m,
                                   void *XT, double *partials, hipStream_t s);
 // inv[b] = 1 / (sqrt(sum_i partials[b][i]) + eps) and inv2[b] = inv[b]^2 (fixed-order sums).

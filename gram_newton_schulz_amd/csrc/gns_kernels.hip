@@ -246,7 +246,10 @@ __device__ __forceinline__ void sym_tile(int t, int nt, int bb, int hh, int *ti,
   *ti = J * bb + r - bj * (bj + 1) / 2;
 }
 
-template <class E, int TILE, int MODE, int PL>
+// BK = 0: both operands row-major along K (C = A B^T).  BK = 1: B is stored
+// K-major, B[k][n] row-major with n contiguous (C = A B), read with the LDS
+// transpose load; 256-edge 16-bit tiles, general results only.
+template <class E, int TILE, int MODE, int PL, int BK = 0>
 __global__ void __launch_bounds__(WaveLayout<TILE>::THREADS)
 gemm_nt(GemmParams p) {
   using S = typename E::S;
@@ -270,6 +273,8 @@ gemm_nt(GemmParams p) {
   constexpr int LPS = 2 * PL * BPW;       // DMA instructions per wave per stage
   static_assert(BPW * NW * 16 == TILE, "blocks must cover the tile");
   static_assert(PL == 1 || (ESZ == 2 && NW == 4), "split planes: 16-bit types, 128-edge tiles");
+  static_assert(BK == 0 || (TILE == 256 && ESZ == 2 && PL == 1 && NW == 8 && MODE != MODE_SYM),
+                "K-major B: 256-edge 16-bit tiles, general results");
   static_assert(NST * STB <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STB];
@@ -335,7 +340,18 @@ gemm_nt(GemmParams p) {
   const int dma_row = lane >> 2;
   const int dma_chunk = (lane & 3) ^ swz(dma_row);
   const int vA = dma_row * static_cast<int>(ldaB) + dma_chunk * 16;
-  const int vB = dma_row * static_cast<int>(ldbB) + dma_chunk * 16;
+  // K-major B: a stage is 32 K rows of TILE elements (512 bytes each), and
+  // one DMA instruction fills two of them (block blk = rows 2 blk, 2 blk + 1).
+  // The 16-byte chunks of row r are XOR-swizzled by (r & 3) << 2, so that
+  // the transpose reads of four consecutive rows hit four different bank
+  // quarters.  A wave's blocks all have the parity of the wave index.
+  int vB;
+  if constexpr (BK) {
+    const int r = 2 * (wave & 1) + (lane >> 5);          // (2 blk + lane / 32) & 3
+    vB = (lane >> 5) * static_cast<int>(ldbB) + (((lane & 31) ^ (r << 2)) * 16);
+  } else {
+    vB = dma_row * static_cast<int>(ldbB) + dma_chunk * 16;
+  }
   // buffer descriptors over this tile's A and B panels, one per plane
   // (hardware range check: loads past the panel return zeros; the values are
   // wave-uniform, readfirstlane puts them in SGPRs for the asm)
@@ -347,12 +363,14 @@ gemm_nt(GemmParams p) {
     return r;
   };
   const int64_t offA = static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda;
-  const int64_t offB = static_cast<int64_t>(mat) * p.sB + static_cast<int64_t>(tj) * TILE * p.ldb;
+  // K-major B: the panel is columns tj*TILE .. of all K rows
+  const int64_t offB = static_cast<int64_t>(mat) * p.sB +
+                       (BK ? static_cast<int64_t>(tj) * TILE : static_cast<int64_t>(tj) * TILE * p.ldb);
   i32x4 rA[PL], rB[PL];
 #pragma unroll
   for (int pl = 0; pl < PL; ++pl) {
     rA[pl] = descriptor(p.A, offA + pl * p.pA, TILE * ldaB);
-    rB[pl] = descriptor(p.B, offB + pl * p.pB, TILE * ldbB);
+    rB[pl] = descriptor(p.B, offB + pl * p.pB, BK ? static_cast<int64_t>(p.K) * ldbB : TILE * ldbB);
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ldaB32 = __builtin_amdgcn_readfirstlane(static_cast<int>(ldaB));
@@ -364,6 +382,13 @@ gemm_nt(GemmParams p) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int fsw = swz(lr);
+  // K-major B transpose reads: lane j (of its group of 16) reads K row
+  // j / 4 (+ the slice's base) and the 8 bytes of columns n0 + 4 (j % 4) ..
+  // + 3, with n0 = 16 (group % 2); chunk index tr_c and byte tr_half within
+  // the 16-byte chunk.
+  const int tr_rsub = (lane & 15) >> 2;
+  const int tr_c = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  const int tr_half = 8 * (lane & 1);
 
   // Accumulators start at (beta/alpha) * D so that the epilogue is a plain
   // scale-and-store.  D is read through its transposed copy DT (D itself
@@ -384,6 +409,27 @@ gemm_nt(GemmParams p) {
     const S *DTm = static_cast<const S *>(p.DT) + static_cast<int64_t>(mat) * p.sDT;
     const int64_t i_base = static_cast<int64_t>(ti) * TILE + wr + 4 * lh;
     const int64_t j_base = static_cast<int64_t>(tj) * TILE + wc + lr;
+    if constexpr (ESZ == 2 && PL == 1) {
+      if (p.d_rows) {
+        // D in row layout, D(i,j) = DT[i * lddt + j]: the four rows of a lane
+        // are four 2-byte loads (consecutive lanes on consecutive columns)
+#pragma unroll
+        for (int i = 0; i < NBI; ++i)
+#pragma unroll
+          for (int j = 0; j < NBJ; ++j) {
+            if (half && j >= 2) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const S *src = DTm + (i_base + i * 32 + 8 * g) * p.lddt + j_base + j * 32;
+              uint32_t e[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) e[q] = src[q * p.lddt];
+              draw[0][i][j][g] = RawD{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+            }
+          }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NBI; ++i)
 #pragma unroll
@@ -470,7 +516,7 @@ gemm_nt(GemmParams p) {
       for (int q = 0; q < BPW; ++q) {
         const int blk = wave_u + q * NW;
         const int soA = blk * 16 * ldaB32 + st * SB;
-        const int soB = blk * 16 * ldbB32 + st * SB;
+        const int soB = BK ? (32 * st + 2 * blk) * ldbB32 : blk * 16 * ldbB32 + st * SB;
 #pragma unroll
         for (int pl = 0; pl < PL; ++pl) {
           asm volatile(
@@ -495,9 +541,35 @@ gemm_nt(GemmParams p) {
 #pragma unroll
         for (int b = 0; b < NBI; ++b)
           fa[slot][pl][b] = Mma<E>::load(la + pl * OPB + (wr + b * 32 + lr) * SB, sub, lh, fsw);
+        if constexpr (BK) {
+          // Transpose reads: in every group of 16 lanes, lane 4a + b receives
+          // element b of the 8-byte pieces addressed by lanes a, 4 + a, 8 + a
+          // and 12 + a.  Lane j of a group addresses K row kb + j / 4 and
+          // columns n0 + 4 (j % 4) .. + 3, so lane i ends with column n0 + i
+          // at rows kb .. kb + 3; two reads give the 8 K values of the
+          // fragment in the same order as the A fragment.
+          const unsigned char *lb = la + (PL + pl) * OPB;
 #pragma unroll
-        for (int b = 0; b < NJ; ++b)
-          fb[slot][pl][b] = Mma<E>::load(la + (PL + pl) * OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
+          for (int b = 0; b < NJ; ++b) {
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4s lv4s;
+            uint2 h2[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int row = 16 * sub + 8 * lh + 4 * q + tr_rsub;
+              const int chunk = ((wc >> 3) + 4 * b + tr_c) ^ (tr_rsub << 2);
+              const unsigned char *addr = lb + row * 512 + chunk * 16 + tr_half;
+              const v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lv4s *)((__attribute__((address_space(3))) unsigned char *)(addr)));
+              h2[q] = __builtin_bit_cast(uint2, t);
+            }
+            fb[slot][pl][b] = u32x4{h2[0].x, h2[0].y, h2[1].x, h2[1].y};
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < NJ; ++b)
+            fb[slot][pl][b] = Mma<E>::load(la + (PL + pl) * OPB + (wc + b * 32 + lr) * SB, sub, lh, fsw);
+        }
       }
     };
     auto mma = [&](int slot, auto nj) {
@@ -998,13 +1070,14 @@ scale_transpose(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int
     }
     const SC sv = TCmp::st(v);
     Xhb[gr * Mp + gc] = sv;
-    tileT[0][col][r] = sv;
+    if (XT) tileT[0][col][r] = sv;
     if constexpr (PL == 2) {
       const SC sl = TCmp::st(v - TCmp::ld(sv));
       Xhb[plane_h + gr * Mp + gc] = sl;
-      tileT[PL - 1][col][r] = sl;
+      if (XT) tileT[PL - 1][col][r] = sl;
     }
   }
+  if (!XT) return;   // row layout only
   __syncthreads();
 #pragma unroll 4
   for (int rr = 0; rr < 16; ++rr) {
@@ -1068,9 +1141,10 @@ scale_transpose16(const void *X, int64_t n, int64_t m, int64_t rows_eff, const i
 #pragma unroll
     for (int pl = 0; pl < PL; ++pl) {
       *reinterpret_cast<u32x4 *>(Xhb + pl * plane_h + gr * Mp + gc) = o[pl];
-      *reinterpret_cast<u32x4 *>(&tile[pl][row][cv]) = o[pl];
+      if (XT) *reinterpret_cast<u32x4 *>(&tile[pl][row][cv]) = o[pl];
     }
   }
+  if (!XT) return;   // row layout only
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1153,7 +1227,7 @@ transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restri
       const float f1 = T::ld(static_cast<uint16_t>(in[h][q] >> 16));
       sq += f0 * f0 + f1 * f1;
     }
-    *reinterpret_cast<u32x4 *>(&tile[v / PR][(v % PR) * 8]) = in[h];
+    if (XT) *reinterpret_cast<u32x4 *>(&tile[v / PR][(v % PR) * 8]) = in[h];
   }
   double d = static_cast<double>(sq);
   for (int off = 32; off > 0; off >>= 1) d += __shfl_down(d, off, 64);
@@ -1163,6 +1237,7 @@ transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restri
     const int64_t tile_id = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
     partials[static_cast<int64_t>(b) * gridDim.x * gridDim.y + tile_id] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   }
+  if (!XT) return;   // sums of squares only
   // X^T row c0 + c takes the 8-row run 8 k .. 8 k + 7 of tile column c
 #pragma unroll
   for (int h = 0; h < NP; ++h) {
@@ -1513,6 +1588,14 @@ static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
   const int grid = p.tiles_per_mat * p.batch;
   if (grid <= 0) return hipSuccess;
   constexpr int nt = WaveLayout<TILE>::THREADS;
+  if constexpr (TILE == 256 && PL == 1) {
+    if (p.b_kmajor && mode != MODE_SYM) {
+      if (mode == MODE_GEN) gemm_nt<E, TILE, MODE_GEN, PL, 1><<<grid, nt, 0, s>>>(p);
+      else gemm_nt<E, TILE, MODE_FINAL, PL, 1><<<grid, nt, 0, s>>>(p);
+      return hipGetLastError();
+    }
+  }
+  if (p.b_kmajor) return hipErrorInvalidValue;   // K-major B needs 256-edge 16-bit tiles
   switch (mode) {
     case MODE_SYM: gemm_nt<E, TILE, MODE_SYM, PL><<<grid, nt, 0, s>>>(p); break;
     case MODE_GEN: gemm_nt<E, TILE, MODE_GEN, PL><<<grid, nt, 0, s>>>(p); break;
@@ -1528,7 +1611,12 @@ hipError_t launch_gemm(int dt, int tile, int mode, const GemmParams &p, hipStrea
   return launch_gemm_t<EF32, 128>(mode, p, s);   // fp32 always uses 128-edge tiles
 }
 
-const char *gemm_kernel_name(int dt, int tile, int mode) {
+const char *gemm_kernel_name(int dt, int tile, int mode, bool b_kmajor) {
+  if (b_kmajor && tile == 256 && (dt == DT_BF16 || dt == DT_F16) && mode != MODE_SYM) {
+    static const char *nn[2][2] = {{"gemm_nn<bf16,256,gen>", "gemm_nn<bf16,256,final>"},
+                                   {"gemm_nn<f16,256,gen>", "gemm_nn<f16,256,final>"}};
+    return nn[dt == DT_F16 ? 1 : 0][mode == MODE_GEN ? 0 : 1];
+  }
   static const char *names[4][2][3] = {
       {{"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"},
        {"gemm_nt<f32,128,sym>", "gemm_nt<f32,128,gen>", "gemm_nt<f32,128,final>"}},
