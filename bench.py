@@ -53,15 +53,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 def short_kernel(name):
     """rocprofv3 kernel name -> the library's short name, e.g.
-    'gns::gemm_nt<gns::EBF16, 256, 0, 1>' -> 'gemm_nt<bf16,256,sym>' (the last
-    template argument is the plane count: 2 means split bf16, 'bf16x3')."""
+    'gns::gemm_nt<gns::EBF16, 256, 0, 1, 0>' -> 'gemm_nt<bf16,256,sym>'.  The
+    fourth template argument is the plane count (2 means split bf16,
+    'bf16x3'); a fifth argument of 1 marks the K-major-B product, 'gemm_nn'."""
     import re
-    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)(?:, (\d))?>", name)
+    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)(?:, (\d))?(?:, (\d))?>", name)
     if m:
         dt = m.group(1).lower()
         if m.group(4) == "2":
             dt = "bf16x3"
-        return f"gemm_nt<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
+        kind = "gemm_nn" if m.group(5) == "1" else "gemm_nt"
+        return f"{kind}<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
     for k in ("norm_partial", "scale_transpose", "transpose_sumsq", "norm_finish", "row_l1",
               "select_topk", "check_rows", "momentum_l1", "row_sumsq", "normuon_factors",
               "dion3_update"):
@@ -132,7 +134,7 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
     for src, key, scale in ((fetch, "fetch", fs), (write, "write", ws)):
         for d in src.values():
             name = short_kernel(d["kernel"])
-            if not (name.startswith("gemm_nt") or name in HBM_KERNELS):
+            if not (name.startswith("gemm_n") or name in HBM_KERNELS):
                 continue
             a = agg.setdefault(name, {"fetch": [], "write": []})
             a[key].append(d["v"] * 1024.0 * scale)
