@@ -22,6 +22,7 @@ GNS_OPT_NO_SQUARE_FALLBACK = 0x2
 GNS_OPT_ONE_STREAM = 0x4
 GNS_OPT_TILE_128 = 0x10
 GNS_OPT_TILE_256 = 0x20
+GNS_OPT_TILE_AUTOTUNE = 0x40
 MAX_ITERS = 64
 
 _DT = {torch.float32: GNS_F32, torch.bfloat16: GNS_BF16, torch.float16: GNS_F16}
@@ -37,7 +38,7 @@ EXPORTS = [
     "gns_standard_workspace_bytes", "gns_gram_batched", "gns_standard_batched",
     "gns_check_row_idx", "gns_timing_enable", "gns_timing_read", "gns_timing_reset",
     "gns_select_workspace_bytes", "gns_select_rows_l1",
-    "gns_dion3_workspace_bytes", "gns_dion3_step",
+    "gns_dion3_workspace_bytes", "gns_dion3_step", "gns_tuned_tile", "gns_autotune_clear",
 ]
 
 
@@ -94,6 +95,10 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                  dbl, dbl, dbl, dbl, dbl, ctypes.c_int, vp, ctypes.c_uint, vp, sz, vp]
+    L.gns_tuned_tile.restype = ctypes.c_int
+    L.gns_tuned_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64]
+    L.gns_autotune_clear.restype = None
+    L.gns_autotune_clear.argtypes = []
     L.gns_check_row_idx.restype = ctypes.c_int
     L.gns_check_row_idx.argtypes = [vp, i64, i64, i64, vp, vp]
     L.gns_timing_enable.argtypes = [ctypes.c_int]
@@ -150,14 +155,18 @@ def standard_workspace_bytes(compute_dtype, batch: int, rows: int, m: int) -> in
     return int(lib().gns_standard_workspace_bytes(_dtype_code(compute_dtype), batch, rows, m))
 
 
-def _tile_opts(tile: Optional[int]) -> int:
+def _tile_opts(tile) -> int:
+    """None: size-based choice; 128 or 256: that edge; "auto": measured per
+    shape (GNS_OPT_TILE_AUTOTUNE)."""
     if tile is None:
         return 0
+    if tile == "auto":
+        return GNS_OPT_TILE_AUTOTUNE
     if tile == 128:
         return GNS_OPT_TILE_128
     if tile == 256:
         return GNS_OPT_TILE_256
-    raise GnsError(10, f"tile must be 128 or 256, got {tile}")
+    raise GnsError(10, f"tile must be None, 128, 256 or 'auto', got {tile}")
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
@@ -169,10 +178,10 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.
 def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] = (2,), *,
                     row_idx: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     compute_dtype=None, naive_algebra: bool = False, square_fallback: bool = True,
-                    tile: Optional[int] = None, split_batch: bool = True,
+                    tile=None, split_batch: bool = True,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Gram Newton-Schulz of every matrix in X ([batch, n, m] or [n, m]) via
-    gns_gram_batched.  ``row_idx`` ([batch, k] int64, device) selects the
+    gns_gram_batched (``tile``: None, 128, 256 or "auto").  ``row_idx`` ([batch, k] int64, device) selects the
     rows to orthogonalise; the other rows of ``out`` are left as they are
     (``out`` defaults to a copy of X in that case)."""
     squeeze = X.dim() == 2
@@ -210,9 +219,10 @@ def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] =
 def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
                         row_idx: Optional[torch.Tensor] = None,
                         out: Optional[torch.Tensor] = None, compute_dtype=None,
-                        tile: Optional[int] = None, split_batch: bool = True,
+                        tile=None, split_batch: bool = True,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Standard Newton-Schulz (Algorithm 1) via gns_standard_batched."""
+    """Standard Newton-Schulz (Algorithm 1) via gns_standard_batched
+    (``tile``: None, 128, 256 or "auto")."""
     squeeze = X.dim() == 2
     Xb = X.unsqueeze(0) if squeeze else X
     if Xb.dim() != 3 or not Xb.is_contiguous():
@@ -238,6 +248,18 @@ def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
         _ptr(row_idx), k, _tile_opts(tile) | (0 if split_batch else GNS_OPT_ONE_STREAM),
         _ptr(ws), ws.numel(), _stream(stream)))
     return out.squeeze(0) if squeeze else out
+
+
+def tuned_tile(compute_dtype, io_dtype, batch: int, rows: int, m: int, standard: bool = False) -> int:
+    """Tile edge kept by tile="auto" for this shape (rows = k with a row
+    subset, else n), or 0 if the shape has not been tuned (gns_tuned_tile)."""
+    return int(lib().gns_tuned_tile(1 if standard else 0, _dtype_code(compute_dtype),
+                                    _dtype_code(io_dtype), batch, rows, m))
+
+
+def autotune_clear() -> None:
+    """Forget every tuned shape (gns_autotune_clear)."""
+    lib().gns_autotune_clear()
 
 
 def check_row_idx(row_idx: torch.Tensor, n: int, stream=None) -> int:

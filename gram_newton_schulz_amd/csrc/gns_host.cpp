@@ -6,10 +6,13 @@
 // allocates, nothing synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "../../include/gns.h"
@@ -469,6 +472,8 @@ gns_status parse_opts(unsigned opts, unsigned allowed, int *tile) {
   allowed |= GNS_OPT_TILE_128 | GNS_OPT_TILE_256 | GNS_OPT_ONE_STREAM;
   if (opts & ~allowed) return GNS_E_FLAGS;
   if ((opts & GNS_OPT_TILE_128) && (opts & GNS_OPT_TILE_256)) return GNS_E_FLAGS;
+  if ((opts & GNS_OPT_TILE_AUTOTUNE) && (opts & (GNS_OPT_TILE_128 | GNS_OPT_TILE_256)))
+    return GNS_E_FLAGS;
   *tile = (opts & GNS_OPT_TILE_128) ? 128 : (opts & GNS_OPT_TILE_256) ? 256 : 0;
   return GNS_OK;
 }
@@ -798,6 +803,77 @@ bool dion3_layout(int cdt, int64_t batch, int64_t n, int64_t m, int64_t k, Dion3
   return true;
 }
 
+// ---------------------------------------------------------------- autotune
+// Shape-keyed table of measured tile edges (GNS_OPT_TILE_AUTOTUNE).
+struct TuneKey {
+  int standard, cdt, io;
+  int64_t batch, rows, m;
+  bool operator<(const TuneKey &o) const {
+    return std::tie(standard, cdt, io, batch, rows, m) <
+           std::tie(o.standard, o.cdt, o.io, o.batch, o.rows, o.m);
+  }
+};
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tune;
+
+int tuned_edge(const TuneKey &key) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  const auto it = g_tune.find(key);
+  return it == g_tune.end() ? 0 : it->second;
+}
+
+void keep_edge(const TuneKey &key, int edge) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tune[key] = edge;
+}
+
+unsigned edge_bit(int edge) { return edge == 256 ? GNS_OPT_TILE_256 : GNS_OPT_TILE_128; }
+
+// run(bits) enqueues the whole call with the tile bits `bits` (0: size-based
+// choice).  An untuned shape is timed with both edges, twice each (the first
+// runs also pay one-time costs such as stream creation), and the winner's
+// result is left in the output.
+template <class Run>
+gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
+  const int kept = tuned_edge(key);
+  if (kept) return run(edge_bit(kept));
+  if (key.cdt == GNS_F32 || key.cdt == GNS_BF16X3) {   // one tile edge only
+    const gns_status st = run(GNS_OPT_TILE_128);
+    if (st == GNS_OK) keep_edge(key, 128);
+    return st;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return GNS_E_HIP;
+  if (cs != hipStreamCaptureStatusNone) return run(0);   // no timing inside a capture
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
+    if (ev[0]) (void)hipEventDestroy(ev[0]);
+    return GNS_E_HIP;
+  }
+  const int edges[2] = {128, 256};
+  float best[2] = {INFINITY, INFINITY};
+  gns_status st = GNS_OK;
+  for (int rep = 0; rep < 2 && st == GNS_OK; ++rep)
+    for (int i = 0; i < 2 && st == GNS_OK; ++i) {
+      float ms = 0.0f;
+      if (hipEventRecord(ev[0], s) != hipSuccess) { st = GNS_E_HIP; break; }
+      if ((st = run(edge_bit(edges[i]))) != GNS_OK) break;
+      if (hipEventRecord(ev[1], s) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
+          hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
+        st = GNS_E_HIP;
+        break;
+      }
+      best[i] = std::min(best[i], ms);
+    }
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  if (st != GNS_OK) return st;
+  const int win = best[1] < best[0] ? 256 : 128;
+  if (win == 128 && (st = run(edge_bit(128))) != GNS_OK) return st;   // the last run used 256
+  keep_edge(key, win);
+  return GNS_OK;
+}
+
 }  // namespace
 
 // ==========================================================================
@@ -846,7 +922,8 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
   if (st != GNS_OK) return st;
   int tile_req = 0;
-  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
+  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK | GNS_OPT_TILE_AUTOTUNE,
+                       &tile_req)) != GNS_OK)
     return st;
   const bool split = !(opts & GNS_OPT_ONE_STREAM);
   std::vector<char> restart_at;
@@ -856,6 +933,13 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
   if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;
   st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
   if (st != GNS_OK) return st;
+  if (opts & GNS_OPT_TILE_AUTOTUNE)
+    return autotune(TuneKey{0, cdt, io, batch, rows, m}, static_cast<hipStream_t>(stream),
+                    [&](unsigned bits) {
+                      return gns_gram_batched(X, out, batch, n, m, io, cdt, coeffs, T, restart_after,
+                                              n_restart, row_idx, k, (opts & ~GNS_OPT_TILE_AUTOTUNE) | bits,
+                                              workspace, workspace_bytes, stream);
+                    });
   // Square matrices: both algorithms cost the same and standard NS needs
   // fewer launches and never forms X X^T of an ill-conditioned square
   // matrix, so the pages fall back to it (Dion3 §4.1, last paragraph).
@@ -894,13 +978,20 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
   gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
   if (st != GNS_OK) return st;
   int tile_req = 0;
-  if ((st = parse_opts(opts, 0u, &tile_req)) != GNS_OK) return st;
+  if ((st = parse_opts(opts, GNS_OPT_TILE_AUTOTUNE, &tile_req)) != GNS_OK) return st;
   const bool split = !(opts & GNS_OPT_ONE_STREAM);
   if (batch == 0) return GNS_OK;
   Plan pl;
   if (!make_plan(cdt, batch, rows, m, 2, tile_req, &pl)) return GNS_E_SHAPE;
   st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
   if (st != GNS_OK) return st;
+  if (opts & GNS_OPT_TILE_AUTOTUNE)
+    return autotune(TuneKey{1, cdt, io, batch, rows, m}, static_cast<hipStream_t>(stream),
+                    [&](unsigned bits) {
+                      return gns_standard_batched(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k,
+                                                  (opts & ~GNS_OPT_TILE_AUTOTUNE) | bits, workspace,
+                                                  workspace_bytes, stream);
+                    });
   const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
   const bool direct = direct_input(pl, X, io, cdt, row_idx);
   return run_batches(pl, cdt, batch, workspace, static_cast<hipStream_t>(stream), split,
@@ -913,6 +1004,15 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
                        return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io,
                                                n, coeffs, T, ri, ri, n);
                      });
+}
+
+int gns_tuned_tile(int standard, gns_dtype cdt, gns_dtype io, int64_t batch, int64_t rows, int64_t m) {
+  return tuned_edge(TuneKey{standard ? 1 : 0, cdt, io, batch, rows, m});
+}
+
+void gns_autotune_clear(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tune.clear();
 }
 
 size_t gns_select_workspace_bytes(int64_t batch, int64_t n) {

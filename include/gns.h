@@ -104,6 +104,10 @@ typedef enum {
                                       library's two streams (see below)      */
 #define GNS_OPT_TILE_128 0x10u     /* force 128 x 128 output tiles            */
 #define GNS_OPT_TILE_256 0x20u     /* force 256 x 256 output tiles            */
+#define GNS_OPT_TILE_AUTOTUNE 0x40u /* pick the tile edge by timing (see
+                                      gns_tuned_tile); gns_gram_batched and
+                                      gns_standard_batched only, not with a
+                                      TILE bit                                */
 /* Without a TILE bit the library picks the tile edge from the problem size.
    Results are identical up to floating-point summation order either way.
    fp32 compute always runs 128-edge tiles (GNS_OPT_TILE_256 is ignored). */
@@ -273,6 +277,29 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
  */
 gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, void *stream);
+
+/*
+ * Shape-keyed tile autotuning ("DMuon: Efficient Distributed Muon Training
+ * with Near-Adam Overhead", §3.3: the best tile shape of the batched Gram NS
+ * kernels varies by shape, so it is chosen per shape by measurement).  With
+ * GNS_OPT_TILE_AUTOTUNE, the first call of
+ * a shape -- entry point, compute and I/O dtypes, batch, rows (k with a row
+ * subset, else n) and m -- runs the whole call with 128- and with 256-edge
+ * tiles, twice each, on `stream` and blocks the host until they end; the
+ * edge with the smaller time is kept in a process-wide table, and the
+ * caller's `out` holds the result of a run with that edge.  Later calls of
+ * the shape run the kept edge with no timing.  fp32 and split-bf16 compute
+ * have one edge (128) and are never timed.  While `stream` is being captured
+ * into a graph, an untuned shape runs the size-based choice and stays
+ * untuned.  A failing run returns its status and keeps nothing.
+ *
+ * gns_tuned_tile returns the kept edge for a shape (standard = 0 for
+ * gns_gram_batched, 1 for gns_standard_batched), or 0 if the shape has not
+ * been tuned.  gns_autotune_clear forgets every shape.  Both are thread-safe.
+ */
+int gns_tuned_tile(int standard, gns_dtype compute_dtype, gns_dtype io_dtype, int64_t batch,
+                   int64_t rows, int64_t m);
+void gns_autotune_clear(void);
 
 /*
  * Optional per-launch timing for measurement tools.  While enabled, every

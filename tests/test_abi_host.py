@@ -104,6 +104,11 @@ def test_gram_argument_errors():
     assert _gram(restarts=(2, 2)) == E["RESTART"]
     assert _gram(opts=0x80) == E["FLAGS"]
     assert _gram(opts=0x30) == E["FLAGS"]                 # both tile bits
+    assert _gram(opts=0x50) == E["FLAGS"]                 # autotune with a tile bit
+    assert _gram(opts=0x60) == E["FLAGS"]
+    # autotune validates every argument before it times anything
+    assert _gram(opts=0x40, ws_bytes=100) == E["WORKSPACE"]
+    assert _gram(opts=0x40, restarts=(5,)) == E["RESTART"]
     assert _gram(X=None) == E["NULL"]
     assert _gram(out=None) == E["NULL"]
     assert _gram(ws=None, ws_bytes=0) != E["OK"]
@@ -128,6 +133,9 @@ def test_standard_argument_errors():
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0, ws, 16, None) == E["WORKSPACE"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 1, ws, need, None) == E["FLAGS"]
     assert L.gns_standard_batched(None, None, 0, 4, 8, 1, 1, carr, 5, None, 0, 0, None, 0, None) == E["OK"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0x50, ws, need, None) == E["FLAGS"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 8, 1, 1, carr, 5, None, 0, 0x40, ws, 16, None) == E["WORKSPACE"]
+    assert L.gns_standard_batched(None, None, 0, 4, 8, 1, 1, carr, 5, None, 0, 0x40, None, 0, None) == E["OK"]
 
 
 def test_check_row_idx_argument_errors():
@@ -220,9 +228,31 @@ def test_dion3_argument_errors():
     assert _dion3(mu=float("inf")) == E["PARAM"]
     assert _dion3(eps=0.0) == E["PARAM"]                   # NorMuon divides by sqrt(v) + eps
     assert _dion3(opts=0x80) == E["FLAGS"]
+    assert _dion3(opts=0x40) == E["FLAGS"]                 # no autotune for the whole update
     assert _dion3(W=None) == E["NULL"] and _dion3(rows=None) == E["NULL"]
     assert _dion3(v=None) == E["NULL"]                     # NorMuon needs v
     assert _dion3(ws_bytes=64) == E["WORKSPACE"] and _dion3(ws=0x7f0000000008) == E["WORKSPACE"]
     assert _dion3(M=FAKE + 4096) == E["ALIAS"]             # momentum overlaps the weights
     assert _dion3(G=0x7f0000000000 + 256) == E["ALIAS"]    # gradient overlaps the workspace
     assert _dion3(batch=0, W=None, G=None, M=None, v=None, rows=None, ws=None, ws_bytes=0) == E["OK"]
+
+
+def test_autotune_table_starts_empty_and_clears():
+    L = gns.lib()
+    L.gns_autotune_clear()
+    assert gns.tuned_tile(gns.GNS_BF16, gns.GNS_BF16, 8, 4096, 16384) == 0
+    assert gns.tuned_tile(gns.GNS_BF16, gns.GNS_BF16, 8, 4096, 16384, standard=True) == 0
+    # a validation failure keeps nothing
+    assert _gram(opts=0x40, ws_bytes=100) == E["WORKSPACE"]
+    assert L.gns_tuned_tile(0, 1, 1, 1, 4, 8) == 0
+    gns.autotune_clear()
+
+
+def test_binding_tile_option():
+    from gram_newton_schulz_amd import binding
+    assert binding._tile_opts(None) == 0
+    assert binding._tile_opts(128) == binding.GNS_OPT_TILE_128
+    assert binding._tile_opts(256) == binding.GNS_OPT_TILE_256
+    assert binding._tile_opts("auto") == binding.GNS_OPT_TILE_AUTOTUNE
+    with pytest.raises(gns.GnsError):
+        binding._tile_opts(64)
