@@ -420,15 +420,16 @@ gns_status apply_nn(const Ctx &c, const void *S, const void *Xrow_in, int64_t ld
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
 
-// Norm + scale + cast + transpose of the (row-selected) input.  On the
-// direct path: the unscaled transpose X^T and the per-matrix scale factors.
+// Norm + scale + cast (+ transpose, where a path reads X^T) of the
+// (row-selected) input.  On the direct path: the per-matrix scale factors and,
+// unless the products read X row-major, the unscaled transpose X^T.
 gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const int64_t *row_idx) {
   double *partials = c.partials();
   const double rows = static_cast<double>(c.pl->rows), m = static_cast<double>(c.pl->m);
   if (c.direct) {
     {
       LaunchScope ls(c.s, "transpose_sumsq", "transpose_sumsq", 2.0 * rows * m * c.batch,
-                     c.batch * rows * m * 2.0 * gns::dtype_size(io));
+                     c.batch * rows * m * (c.nn ? 1.0 : 2.0) * gns::dtype_size(io));
       hipError_t e = gns::launch_transpose_sumsq(io, X, c.batch, c.pl->rows, c.pl->m,
                                                  c.nn ? nullptr : c.xt(0), c.tile_partials(), c.s);
       ls.done();
@@ -593,7 +594,7 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
   const void *xrow = c.direct ? c.xin : c.xh();
   int64_t xrow_ld = c.direct ? c.pl->m : c.pl->Mp;
   int rcur = c.direct ? 0 : 1;
-  // the unscaled input transpose carries the normalisation as a factor
+  // the unscaled input (row-major, or its transpose) carries the normalisation as a factor
   const float *x_scale = c.direct ? c.inv() : nullptr;
   for (int t = 1; t <= T; ++t) {
     const float a = static_cast<float>(coeffs[3 * (t - 1) + 0]);

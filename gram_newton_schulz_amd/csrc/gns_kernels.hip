@@ -3,9 +3,12 @@
 // * norm_partial     -- Frobenius norm, first stage: per-workgroup sums of
 //                       squares in fixed order (HBM-bound, vector loads).
 // * scale_transpose  -- X_hat = X / (||X||_F + eps) rounded once to the
-//                       compute dtype, written both row-major [n][m] and
-//                       transposed [m][n] (zero padded to whole tiles); the
-//                       second stage of the norm reduction runs in its prologue.
+//                       compute dtype, written row-major [n][m] and, where a
+//                       path reads it, transposed [m][n] (zero padded to whole
+//                       tiles); the second stage of the norm reduction runs in
+//                       its prologue.
+// * transpose_sumsq  -- input already in the compute type: per-tile sums of
+//                       squares (and the transposed copy, where one is read).
 // * gemm_nt          -- C = alpha * A B^T + beta * D on bf16/fp16 (32x32x16)
 //                       or fp32 (32x32x2) MFMA with fp32 accumulation, or on
 //                       split hi/lo bf16 pairs (three bf16 MFMAs per product).
@@ -14,12 +17,17 @@
 //                       LDS-DMA buffer loads into a 5-stage ring of 32-element
 //                       K stages, XOR-swizzled.  Symmetric results compute only
 //                       the upper tiles and mirror them ("Dion3: Full-Stack
-//                       Orthogonal Updates", §5 and App. C.1-C.2).
+//                       Orthogonal Updates", §5 and App. C.1-C.2).  With a
+//                       K-major B (BK = 1) the same kernel computes C = A B.
+// * row_l1, select_topk, momentum_l1, row_sumsq, normuon_factors,
+//   dion3_update     -- the HBM-bound steps of the Dion3 update around the
+//                       orthogonalisation (Dion3 §6, Algorithm 4).
 //
-// Every product of the method is written as A B^T with both operands stored
-// row-major along the contraction index: X X^T directly; products of two
-// n x n iterates because every stored iterate is exactly symmetric (so its
-// rows are its columns); Q X through the transposed copy of X kept beside it.
+// Every product of the method reads its operands row-major: X X^T directly;
+// products of two n x n iterates as A B^T, because every stored iterate is
+// exactly symmetric (so its rows are its columns); Q X either with X as a
+// K-major B (16-bit 256-edge tiles, LDS transpose reads) or, on the other
+// paths, as A B^T through the transposed copy of X kept beside it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -155,6 +155,31 @@ def test_row_subset(algo, cdt):
         assert np.array_equal(got[b][keep], init64[b][keep])
 
 
+@pytest.mark.parametrize("cdt", ["bf16", "f16"])
+@pytest.mark.parametrize("restarts", [(2,), (1, 3), ()])
+def test_row_subset_kmajor_products(cdt, restarts):
+    """Row subset on 256-edge 16-bit tiles, where Q X reads X row-major
+    (K-major B): ragged k and m, the restart's second row buffer, and the
+    final product's row scatter; other rows bit-exact."""
+    gns = need_gpu()
+    B, n, m, k = 2, 600, 900, 301
+    X, X64 = _inputs(B, n, m, "bf16", seed=37)
+    rows = np.stack([synth.row_subset(n, k, seed=37, index=b) for b in range(B)])
+    init = torch.randn(B, n, m, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    out = init.clone().cuda()
+    say(f"row subset k-major {cdt} restarts={restarts}")
+    gns.gram_ns_batched(X.cuda(), NS5, restarts=restarts, compute_dtype=DT[cdt], tile=256,
+                        row_idx=torch.from_numpy(rows).cuda(), out=out)
+    torch.cuda.synchronize()
+    got = synth.as_f64(out)
+    init64 = synth.as_f64(init)
+    for b in range(B):
+        sel = rows[b]
+        assert rel_err(got[b][sel], oracle_gram(X64[b][sel], restarts=restarts)) <= TOL_HALF
+        keep = np.setdiff1d(np.arange(n), sel)
+        assert np.array_equal(got[b][keep], init64[b][keep])
+
+
 def test_row_subset_full_permutation_matches_plain():
     gns = need_gpu()
     B, n, m = 2, 140, 300
