@@ -454,8 +454,11 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
     if (e != hipSuccess) return GNS_E_HIP;
   }
   {
+    // reads X once, writes X_hat (all planes) and, unless the products read X
+    // row-major, its transpose
     LaunchScope ls(c.s, "scale_transpose", "scale_transpose", rows * m * c.batch,
-                   c.batch * rows * m * (gns::dtype_size(io) + 2.0 * c.pl->esz));
+                   c.batch * rows * m *
+                       (gns::dtype_size(io) + (c.nn ? 1.0 : 2.0) * c.pl->planes * c.pl->esz));
     // X_hat row-major [rows][m] and its transpose; for a tall problem X_hat is
     // Y^T (the xt buffer) and its transpose is Y (the xh buffer)
     void *dst_rows = c.pl->tall ? c.xt(0) : c.xh();

@@ -83,6 +83,26 @@ struct EF32 {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming passes that read and write every element once give their loads
+// and stores the non-temporal hint, which moves these mixed read/write
+// streams faster (Dion3 momentum pass 4.7 -> 5.1 TB/s, update 4.7 -> 5.2,
+// row sums 4.3 -> 5.4).
+__device__ __forceinline__ void st_once(float4 *p, float4 x) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4f{x.x, x.y, x.z, x.w}, reinterpret_cast<v4f *>(p));
+}
+__device__ __forceinline__ float4 ld_once(const float4 *p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_once(const uint2 *p) {
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(p));
+  return make_uint2(v.x, v.y);
+}
+
+
 // One lane's share of a 16-deep slice of the contraction: 8 consecutive
 // elements (one 16-byte chunk for 16-bit types, two for fp32).  A and B
 // fragments use the same element -> k mapping, so the products pair up
@@ -1095,6 +1115,45 @@ scale_transpose(const void *X, int64_t n, int64_t m, int64_t rows_eff, const int
   }
 }
 
+// Same operation for fp32 input, a 16-bit compute type and the row layout
+// only (no transposed copy), with m a multiple of 4 and X 16-byte aligned:
+// one wave per row of X_hat (gathered through row_idx), 16-byte loads and
+// 8-byte stores, zeros in the padding up to Np x Mp.  The same norm and the
+// same rounding as above.
+template <class TCmp>
+__global__ void __launch_bounds__(256)
+scale_rows_f32(const float *X, int64_t n, int64_t m, int64_t rows_eff, const int64_t *row_idx,
+               const double *partials, int parts, double eps, void *Xh, int64_t Np, int64_t Mp) {
+  using SC = typename TCmp::S;
+  const int b = blockIdx.y;
+  __shared__ float inv_s;
+  if (threadIdx.x < 64) {  // norm stage 2, same fixed order in every workgroup
+    double s = 0.0;
+    for (int i = threadIdx.x; i < parts; i += 64) s += partials[static_cast<int64_t>(b) * parts + i];
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off, 64);
+    if (threadIdx.x == 0) inv_s = static_cast<float>(1.0 / (sqrt(s) + eps));
+  }
+  __syncthreads();
+  const float inv = inv_s;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= Np) return;
+  SC *dst = static_cast<SC *>(Xh) + (static_cast<int64_t>(b) * Np + r) * Mp;
+  const float *src = nullptr;
+  if (r < rows_eff) {
+    const int64_t row = row_idx ? row_idx[static_cast<int64_t>(b) * rows_eff + r] : r;
+    if (row >= 0 && row < n) src = X + (static_cast<int64_t>(b) * n + row) * m;
+  }
+  const int64_t m4 = src ? m / 4 : 0;
+  for (int64_t v = lane; v < Mp / 4; v += 64) {
+    float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (v < m4) x = ld_once(reinterpret_cast<const float4 *>(src) + v);
+    const uint32_t lo = static_cast<uint32_t>(TCmp::st(x.x * inv)) | (static_cast<uint32_t>(TCmp::st(x.y * inv)) << 16);
+    const uint32_t hi = static_cast<uint32_t>(TCmp::st(x.z * inv)) | (static_cast<uint32_t>(TCmp::st(x.w * inv)) << 16);
+    reinterpret_cast<uint2 *>(dst)[v] = make_uint2(lo, hi);
+  }
+}
+
 // Same operation for 16-bit input and compute types with m a multiple of 8:
 // 16-byte loads and stores on every global access (rows of X and X_hat, and
 // 8-row runs of each X^T row), transposed through a padded LDS tile.
@@ -1401,25 +1460,6 @@ select_topk(const double *keys, int64_t n, int64_t k, int64_t *out) {
 // Dion3 update around the orthogonalisation ("Dion3: Full-Stack Orthogonal
 // Updates", §6, Algorithm 4, with the optional NorMuon steps of §2.1, eq. (2))
 // ---------------------------------------------------------------------------
-// The streaming passes read and write every element once; their loads and
-// stores carry the non-temporal hint, which moves these mixed read/write
-// streams faster (momentum pass 4.7 -> 5.1 TB/s, update 4.7 -> 5.2, row sums
-// 4.3 -> 5.4).
-__device__ __forceinline__ void st_once(float4 *p, float4 x) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(v4f{x.x, x.y, x.z, x.w}, reinterpret_cast<v4f *>(p));
-}
-__device__ __forceinline__ float4 ld_once(const float4 *p) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 ld_once(const uint2 *p) {
-  typedef unsigned v2u __attribute__((ext_vector_type(2)));
-  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(p));
-  return make_uint2(v.x, v.y);
-}
-
 // The momentum takes the gradient, M <- M + G (one fp32 addition per
 // element, stored), and every row of the sum gets its l1 key sum_j |M_ij|
 // (fp64; lane-strided 16-byte pieces, then the wave tree: a fixed order for
@@ -1687,6 +1727,16 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
                                   void *XT, int64_t Np, int64_t Mp, int64_t ph, int64_t pt,
                                   hipStream_t s) {
   dim3 grid(static_cast<unsigned>(Mp / 64), static_cast<unsigned>(Np / 64), static_cast<unsigned>(batch));
+  if (io == DT_F32 && (cdt == DT_BF16 || cdt == DT_F16) && !XT && m % 4 == 0 && Mp % 4 == 0 &&
+      (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (reinterpret_cast<uintptr_t>(Xh) & 7) == 0) {
+    const dim3 g(static_cast<unsigned>((Np + 3) / 4), static_cast<unsigned>(batch));
+    const float *Xf = static_cast<const float *>(X);
+    if (cdt == DT_BF16)
+      scale_rows_f32<EBF16><<<g, 256, 0, s>>>(Xf, n, m, rows_eff, row_idx, partials, parts, eps, Xh, Np, Mp);
+    else
+      scale_rows_f32<EF16><<<g, 256, 0, s>>>(Xf, n, m, rows_eff, row_idx, partials, parts, eps, Xh, Np, Mp);
+    return hipGetLastError();
+  }
   const bool vec = (m % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && io != DT_F32 && cdt != DT_F32;
   if (vec) {
 #define GNS_ST16(TI, TC, PL) \

@@ -180,6 +180,33 @@ def test_row_subset_kmajor_products(cdt, restarts):
         assert np.array_equal(got[b][keep], init64[b][keep])
 
 
+@pytest.mark.parametrize("cdt", ["bf16", "f16"])
+@pytest.mark.parametrize("m", [700, 702])
+@pytest.mark.parametrize("subset", [False, True])
+def test_f32_input_row_layout(cdt, m, subset):
+    """fp32 input, 16-bit products on 256-edge tiles: the normalised copy is
+    written in row layout only (one wave per row when m is a multiple of 4,
+    the tiled kernel otherwise), with and without a row subset."""
+    gns = need_gpu()
+    B, n = 2, 300
+    X, X64 = _inputs(B, n, m, "f32", seed=38)
+    kw = {}
+    rows = None
+    if subset:
+        rows = np.stack([synth.row_subset(n, 211, seed=38, index=b) for b in range(B)])
+        kw = dict(row_idx=torch.from_numpy(rows).cuda(), out=torch.zeros(B, n, m, device="cuda"))
+    say(f"f32 input row layout cdt={cdt} m={m} subset={subset}")
+    out = gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=DT[cdt], tile=256, **kw)
+    torch.cuda.synchronize()
+    got = synth.as_f64(out)
+    for b in range(B):
+        sel = rows[b] if subset else np.arange(n)
+        assert rel_err(got[b][sel], oracle_gram(X64[b][sel])) <= TOL_HALF
+        if subset:
+            keep = np.setdiff1d(np.arange(n), sel)
+            assert not np.any(got[b][keep])
+
+
 def test_row_subset_full_permutation_matches_plain():
     gns = need_gpu()
     B, n, m = 2, 140, 300
