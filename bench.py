@@ -64,7 +64,7 @@ def short_kernel(name):
             dt = "bf16x3"
         kind = "gemm_nn" if m.group(5) == "1" else "gemm_nt"
         return f"{kind}<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
-    for k in ("norm_partial", "scale_transpose", "transpose_sumsq", "norm_finish", "row_l1",
+    for k in ("norm_partial", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish", "row_l1",
               "select_topk", "check_rows", "momentum_l1", "row_sumsq", "normuon_factors",
               "dion3_update"):
         if k in name:
@@ -151,7 +151,7 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
                                         "source_sha256_16": kernel_source_hash()}))
 
 
-HBM_KERNELS = ("norm_partial", "scale_transpose", "transpose_sumsq", "norm_finish", "momentum_l1",
+HBM_KERNELS = ("norm_partial", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish", "momentum_l1",
                "row_sumsq", "normuon_factors", "dion3_update", "select_topk")
 
 

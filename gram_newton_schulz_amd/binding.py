@@ -23,6 +23,7 @@ GNS_OPT_ONE_STREAM = 0x4
 GNS_OPT_TILE_128 = 0x10
 GNS_OPT_TILE_256 = 0x20
 GNS_OPT_TILE_AUTOTUNE = 0x40
+GNS_OPT_TILE_MIXED = 0x80
 MAX_ITERS = 64
 
 _DT = {torch.float32: GNS_F32, torch.bfloat16: GNS_BF16, torch.float16: GNS_F16}
@@ -96,7 +97,8 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                  dbl, dbl, dbl, dbl, dbl, ctypes.c_int, vp, ctypes.c_uint, vp, sz, vp]
     L.gns_tuned_tile.restype = ctypes.c_int
-    L.gns_tuned_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64]
+    L.gns_tuned_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                 ctypes.POINTER(ctypes.c_int)]
     L.gns_autotune_clear.restype = None
     L.gns_autotune_clear.argtypes = []
     L.gns_check_row_idx.restype = ctypes.c_int
@@ -156,17 +158,20 @@ def standard_workspace_bytes(compute_dtype, batch: int, rows: int, m: int) -> in
 
 
 def _tile_opts(tile) -> int:
-    """None: size-based choice; 128 or 256: that edge; "auto": measured per
-    shape (GNS_OPT_TILE_AUTOTUNE)."""
+    """None: size-based choice; 128 or 256: that edge for every product;
+    "mixed": 256 for the rectangular and 128 for the symmetric products;
+    "auto": measured per shape (GNS_OPT_TILE_AUTOTUNE)."""
     if tile is None:
         return 0
     if tile == "auto":
         return GNS_OPT_TILE_AUTOTUNE
+    if tile == "mixed":
+        return GNS_OPT_TILE_MIXED
     if tile == 128:
         return GNS_OPT_TILE_128
     if tile == 256:
         return GNS_OPT_TILE_256
-    raise GnsError(10, f"tile must be None, 128, 256 or 'auto', got {tile}")
+    raise GnsError(10, f"tile must be None, 128, 256, 'mixed' or 'auto', got {tile}")
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
@@ -181,7 +186,7 @@ def gram_ns_batched(X: torch.Tensor, coeffs: Sequence, restarts: Sequence[int] =
                     tile=None, split_batch: bool = True,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Gram Newton-Schulz of every matrix in X ([batch, n, m] or [n, m]) via
-    gns_gram_batched (``tile``: None, 128, 256 or "auto").  ``row_idx`` ([batch, k] int64, device) selects the
+    gns_gram_batched (``tile``: None, 128, 256, "mixed" or "auto").  ``row_idx`` ([batch, k] int64, device) selects the
     rows to orthogonalise; the other rows of ``out`` are left as they are
     (``out`` defaults to a copy of X in that case)."""
     squeeze = X.dim() == 2
@@ -222,7 +227,7 @@ def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
                         tile=None, split_batch: bool = True,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Standard Newton-Schulz (Algorithm 1) via gns_standard_batched
-    (``tile``: None, 128, 256 or "auto")."""
+    (``tile``: None, 128, 256, "mixed" or "auto")."""
     squeeze = X.dim() == 2
     Xb = X.unsqueeze(0) if squeeze else X
     if Xb.dim() != 3 or not Xb.is_contiguous():
@@ -250,11 +255,15 @@ def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
     return out.squeeze(0) if squeeze else out
 
 
-def tuned_tile(compute_dtype, io_dtype, batch: int, rows: int, m: int, standard: bool = False) -> int:
+def tuned_tile(compute_dtype, io_dtype, batch: int, rows: int, m: int, standard: bool = False,
+               symmetric: bool = False) -> int:
     """Tile edge kept by tile="auto" for this shape (rows = k with a row
-    subset, else n), or 0 if the shape has not been tuned (gns_tuned_tile)."""
-    return int(lib().gns_tuned_tile(1 if standard else 0, _dtype_code(compute_dtype),
-                                    _dtype_code(io_dtype), batch, rows, m))
+    subset, else n) for the rectangular products, or with ``symmetric`` for
+    the symmetric ones; 0 if the shape has not been tuned (gns_tuned_tile)."""
+    sym = ctypes.c_int(0)
+    rect = int(lib().gns_tuned_tile(1 if standard else 0, _dtype_code(compute_dtype),
+                                    _dtype_code(io_dtype), batch, rows, m, ctypes.byref(sym)))
+    return sym.value if symmetric else rect
 
 
 def autotune_clear() -> None:

@@ -39,7 +39,8 @@ bool valid_compute(int dt) { return valid_dtype(dt) || dt == GNS_BF16X3; }
 // (polar(X) = polar(X^T)^T; "Dion3" §2 assumes n <= m without loss of
 // generality).  Buffers: xh = Y row-major [Np][Mp], xt = Y^T row-major [Mp][Np].
 struct Plan {
-  int tile = 128;
+  int tile = 128;                      // tile edge of the rectangular products
+  int sym_tile = 128;                  // and of the symmetric ones
   int64_t batch = 0, rows = 0, m = 0;  // the caller's (selected) rows and columns
   int64_t r = 0, c = 0;                // short and long side of Y
   bool tall = false;                   // rows > m
@@ -72,7 +73,22 @@ int choose_parts(int64_t batch, int64_t rows) {
   return static_cast<int>(std::max<int64_t>(p, 1));
 }
 
-// tile_request: 0 = choose, else 128 or 256.  Workspace sizes are quoted
+// Tile request: 0 = choose from the size, 128 or 256 = that edge for every
+// product, kTileMixed = 256 for the rectangular and 128 for the symmetric
+// products.
+constexpr int kTileMixed = 384;
+
+// The symmetric products keep the 256 edge once they have as many upper
+// tiles over the batch as the GPU has compute units; below that, 128-edge
+// tiles fill it better (8 x 1024x16384: 2.02 -> 1.61 ms per call, the 1024
+// selected rows of 8 x 4096x16384: 2.38 -> 2.03, 4 x 2048x8192: 1.99 ->
+// 1.82, 16 x 1024x4096: 1.40 -> 1.31, 8 x 2048x4096: 2.25 -> 2.21).
+int choose_sym_tile(int64_t batch, int64_t rows) {
+  const int64_t t256 = (rows + 255) / 256;
+  return t256 * (t256 + 1) / 2 * batch >= 256 ? 256 : 128;
+}
+
+// tile_request: see kTileMixed.  Workspace sizes are quoted
 // for 256-padded buffers so that any tile choice fits.
 bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, int tile_request,
                Plan *pl) {
@@ -80,9 +96,17 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
   pl->tall = rows > m;
   pl->r = std::min(rows, m);
   pl->c = std::max(rows, m);
-  pl->tile = tile_request ? tile_request : choose_tile(cdt, batch, pl->r);
+  if (tile_request == 0) {
+    pl->tile = choose_tile(cdt, batch, pl->r);
+    pl->sym_tile = pl->tile == 256 ? choose_sym_tile(batch, pl->r) : 128;
+  } else if (tile_request == kTileMixed) {
+    pl->tile = 256;
+    pl->sym_tile = 128;
+  } else {
+    pl->tile = pl->sym_tile = tile_request;
+  }
   // the fp32 and split-plane kernels exist for 128-edge tiles only
-  if (cdt == GNS_F32 || cdt == GNS_BF16X3) pl->tile = 128;
+  if (cdt == GNS_F32 || cdt == GNS_BF16X3) pl->tile = pl->sym_tile = 128;
   pl->batch = batch;
   pl->rows = rows;
   pl->m = m;
@@ -280,7 +304,7 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
                 const void *D2 = nullptr, float beta2 = 0.0f) {
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np;
-  const int nt = static_cast<int>(N / c.pl->tile);
+  const int nt = static_cast<int>(N / c.pl->sym_tile);
   p.A = A; p.lda = N; p.sA = c.sq_stride();
   p.B = B; p.ldb = N; p.sB = c.sq_stride();
   p.K = static_cast<int>(N);
@@ -298,9 +322,9 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.diag1 = diag1; p.diag2 = diag2;
   const double n = static_cast<double>(c.pl->r);
   const double bytes = c.batch * n * n * c.pl->esz * (3.0 + (D ? 1.0 : 0.0) + (D2 ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
-  LaunchScope ls(c.s, what, gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), flops * c.batch,
+  LaunchScope ls(c.s, what, gns::gemm_kernel_name(c.cdt, c.pl->sym_tile, gns::MODE_SYM), flops * c.batch,
                  bytes);
-  hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, gns::MODE_SYM, p, c.s);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->sym_tile, gns::MODE_SYM, p, c.s);
   ls.done();
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
@@ -312,7 +336,7 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
 gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow = nullptr) {
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
-  const int nt = static_cast<int>(N / c.pl->tile);
+  const int nt = static_cast<int>(N / c.pl->sym_tile);
   const bool direct = from_input && c.direct;
   const void *Xh = direct ? c.xin : (xrow ? xrow : c.xh());
   if (direct) p.alpha_vec = c.inv2();
@@ -324,9 +348,9 @@ gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow
   p.pA = p.pB = c.plane_rect();
   p.pC = c.plane_sq();
   const double n = static_cast<double>(c.pl->r), m = static_cast<double>(c.pl->c);
-  LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->tile, gns::MODE_SYM), n * n * m * c.batch,
+  LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->sym_tile, gns::MODE_SYM), n * n * m * c.batch,
                  c.batch * (n * m + n * n) * c.pl->esz);
-  hipError_t e = gns::launch_gemm(c.cdt, c.pl->tile, gns::MODE_SYM, p, c.s);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->sym_tile, gns::MODE_SYM, p, c.s);
   ls.done();
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
@@ -476,12 +500,15 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
 }
 
 gns_status parse_opts(unsigned opts, unsigned allowed, int *tile) {
-  allowed |= GNS_OPT_TILE_128 | GNS_OPT_TILE_256 | GNS_OPT_ONE_STREAM;
+  allowed |= GNS_OPT_TILE_128 | GNS_OPT_TILE_256 | GNS_OPT_TILE_MIXED | GNS_OPT_ONE_STREAM;
   if (opts & ~allowed) return GNS_E_FLAGS;
-  if ((opts & GNS_OPT_TILE_128) && (opts & GNS_OPT_TILE_256)) return GNS_E_FLAGS;
-  if ((opts & GNS_OPT_TILE_AUTOTUNE) && (opts & (GNS_OPT_TILE_128 | GNS_OPT_TILE_256)))
-    return GNS_E_FLAGS;
-  *tile = (opts & GNS_OPT_TILE_128) ? 128 : (opts & GNS_OPT_TILE_256) ? 256 : 0;
+  const unsigned tile_bits =
+      opts & (GNS_OPT_TILE_128 | GNS_OPT_TILE_256 | GNS_OPT_TILE_MIXED | GNS_OPT_TILE_AUTOTUNE);
+  if (tile_bits & (tile_bits - 1)) return GNS_E_FLAGS;   // at most one
+  *tile = (opts & GNS_OPT_TILE_128) ? 128
+          : (opts & GNS_OPT_TILE_256) ? 256
+          : (opts & GNS_OPT_TILE_MIXED) ? kTileMixed
+                                        : 0;
   return GNS_OK;
 }
 
@@ -811,7 +838,8 @@ bool dion3_layout(int cdt, int64_t batch, int64_t n, int64_t m, int64_t k, Dion3
 }
 
 // ---------------------------------------------------------------- autotune
-// Shape-keyed table of measured tile edges (GNS_OPT_TILE_AUTOTUNE).
+// Shape-keyed table of measured tile choices (GNS_OPT_TILE_AUTOTUNE); the
+// value is the TILE option bit that won.
 struct TuneKey {
   int standard, cdt, io;
   int64_t batch, rows, m;
@@ -821,32 +849,30 @@ struct TuneKey {
   }
 };
 std::mutex g_tune_mu;
-std::map<TuneKey, int> g_tune;
+std::map<TuneKey, unsigned> g_tune;
 
-int tuned_edge(const TuneKey &key) {
+unsigned tuned_choice(const TuneKey &key) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   const auto it = g_tune.find(key);
-  return it == g_tune.end() ? 0 : it->second;
+  return it == g_tune.end() ? 0u : it->second;
 }
 
-void keep_edge(const TuneKey &key, int edge) {
+void keep_choice(const TuneKey &key, unsigned bit) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
-  g_tune[key] = edge;
+  g_tune[key] = bit;
 }
-
-unsigned edge_bit(int edge) { return edge == 256 ? GNS_OPT_TILE_256 : GNS_OPT_TILE_128; }
 
 // run(bits) enqueues the whole call with the tile bits `bits` (0: size-based
-// choice).  An untuned shape is timed with both edges, twice each (the first
-// runs also pay one-time costs such as stream creation), and the winner's
-// result is left in the output.
+// choice).  An untuned shape is timed with every choice, twice each (the
+// first runs also pay one-time costs such as stream creation), and the
+// winner's result is left in the output.
 template <class Run>
 gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
-  const int kept = tuned_edge(key);
-  if (kept) return run(edge_bit(kept));
+  const unsigned kept = tuned_choice(key);
+  if (kept) return run(kept);
   if (key.cdt == GNS_F32 || key.cdt == GNS_BF16X3) {   // one tile edge only
     const gns_status st = run(GNS_OPT_TILE_128);
-    if (st == GNS_OK) keep_edge(key, 128);
+    if (st == GNS_OK) keep_choice(key, GNS_OPT_TILE_128);
     return st;
   }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -857,14 +883,15 @@ gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
     if (ev[0]) (void)hipEventDestroy(ev[0]);
     return GNS_E_HIP;
   }
-  const int edges[2] = {128, 256};
-  float best[2] = {INFINITY, INFINITY};
+  constexpr int kChoices = 3;
+  const unsigned bits[kChoices] = {GNS_OPT_TILE_128, GNS_OPT_TILE_256, GNS_OPT_TILE_MIXED};
+  float best[kChoices] = {INFINITY, INFINITY, INFINITY};
   gns_status st = GNS_OK;
   for (int rep = 0; rep < 2 && st == GNS_OK; ++rep)
-    for (int i = 0; i < 2 && st == GNS_OK; ++i) {
+    for (int i = 0; i < kChoices && st == GNS_OK; ++i) {
       float ms = 0.0f;
       if (hipEventRecord(ev[0], s) != hipSuccess) { st = GNS_E_HIP; break; }
-      if ((st = run(edge_bit(edges[i]))) != GNS_OK) break;
+      if ((st = run(bits[i])) != GNS_OK) break;
       if (hipEventRecord(ev[1], s) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
           hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
         st = GNS_E_HIP;
@@ -875,9 +902,12 @@ gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
   (void)hipEventDestroy(ev[0]);
   (void)hipEventDestroy(ev[1]);
   if (st != GNS_OK) return st;
-  const int win = best[1] < best[0] ? 256 : 128;
-  if (win == 128 && (st = run(edge_bit(128))) != GNS_OK) return st;   // the last run used 256
-  keep_edge(key, win);
+  int win = 0;
+  for (int i = 1; i < kChoices; ++i)
+    if (best[i] < best[win]) win = i;
+  // the last run used the last choice: leave the winner's result in the output
+  if (win != kChoices - 1 && (st = run(bits[win])) != GNS_OK) return st;
+  keep_choice(key, bits[win]);
   return GNS_OK;
 }
 
@@ -1013,8 +1043,12 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
                      });
 }
 
-int gns_tuned_tile(int standard, gns_dtype cdt, gns_dtype io, int64_t batch, int64_t rows, int64_t m) {
-  return tuned_edge(TuneKey{standard ? 1 : 0, cdt, io, batch, rows, m});
+int gns_tuned_tile(int standard, gns_dtype cdt, gns_dtype io, int64_t batch, int64_t rows, int64_t m,
+                   int *sym_edge) {
+  const unsigned bit = tuned_choice(TuneKey{standard ? 1 : 0, cdt, io, batch, rows, m});
+  const int rect = bit == GNS_OPT_TILE_128 ? 128 : bit ? 256 : 0;
+  if (sym_edge) *sym_edge = bit == GNS_OPT_TILE_256 ? 256 : bit ? 128 : 0;
+  return rect;
 }
 
 void gns_autotune_clear(void) {

@@ -104,13 +104,20 @@ typedef enum {
                                       library's two streams (see below)      */
 #define GNS_OPT_TILE_128 0x10u     /* force 128 x 128 output tiles            */
 #define GNS_OPT_TILE_256 0x20u     /* force 256 x 256 output tiles            */
-#define GNS_OPT_TILE_AUTOTUNE 0x40u /* pick the tile edge by timing (see
+#define GNS_OPT_TILE_AUTOTUNE 0x40u /* pick the tiles by timing (see
                                       gns_tuned_tile); gns_gram_batched and
-                                      gns_standard_batched only, not with a
-                                      TILE bit                                */
-/* Without a TILE bit the library picks the tile edge from the problem size.
-   Results are identical up to floating-point summation order either way.
-   fp32 compute always runs 128-edge tiles (GNS_OPT_TILE_256 is ignored). */
+                                      gns_standard_batched only, not with
+                                      another TILE bit                        */
+#define GNS_OPT_TILE_MIXED 0x80u   /* 256 x 256 tiles for the rectangular
+                                      products (Gram-matrix inputs times Q),
+                                      128 x 128 tiles for the symmetric ones */
+/* At most one TILE bit.  Without one the library picks from the problem
+   size: 256-edge tiles once the symmetric products have 64 upper 256-edge
+   tiles over the batch, and of those, 128-edge tiles for the symmetric
+   products while they have fewer 256-edge tiles than the GPU has compute
+   units (256), so that they fill it.  The tile edges do not change the
+   arithmetic.  fp32 and split-bf16 compute always run 128-edge tiles
+   (GNS_OPT_TILE_256 and GNS_OPT_TILE_MIXED are ignored there). */
 
 /* Version of this ABI (GNS_ABI_VERSION). */
 int gns_abi_version(void);
@@ -282,23 +289,25 @@ gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, i
  * Shape-keyed tile autotuning ("DMuon: Efficient Distributed Muon Training
  * with Near-Adam Overhead", §3.3: the best tile shape of the batched Gram NS
  * kernels varies by shape, so it is chosen per shape by measurement).  With
- * GNS_OPT_TILE_AUTOTUNE, the first call of
- * a shape -- entry point, compute and I/O dtypes, batch, rows (k with a row
- * subset, else n) and m -- runs the whole call with 128- and with 256-edge
- * tiles, twice each, on `stream` and blocks the host until they end; the
- * edge with the smaller time is kept in a process-wide table, and the
- * caller's `out` holds the result of a run with that edge.  Later calls of
- * the shape run the kept edge with no timing.  fp32 and split-bf16 compute
- * have one edge (128) and are never timed.  While `stream` is being captured
+ * GNS_OPT_TILE_AUTOTUNE, the first call of a shape -- entry point, compute
+ * and I/O dtypes, batch, rows (k with a row subset, else n) and m -- runs
+ * the whole call with each tile choice (128-edge, 256-edge and mixed tiles,
+ * see GNS_OPT_TILE_MIXED), twice each, on `stream` and blocks the host until
+ * they end; the choice with the smallest time is kept in a process-wide
+ * table, and the caller's `out` holds the result of a run with that choice.
+ * Later calls of the shape run the kept choice with no timing.  fp32 and
+ * split-bf16 compute have one choice (128) and are never timed.  While `stream` is being captured
  * into a graph, an untuned shape runs the size-based choice and stays
  * untuned.  A failing run returns its status and keeps nothing.
  *
- * gns_tuned_tile returns the kept edge for a shape (standard = 0 for
- * gns_gram_batched, 1 for gns_standard_batched), or 0 if the shape has not
- * been tuned.  gns_autotune_clear forgets every shape.  Both are thread-safe.
+ * gns_tuned_tile returns the kept tile edge of the rectangular products for
+ * a shape (standard = 0 for gns_gram_batched, 1 for gns_standard_batched),
+ * or 0 if the shape has not been tuned; when sym_edge is not NULL it
+ * receives the edge of the symmetric products (0 if untuned).
+ * gns_autotune_clear forgets every shape.  Both are thread-safe.
  */
 int gns_tuned_tile(int standard, gns_dtype compute_dtype, gns_dtype io_dtype, int64_t batch,
-                   int64_t rows, int64_t m);
+                   int64_t rows, int64_t m, int *sym_edge);
 void gns_autotune_clear(void);
 
 /*

@@ -102,10 +102,12 @@ def test_gram_argument_errors():
     assert _gram(restarts=(5,)) == E["RESTART"]           # must be <= T-1
     assert _gram(restarts=(3, 2)) == E["RESTART"]
     assert _gram(restarts=(2, 2)) == E["RESTART"]
-    assert _gram(opts=0x80) == E["FLAGS"]
-    assert _gram(opts=0x30) == E["FLAGS"]                 # both tile bits
+    assert _gram(opts=0x100) == E["FLAGS"]
+    assert _gram(opts=0x30) == E["FLAGS"]                 # two tile bits
     assert _gram(opts=0x50) == E["FLAGS"]                 # autotune with a tile bit
     assert _gram(opts=0x60) == E["FLAGS"]
+    assert _gram(opts=0x90) == E["FLAGS"] and _gram(opts=0xa0) == E["FLAGS"] and _gram(opts=0xc0) == E["FLAGS"]
+    assert _gram(opts=0x80, ws_bytes=100) == E["WORKSPACE"]   # mixed tiles: a valid option
     # autotune validates every argument before it times anything
     assert _gram(opts=0x40, ws_bytes=100) == E["WORKSPACE"]
     assert _gram(opts=0x40, restarts=(5,)) == E["RESTART"]
@@ -132,6 +134,7 @@ def test_standard_argument_errors():
     assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 8, 1, 1, carr, 5, None, 0, 0, ws, 16, None) == E["WORKSPACE"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0, ws, 16, None) == E["WORKSPACE"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 1, ws, need, None) == E["FLAGS"]
+    assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0xc0, ws, need, None) == E["FLAGS"]
     assert L.gns_standard_batched(None, None, 0, 4, 8, 1, 1, carr, 5, None, 0, 0, None, 0, None) == E["OK"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 4, 8, 1, 1, carr, 5, None, 0, 0x50, ws, need, None) == E["FLAGS"]
     assert L.gns_standard_batched(FAKE, FAKE, 1, 9, 8, 1, 1, carr, 5, None, 0, 0x40, ws, 16, None) == E["WORKSPACE"]
@@ -227,8 +230,9 @@ def test_dion3_argument_errors():
     assert _dion3(lr=float("nan")) == E["PARAM"]
     assert _dion3(mu=float("inf")) == E["PARAM"]
     assert _dion3(eps=0.0) == E["PARAM"]                   # NorMuon divides by sqrt(v) + eps
-    assert _dion3(opts=0x80) == E["FLAGS"]
+    assert _dion3(opts=0x100) == E["FLAGS"]
     assert _dion3(opts=0x40) == E["FLAGS"]                 # no autotune for the whole update
+    assert _dion3(opts=0x90) == E["FLAGS"]                 # two tile bits
     assert _dion3(W=None) == E["NULL"] and _dion3(rows=None) == E["NULL"]
     assert _dion3(v=None) == E["NULL"]                     # NorMuon needs v
     assert _dion3(ws_bytes=64) == E["WORKSPACE"] and _dion3(ws=0x7f0000000008) == E["WORKSPACE"]
@@ -244,7 +248,9 @@ def test_autotune_table_starts_empty_and_clears():
     assert gns.tuned_tile(gns.GNS_BF16, gns.GNS_BF16, 8, 4096, 16384, standard=True) == 0
     # a validation failure keeps nothing
     assert _gram(opts=0x40, ws_bytes=100) == E["WORKSPACE"]
-    assert L.gns_tuned_tile(0, 1, 1, 1, 4, 8) == 0
+    sym = ctypes.c_int(-1)
+    assert L.gns_tuned_tile(0, 1, 1, 1, 4, 8, ctypes.byref(sym)) == 0 and sym.value == 0
+    assert L.gns_tuned_tile(0, 1, 1, 1, 4, 8, None) == 0
     gns.autotune_clear()
 
 
@@ -254,5 +260,6 @@ def test_binding_tile_option():
     assert binding._tile_opts(128) == binding.GNS_OPT_TILE_128
     assert binding._tile_opts(256) == binding.GNS_OPT_TILE_256
     assert binding._tile_opts("auto") == binding.GNS_OPT_TILE_AUTOTUNE
+    assert binding._tile_opts("mixed") == binding.GNS_OPT_TILE_MIXED
     with pytest.raises(gns.GnsError):
         binding._tile_opts(64)

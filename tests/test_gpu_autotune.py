@@ -1,8 +1,9 @@
 """Shape-keyed tile autotuning (tile="auto", GNS_OPT_TILE_AUTOTUNE) through
-the C ABI: the first call of a shape times both tile edges and keeps the
-faster one; its result and every later call's are those of that edge, and
-within the fp64 oracle's tolerance.  fp32 has one edge; an untuned shape
-under graph capture runs the size-based choice and stays untuned."""
+the C ABI: the first call of a shape times the tile choices (128, 256,
+mixed) and keeps the fastest; its result and every later call's are those
+of that choice, and within the fp64 oracle's tolerance.  fp32 has one
+choice; an untuned shape under graph capture runs the size-based choice
+and stays untuned."""
 import numpy as np
 import pytest
 import torch
@@ -33,12 +34,14 @@ def test_autotune_keeps_an_edge_and_matches_it(algo):
     first = run(tile="auto")
     torch.cuda.synchronize()
     edge = gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m, standard=std)
-    assert edge in (128, 256)
+    sym = gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m, standard=std, symmetric=True)
+    assert (edge, sym) in ((128, 128), (256, 256), (256, 128))
+    choice = "mixed" if (edge, sym) == (256, 128) else edge
     # the other entry point's table entry is separate
     assert gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m, standard=not std) == 0
-    say(f"autotune {algo}: kept edge {edge}, later call and forced edge")
+    say(f"autotune {algo}: kept {choice}, later call and forced choice")
     again = run(tile="auto")
-    forced = run(tile=edge)
+    forced = run(tile=choice)
     torch.cuda.synchronize()
     assert torch.equal(first, forced)
     assert torch.equal(again, forced)
@@ -79,6 +82,7 @@ def test_autotune_fp32_has_one_edge():
     out = gns.gram_ns_batched(X.cuda(), NS5, tile="auto")
     torch.cuda.synchronize()
     assert gns.tuned_tile(torch.float32, torch.float32, B, n, m) == 128
+    assert gns.tuned_tile(torch.float32, torch.float32, B, n, m, symmetric=True) == 128
     ref = np.stack([oracle_gram(x) for x in X64])
     assert max(per_matrix_rel(out.double().cpu().numpy(), ref)) < TOL_F32
     gns.autotune_clear()

@@ -48,7 +48,7 @@ def test_config1_fp32():
     assert rel_err(ref, oracle.spectral_map(X64[0], NS5)) <= 1e-10
 
 
-@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("tile", [128, 256, "mixed"])
 @pytest.mark.parametrize("algo", ["gram", "standard"])
 @pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("bf16", "f16"), ("f32", "f32"),
                                     ("f16", "f16"), ("f32", "bf16"), ("bf16", "bf16x3"),
@@ -504,7 +504,7 @@ def test_graph_capture_replays(split):
 
 
 @pytest.mark.parametrize("algo,restarts", [("gram", (2,)), ("gram", ()), ("gram", (1, 3)), ("standard", ())])
-@pytest.mark.parametrize("io,tile", [("bf16", 128), ("bf16", 256), ("f16", 256)])
+@pytest.mark.parametrize("io,tile", [("bf16", 128), ("bf16", 256), ("f16", 256), ("bf16", "mixed")])
 def test_direct_input_path(algo, restarts, io, tile):
     """Whole-tile shapes with the input already in the compute type: the
     products read X itself and apply the normalisation in their epilogues
