@@ -78,14 +78,16 @@ int choose_parts(int64_t batch, int64_t rows) {
 // products.
 constexpr int kTileMixed = 384;
 
-// The symmetric products keep the 256 edge once they have as many upper
-// tiles over the batch as the GPU has compute units; below that, 128-edge
-// tiles fill it better (8 x 1024x16384: 2.02 -> 1.61 ms per call, the 1024
-// selected rows of 8 x 4096x16384: 2.38 -> 2.03, 4 x 2048x8192: 1.99 ->
-// 1.82, 16 x 1024x4096: 1.40 -> 1.31, 8 x 2048x4096: 2.25 -> 2.21).
+// The symmetric products switch to 128-edge tiles when their 256-edge grid
+// has fewer upper tiles over the batch than the GPU has compute units and
+// the n x n contractions are short (n <= 2048): the fuller grid then wins
+// (8 x 1024x16384: 2.02 -> 1.61 ms per call, the 1024 selected rows of
+// 8 x 4096x16384: 2.38 -> 2.03, 4 x 2048x8192: 1.99 -> 1.82, 16 x 1024x4096:
+// 1.40 -> 1.31).  With n = 4096 the 256 edge stays faster even on 136 tiles
+// (1 x 4096x16384: 3.25 against 3.61 ms), as on every larger grid measured.
 int choose_sym_tile(int64_t batch, int64_t rows) {
   const int64_t t256 = (rows + 255) / 256;
-  return t256 * (t256 + 1) / 2 * batch >= 256 ? 256 : 128;
+  return (t256 * (t256 + 1) / 2 * batch < 256 && rows <= 2048) ? 128 : 256;
 }
 
 // tile_request: see kTileMixed.  Workspace sizes are quoted

@@ -115,7 +115,8 @@ typedef enum {
    size: 256-edge tiles once the symmetric products have 64 upper 256-edge
    tiles over the batch, and of those, 128-edge tiles for the symmetric
    products while they have fewer 256-edge tiles than the GPU has compute
-   units (256), so that they fill it.  The tile edges do not change the
+   units (256) and the orthogonalised side is at most 2048, so that they
+   fill it.  The tile edges do not change the
    arithmetic.  fp32 and split-bf16 compute always run 128-edge tiles
    (GNS_OPT_TILE_256 and GNS_OPT_TILE_MIXED are ignored there). */
 
