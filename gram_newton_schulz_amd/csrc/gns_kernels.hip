@@ -953,13 +953,26 @@ gemm_nt(GemmParams p) {
     const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
     const bool plain = !ridx && p.out_dtype == E::code;
     if constexpr (kStage) {
-      // the whole tile lies inside the caller's matrix, in the compute type,
-      // with 16-byte aligned rows: staged full-row stores
-      if (plain && tr0 + TILE <= p.rows_eff && tc0 + TILE <= p.out_cols && (p.out_cols & 7) == 0 &&
-          (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
+      // output in the compute type with 16-byte aligned rows: staged row
+      // pieces, each row to its destination row (through row_idx if given);
+      // rows past rows_eff and pieces past out_cols (a multiple of 8) are
+      // padding and skipped
+      if (p.out_dtype == E::code && (p.out_cols & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
         pack(false);
         stage_direct();
-        store_staged(static_cast<S *>(p.out) + obase, p.out_cols, tr0, tc0, false);
+        S *O = static_cast<S *>(p.out) + obase;
+        constexpr int CPR = TILE / 8;                      // 16-byte pieces per row
+#pragma unroll 4
+        for (int k = tid; k < TILE * CPR; k += NT) {
+          const int rr = k / CPR;
+          const int cc = (k % CPR) * 8;
+          const int64_t i = tr0 + rr;
+          if (i >= p.rows_eff || tc0 + cc >= p.out_cols) continue;
+          const int64_t row = ridx ? ridx[i] : i;
+          if (row < 0 || row >= p.out_rows) continue;
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(Ts + rr * TP + cc);
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(O + row * p.out_cols + tc0 + cc));
+        }
         return;
       }
     }
