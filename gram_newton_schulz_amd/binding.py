@@ -339,7 +339,7 @@ def dion3_step(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, v: Optional[to
                k: int, coeffs: Sequence, restarts: Sequence[int] = (2,), *, lr: float = 0.02,
                weight_decay: float = 0.0, mu: float = 0.95, beta2: float = 0.95, eps: float = 1e-8,
                normuon: bool = True, compute_dtype=torch.bfloat16, naive_algebra: bool = False,
-               square_fallback: bool = True, tile: Optional[int] = None, split_batch: bool = True,
+               square_fallback: bool = True, tile=None, split_batch: bool = True,
                row_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     """One Dion3 update (Algorithm 4) of every matrix in W ([batch, n, m] or

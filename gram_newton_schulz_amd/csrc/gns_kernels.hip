@@ -975,6 +975,47 @@ gemm_nt(GemmParams p) {
         }
         return;
       }
+      // fp32 output (not rounded to the compute type): the same, in two
+      // halves of 128 rows (waves 0-3 hold rows 0-127, waves 4-7 rows
+      // 128-255), each staged as fp32 with a 260-float row pitch.  bf16
+      // products only: with fp16 the path makes the kernel spill.
+      if (std::is_same<E, EBF16>::value && p.out_dtype == DT_F32 && (p.out_cols & 3) == 0 &&
+          (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
+        constexpr int HR = TILE / 2;                       // rows per half
+        constexpr int TPF = TILE + 4;                      // fp32 row pitch
+        static_assert(HR * TPF * 4 <= NST * STB, "fp32 half tile fits the ring");
+        float *const Tf = reinterpret_cast<float *>(lds);
+        float *O = static_cast<float *>(p.out) + obase;
+        constexpr int CPR = TILE / 4;                      // 16-byte pieces per row
+        for (int h = 0; h < 2; ++h) {
+          __syncthreads();                                 // ring / previous half no longer read
+          if ((wr >= HR) == (h == 1)) {
+            float *const tw = Tf + (wr - HR * h + 4 * lh) * TPF + wc + lr;
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+              for (int jb = 0; jb < NBJ; ++jb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    tw[(ib * 32 + 8 * g + q) * TPF + jb * 32] = alpha * acc[ib][jb][4 * g + q];
+          }
+          __syncthreads();
+#pragma unroll 4
+          for (int k = tid; k < HR * CPR; k += NT) {
+            const int rr = k / CPR;
+            const int cc = (k % CPR) * 4;
+            const int64_t i = tr0 + HR * h + rr;
+            if (i >= p.rows_eff || tc0 + cc >= p.out_cols) continue;
+            const int64_t row = ridx ? ridx[i] : i;
+            if (row < 0 || row >= p.out_rows) continue;
+            const float4 v = *reinterpret_cast<const float4 *>(Tf + rr * TPF + cc);
+            st_once(reinterpret_cast<float4 *>(O + row * p.out_cols + tc0 + cc), v);
+          }
+        }
+        return;
+      }
     }
     if (plain && row_base + WTM <= p.rows_eff && col_base + WTN <= p.out_cols) {
       // the whole wave tile lies inside the caller's matrix and needs no

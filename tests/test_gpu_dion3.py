@@ -33,21 +33,21 @@ def _run(gns, W, G, M, v, k, **kw):
     return Wd.cpu(), Md.cpu(), (None if vd is None else vd.cpu()), S.cpu()
 
 
-def _check_step(gns, count, n, m, k, seed, grad_dtype, compute_dtype, tol, members):
+def _check_step(gns, count, n, m, k, seed, grad_dtype, compute_dtype, tol, members, tile=None):
     W, G, M, v = synth.dion3_state(count, n, m, seed=seed, grad_dtype=grad_dtype)
     Z = torch.zeros_like(W)
     Msum = (M + G.float())                               # plain fp32 torch
     mu = 0.5
-    say(f"dion3 run A {count}x{n}x{m} k={k} {grad_dtype} {compute_dtype}")
+    say(f"dion3 run A {count}x{n}x{m} k={k} {grad_dtype} {compute_dtype} tile={tile}")
     WA, MA, _, SA = _run(gns, Z, G, M, None, k, lr=1.0, weight_decay=0.0, mu=mu, normuon=False,
-                         compute_dtype=compute_dtype)
+                         compute_dtype=compute_dtype, tile=tile)
     say(f"dion3 run B")
     WB, MB, vB, SB = _run(gns, Z, G, M, v, k, lr=1.0, weight_decay=0.0, mu=mu, beta2=0.9, eps=1e-8,
-                          normuon=True, compute_dtype=compute_dtype)
+                          normuon=True, compute_dtype=compute_dtype, tile=tile)
     lr, wd = 0.02, 0.1
     say(f"dion3 run C")
     WC, MC, vC, SC = _run(gns, W, G, M, v, k, lr=lr, weight_decay=wd, mu=mu, beta2=0.9, eps=1e-8,
-                          normuon=True, compute_dtype=compute_dtype)
+                          normuon=True, compute_dtype=compute_dtype, tile=tile)
     assert torch.equal(SA, SB) and torch.equal(SA, SC)
     decay = np.float32(1.0 - lr * wd)
     for b in members:
@@ -93,6 +93,16 @@ def test_dion3_step_small_ragged():
     """3 x 150x520 (ragged against every tile), k = 40, bf16 gradient."""
     gns = need_gpu()
     _check_step(gns, 3, 150, 520, 40, 31, torch.bfloat16, torch.bfloat16, TOL_HALF, range(3))
+
+
+@pytest.mark.parametrize("tile", [256, "mixed"])
+def test_dion3_step_256_tiles(tile):
+    """3 x 300x1030 with k = 211 on forced 256-edge (or mixed) tiles: the
+    fp32 update leaves the last product through the staged fp32 epilogue
+    (ragged rows) or, with m not a multiple of 4, element by element."""
+    gns = need_gpu()
+    _check_step(gns, 3, 300, 1030, 211, 39, torch.bfloat16, torch.bfloat16, TOL_HALF, range(3), tile=tile)
+    _check_step(gns, 2, 300, 1032, 211, 40, torch.bfloat16, torch.bfloat16, TOL_HALF, range(2), tile=tile)
 
 
 def test_dion3_step_fp32_compute():
