@@ -430,7 +430,24 @@ def test_tall_matches_transposed_problem(tile):
     assert max(per_matrix_rel(synth.as_f64(a), synth.as_f64(b.transpose(1, 2)))) <= 1e-5
 
 
-def test_tall_row_subset():
+@pytest.mark.parametrize("tile", [256, "mixed"])
+@pytest.mark.parametrize("algo", ["gram", "standard"])
+def test_tall_16bit_tiles(algo, tile):
+    """n > m in bf16 on forced 256-edge or mixed tiles: the transposed path
+    of the rectangular products, and the final product's staged stores into
+    the caller's layout (ragged on both sides)."""
+    gns = need_gpu()
+    B, n, m = 3, 700, 300
+    X, X64 = _inputs(B, n, m, "bf16", seed=41)
+    say(f"tall 16-bit {algo} tile={tile}")
+    out = _run(gns, algo, X.cuda(), "bf16", tile=tile)
+    torch.cuda.synchronize()
+    ref = np.stack([(oracle_gram if algo == "gram" else oracle_standard)(X64[b]) for b in range(B)])
+    assert max(per_matrix_rel(synth.as_f64(out), ref)) <= TOL_HALF
+
+
+@pytest.mark.parametrize("tile", [None, 256, "mixed"])
+def test_tall_row_subset(tile):
     """Dion3 rows with more selected rows than columns (k > m)."""
     gns = need_gpu()
     B, n, m, k = 2, 400, 150, 230
@@ -438,8 +455,8 @@ def test_tall_row_subset():
     rows = np.stack([synth.row_subset(n, k, seed=28, index=b) for b in range(B)])
     init = torch.randn(B, n, m, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
     out = init.clone().cuda()
-    say("tall row subset")
-    gns.gram_ns_batched(X.cuda(), NS5, row_idx=torch.from_numpy(rows).cuda(), out=out)
+    say(f"tall row subset tile={tile}")
+    gns.gram_ns_batched(X.cuda(), NS5, row_idx=torch.from_numpy(rows).cuda(), out=out, tile=tile)
     torch.cuda.synchronize()
     got = synth.as_f64(out)
     init64 = synth.as_f64(init)
