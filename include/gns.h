@@ -108,17 +108,18 @@ typedef enum {
                                       gns_tuned_tile); gns_gram_batched and
                                       gns_standard_batched only, not with
                                       another TILE bit                        */
-#define GNS_OPT_TILE_MIXED 0x80u   /* 256 x 256 tiles for the rectangular
-                                      products (Gram-matrix inputs times Q),
-                                      128 x 128 tiles for the symmetric ones */
+#define GNS_OPT_TILE_MIXED 0x80u   /* 256 x 256 tiles for the products Q X
+                                      (restart and final), 128 x 128 tiles for
+                                      the symmetric ones (Gram matrix, n x n
+                                      iteration)                              */
 /* At most one TILE bit.  Without one the library picks from the problem
    size: 256-edge tiles once the symmetric products have 64 upper 256-edge
-   tiles over the batch, and of those, 128-edge tiles for the symmetric
-   products while they have fewer 256-edge tiles than the GPU has compute
-   units (256) and the orthogonalised side is at most 2048, so that they
-   fill it.  The tile edges do not change the
-   arithmetic.  fp32 and split-bf16 compute always run 128-edge tiles
-   (GNS_OPT_TILE_256 and GNS_OPT_TILE_MIXED are ignored there). */
+   tiles over the batch; of those, the symmetric products run 128-edge tiles
+   while they have fewer 256-edge tiles than the GPU has compute units (256)
+   and the orthogonalised side is at most 2048, so that they fill it.  The
+   tile edges do not change the arithmetic.  fp32 and split-bf16 compute
+   always run 128-edge tiles (GNS_OPT_TILE_256 and GNS_OPT_TILE_MIXED are
+   ignored there). */
 
 /* Version of this ABI (GNS_ABI_VERSION). */
 int gns_abi_version(void);
@@ -297,9 +298,10 @@ gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, i
  * they end; the choice with the smallest time is kept in a process-wide
  * table, and the caller's `out` holds the result of a run with that choice.
  * Later calls of the shape run the kept choice with no timing.  fp32 and
- * split-bf16 compute have one choice (128) and are never timed.  While `stream` is being captured
- * into a graph, an untuned shape runs the size-based choice and stays
- * untuned.  A failing run returns its status and keeps nothing.
+ * split-bf16 compute have one choice (128) and are never timed.  While
+ * `stream` is being captured into a graph, an untuned shape runs the
+ * size-based choice and stays untuned.  A failing run returns its status
+ * and keeps nothing.
  *
  * gns_tuned_tile returns the kept tile edge of the rectangular products for
  * a shape (standard = 0 for gns_gram_batched, 1 for gns_standard_batched),
