@@ -256,7 +256,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU sharding is a design note, not part of this build", file=sys.stderr)
+              "the library runs on one GPU; sharding across GPUs is described, not implemented",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

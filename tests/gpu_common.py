@@ -26,7 +26,7 @@ def need_gpu():
         pytest.skip("no GPU")
     import gram_newton_schulz_amd as gns
     if not os.path.exists(gns.LIB_PATH):
-        raise RuntimeError("libgns.so not built: the HIP path is required on a GPU box")
+        raise RuntimeError("libgns.so not built: the HIP path is required where a GPU is present")
     return gns
 
 
