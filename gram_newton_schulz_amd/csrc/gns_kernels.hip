@@ -83,6 +83,9 @@ struct EF32 {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// Type tag (selects the 16-bit type an epilogue rounds to).
+template <class T> struct Tag { using type = T; };
+
 // Streaming passes that read and write every element once give their loads
 // and stores the non-temporal hint, which moves these mixed read/write
 // streams faster (Dion3 momentum pass 4.7 -> 5.1 TB/s, update 4.7 -> 5.2,
@@ -739,7 +742,10 @@ gemm_nt(GemmParams p) {
   // diagonal entry this lane holds (dv[ib]; see fix_diag).
   uint32_t pk[NBI][NBJ][8];
   float dv[NBI];
-  auto pack = [&](bool keep_diag) {
+  // tag: the 16-bit type to round to (the compute type, or the caller's
+  // output type for the final product)
+  auto pack = [&](bool keep_diag, auto tag) {
+    using T = typename decltype(tag)::type;
     const int dreg = 4 * (lr >> 3) + (lr & 3);
 #pragma unroll
     for (int ib = 0; ib < NBI; ++ib) {
@@ -755,8 +761,8 @@ gemm_nt(GemmParams p) {
         }
 #pragma unroll
         for (int h = 0; h < 8; ++h)
-          pk[ib][jb][h] = static_cast<uint32_t>(E::st(alpha * acc[ib][jb][2 * h])) |
-                          (static_cast<uint32_t>(E::st(alpha * acc[ib][jb][2 * h + 1])) << 16);
+          pk[ib][jb][h] = static_cast<uint32_t>(T::st(alpha * acc[ib][jb][2 * h])) |
+                          (static_cast<uint32_t>(T::st(alpha * acc[ib][jb][2 * h + 1])) << 16);
       }
     }
   };
@@ -846,7 +852,7 @@ gemm_nt(GemmParams p) {
     S *C2m = p.C2 ? static_cast<S *>(p.C2) + static_cast<int64_t>(mat) * p.sC2 : nullptr;
     const bool diag_tile = (ti == tj);
     if constexpr (kStage) {
-      pack(diag_tile);
+      pack(diag_tile, Tag<E>{});
       if (!diag_tile) {
         // C and its mirror; C2 equals C off the diagonal
         stage_direct();
@@ -917,7 +923,7 @@ gemm_nt(GemmParams p) {
     S *Cm = static_cast<S *>(p.C) + static_cast<int64_t>(mat) * p.sC;
     S *CTm = p.CT ? static_cast<S *>(p.CT) + static_cast<int64_t>(mat) * p.sCT : nullptr;
     if constexpr (kStage) {
-      pack(false);
+      pack(false, Tag<E>{});
       stage_direct();
       store_staged(Cm, p.ldc, tr0, tc0, false);
       if (CTm) {
@@ -953,12 +959,22 @@ gemm_nt(GemmParams p) {
     const int64_t obase = static_cast<int64_t>(mat) * p.out_rows * p.out_cols;
     const bool plain = !ridx && p.out_dtype == E::code;
     if constexpr (kStage) {
-      // output in the compute type with 16-byte aligned rows: staged row
-      // pieces, each row to its destination row (through row_idx if given);
-      // rows past rows_eff and pieces past out_cols (a multiple of 8) are
-      // padding and skipped
-      if (p.out_dtype == E::code && (p.out_cols & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
-        pack(false);
+      // 16-bit output with 16-byte aligned rows: rounded once to the output
+      // type, staged, and written as row pieces, each row to its destination
+      // row (through row_idx if given); rows past rows_eff and pieces past
+      // out_cols (a multiple of 8) are padding and skipped
+      // (fp16 products also round to a bf16 output here; bf16 products with
+      // an fp16 output take the element path below, as a second rounding
+      // there would make the bf16 kernels spill)
+      constexpr bool kToBf16 = std::is_same<E, EF16>::value;
+      if ((p.out_dtype == E::code || (kToBf16 && p.out_dtype == DT_BF16)) && (p.out_cols & 7) == 0 &&
+          (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
+        if constexpr (kToBf16) {
+          if (p.out_dtype == DT_BF16) pack(false, Tag<EBF16>{});
+          else pack(false, Tag<E>{});
+        } else {
+          pack(false, Tag<E>{});
+        }
         stage_direct();
         S *O = static_cast<S *>(p.out) + obase;
         constexpr int CPR = TILE / 8;                      // 16-byte pieces per row

@@ -207,6 +207,35 @@ def test_f32_input_row_layout(cdt, m, subset):
             assert not np.any(got[b][keep])
 
 
+@pytest.mark.parametrize("subset", [False, True])
+@pytest.mark.parametrize("io,cdt", [("bf16", "f16"), ("bf16", "bf16"), ("f16", "f16")])
+def test_final_staged_matches_element_path(io, cdt, subset):
+    """The final product's staged row-piece stores (16-bit output, rows
+    aligned) round exactly as its element-by-element stores (forced with an
+    output 2 bytes off alignment): bit-identical, and within the oracle's
+    tolerance; fp16 products with a bf16 output included."""
+    gns = need_gpu()
+    B, n, m = 2, 300, 1032
+    X, X64 = _inputs(B, n, m, io, seed=42)
+    kw = {}
+    rows = None
+    if subset:
+        rows = np.stack([synth.row_subset(n, 173, seed=42, index=b) for b in range(B)])
+        kw["row_idx"] = torch.from_numpy(rows).cuda()
+    buf = torch.zeros(2 * B * n * m + 8, dtype=X.dtype, device="cuda")
+    aligned = buf[:B * n * m].view(B, n, m)
+    shifted = buf[B * n * m + 1:2 * B * n * m + 1].view(B, n, m)   # 2 bytes off 16-byte alignment
+    say(f"final staged vs element io={io} cdt={cdt} subset={subset}")
+    for out in (aligned, shifted):
+        gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=DT[cdt], tile=256, out=out, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned, shifted)
+    got = synth.as_f64(aligned)
+    for b in range(B):
+        sel = rows[b] if subset else np.arange(n)
+        assert rel_err(got[b][sel], oracle_gram(X64[b][sel])) <= TOL_HALF
+
+
 def test_row_subset_full_permutation_matches_plain():
     gns = need_gpu()
     B, n, m = 2, 140, 300
