@@ -41,6 +41,8 @@ bool valid_compute(int dt) { return valid_dtype(dt) || dt == GNS_BF16X3; }
 struct Plan {
   int tile = 128;                      // tile edge of the rectangular products
   int sym_tile = 128;                  // and of the symmetric ones
+  int syrk_parts = 1;                  // K parts of the Gram matrix (256-edge tiles)
+  int syrk_parts_room = 1;             // parts the workspace has room for
   int64_t batch = 0, rows = 0, m = 0;  // the caller's (selected) rows and columns
   int64_t r = 0, c = 0;                // short and long side of Y
   bool tall = false;                   // rows > m
@@ -51,6 +53,7 @@ struct Plan {
   size_t off_partials = 0, off_inv = 0, off_xh = 0, off_xt0 = 0, off_xt1 = 0;
   int64_t tile_parts = 0;              // 128x128 tiles per matrix (direct input path)
   size_t off_sq[5] = {0, 0, 0, 0, 0};  // R, Z, RZ, Q0, Q1 (standard NS: A, B)
+  size_t off_part = 0;                 // fp32 partial Gram tiles of a K split
   size_t bytes = 0;
 };
 
@@ -88,6 +91,21 @@ constexpr int kTileMixed = 384;
 int choose_sym_tile(int64_t batch, int64_t rows) {
   const int64_t t256 = (rows + 255) / 256;
   return (t256 * (t256 + 1) / 2 * batch < 256 && rows <= 2048) ? 128 : 256;
+}
+
+// The Gram matrix contracts over the long side.  When its 256-edge upper
+// tiles over the batch fill at most half of the GPU's 256 compute units, its
+// contraction is cut into parts so that tiles x parts come close to one full
+// round (each part at least 2048 long); a second short pass adds the parts.
+// The 1024 selected rows of 8 x 4096x16384: 80 tiles, 3 parts.
+int choose_syrk_parts(int cdt, int64_t batch, int64_t Np256, int64_t Mp256) {
+  if (cdt != GNS_BF16 && cdt != GNS_F16) return 1;
+  const int64_t t = Np256 / 256;
+  const int64_t tiles = t * (t + 1) / 2 * batch;
+  if (tiles < 1 || tiles > 128) return 1;
+  int64_t parts = std::min<int64_t>(256 / tiles, 4);
+  parts = std::min<int64_t>(parts, Mp256 / 2048);
+  return parts >= 2 ? static_cast<int>(parts) : 1;
 }
 
 // tile_request: see kTileMixed.  Workspace sizes are quoted
@@ -142,6 +160,20 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
   for (int i = 0; i < n_square; ++i) {
     pl->off_sq[i] = off;
     off = align_up(off + sq, kAlign);
+  }
+  // room for a K split of the Gram matrix, from the 256-edge geometry (the
+  // same for every tile request, so that quoted sizes fit the size rule)
+  {
+    const int64_t Np256 = round_up(pl->r, 256), Mp256 = round_up(pl->c, 256);
+    pl->syrk_parts_room = pl->tall ? 1 : choose_syrk_parts(cdt, batch, Np256, Mp256);
+    pl->syrk_parts = (tile_request == 0 && pl->tile == 256) ? pl->syrk_parts_room : 1;
+    pl->off_part = off;
+    if (pl->syrk_parts_room > 1) {
+      const int64_t t = Np256 / 256;
+      off = align_up(off + sizeof(float) * static_cast<size_t>(pl->syrk_parts_room) * batch * (t * (t + 1) / 2) *
+                               256 * 256,
+                     kAlign);
+    }
   }
   pl->bytes = off;
   return true;
@@ -231,6 +263,12 @@ struct Ctx {
     return reinterpret_cast<double *>(ws + pl->off_partials) + b0 * pl->tile_parts;
   }
   float *inv() const { return reinterpret_cast<float *>(ws + pl->off_inv) + b0; }
+  // this sub-batch's partial Gram tiles: [parts][batch][tiles][256 * 256]
+  float *part() const {
+    const int64_t t = pl->Np / 256;
+    return reinterpret_cast<float *>(ws + pl->off_part) +
+           b0 * static_cast<int64_t>(pl->syrk_parts_room) * (t * (t + 1) / 2) * 256 * 256;
+  }
   float *inv2() const { return reinterpret_cast<float *>(ws + pl->off_inv) + pl->batch + b0; }
   // element offset from a hi plane to its lo plane (split storage only)
   int64_t plane_sq() const { return pl->planes == 2 ? pl->batch * sq_stride() : 0; }
@@ -335,7 +373,57 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
 // from the caller's X with 1/(||X||+eps)^2 applied in the epilogue.
 // xrow: the row-layout X to use instead of the normalised copy (the restarted
 // X of a K-major-B call lives in one of two row buffers).
+// The Gram matrix in two passes (see choose_syrk_parts): 256-edge tiles
+// over `parts` slices of the contraction write raw fp32 partial tiles, then a
+// pass with no contraction sums them in part order and runs the usual
+// epilogue (normalisation factor, rounding, mirror).
+gns_status syrk_split(const Ctx &c, void *R, bool from_input, const void *xrow) {
+  const int parts = c.pl->syrk_parts;
+  const int64_t N = c.pl->Np, M = c.pl->Mp;
+  const int nt = static_cast<int>(N / 256);
+  const bool direct = from_input && c.direct;
+  const void *Xh = direct ? c.xin : (xrow ? xrow : c.xh());
+  GemmParams p = base_params(c);
+  p.A = Xh; p.lda = M; p.sA = c.rect_stride();
+  p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
+  p.K = static_cast<int>(M);
+  p.tiles_m = p.tiles_n = nt;
+  p.tiles_per_mat = nt * (nt + 1) / 2;
+  p.sym_block = kSyrkBlock;
+  p.sym_half = kSyrkBand;
+  p.xcd_chunk = xcd_chunk(p.tiles_per_mat, c.batch * parts, 4);
+  p.k_parts = parts;
+  p.part_out = c.part();
+  const double n = static_cast<double>(c.pl->r), m = static_cast<double>(c.pl->c);
+  const double part_bytes = 4.0 * parts * c.batch * p.tiles_per_mat * 256.0 * 256.0;
+  {
+    LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, 256, gns::MODE_SYM), n * n * m * c.batch,
+                   c.batch * n * m * c.pl->esz + part_bytes);
+    const hipError_t e = gns::launch_gemm(c.cdt, 256, gns::MODE_SYM, p, c.s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  }
+  GemmParams q = base_params(c);
+  if (direct) q.alpha_vec = c.inv2();
+  q.K = 0;
+  q.tiles_m = q.tiles_n = nt;
+  q.tiles_per_mat = p.tiles_per_mat;
+  q.sym_block = kSyrkBlock;
+  q.sym_half = kSyrkBand;
+  q.xcd_chunk = xcd_chunk(q.tiles_per_mat, c.batch, 4);
+  q.part_in = c.part();
+  q.parts_in = parts;
+  q.C = R; q.ldc = N; q.sC = c.sq_stride();
+  q.pC = c.plane_sq();
+  LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, 256, gns::MODE_SYM), 0.0,
+                 part_bytes + c.batch * n * n * c.pl->esz);
+  const hipError_t e = gns::launch_gemm(c.cdt, 256, gns::MODE_SYM, q, c.s);
+  ls.done();
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
 gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow = nullptr) {
+  if (c.pl->syrk_parts > 1) return syrk_split(c, R, from_input, xrow);
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int nt = static_cast<int>(N / c.pl->sym_tile);

@@ -39,6 +39,16 @@ struct GemmParams {
   int tiles_per_mat;                // sym: tiles_m*(tiles_m+1)/2
   int sym_block, sym_half;          // sym: tile order (0 = column-major triangle;
                                     // else blocks of sym_block, bands of sym_half rows)
+  // K split of a symmetric result (256-edge 16-bit tiles): the first pass runs
+  // k_parts slices of K (grid = tiles x batch x k_parts; whole 32-element
+  // stages, the last part taking the remainder)
+  // and writes raw fp32 accumulators to part_out [k_parts][batch][tiles][256*256];
+  // the second pass (K = 0) starts from the sum of parts_in such parts in
+  // part_in and runs the normal epilogue.
+  int k_parts;
+  float *part_out;
+  const float *part_in;
+  int parts_in;
   int batch;
   int xcd_chunk;                    // tiles per run dealt to one XCD (see gemm_nt);
                                     // must divide (grid & ~7) / 8

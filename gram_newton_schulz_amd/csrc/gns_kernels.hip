@@ -280,7 +280,9 @@ __device__ __forceinline__ void sym_tile(int t, int nt, int bb, int hh, int *ti,
 // BK = 0: both operands row-major along K (C = A B^T).  BK = 1: B is stored
 // K-major, B[k][n] row-major with n contiguous (C = A B), read with the LDS
 // transpose load; 256-edge 16-bit tiles, general results only.
-template <class E, int TILE, int MODE, int PL, int BK = 0>
+// KS: 0 = one pass; K split of a symmetric result: 1 = a part's raw
+// accumulators out, 2 = sum of the parts in, then the usual epilogue.
+template <class E, int TILE, int MODE, int PL, int BK = 0, int KS = 0>
 __global__ void __launch_bounds__(WaveLayout<TILE>::THREADS)
 gemm_nt(GemmParams p) {
   using S = typename E::S;
@@ -307,6 +309,8 @@ gemm_nt(GemmParams p) {
   static_assert(BK == 0 || (TILE == 256 && ESZ == 2 && PL == 1 && NW == 8 && MODE != MODE_SYM),
                 "K-major B: 256-edge 16-bit tiles, general results");
   static_assert(NST * STB <= 160 * 1024, "LDS budget");
+  static_assert(KS == 0 || (MODE == MODE_SYM && TILE == 256 && ESZ == 2 && PL == 1 && NW == 8),
+                "K split: symmetric 256-edge 16-bit tiles");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STB];
 
@@ -321,7 +325,11 @@ gemm_nt(GemmParams p) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int G8 = G & ~7;
-  int mat, ti, tj;
+  int mat, ti, tj, t;
+  // K split (symmetric results): the grid holds k_parts copies of the tile
+  // set, part kp contracting over its own slice of K
+  const int kparts = KS == 1 ? p.k_parts : 1;
+  int kp = 0;
   {
     int lw = w;
     if (w < G8 && p.xcd_chunk > 0) {
@@ -329,8 +337,13 @@ gemm_nt(GemmParams p) {
       lw = ((slot / c) * 8 + (w & 7)) * c + slot % c;
       if (lw >= G8) lw = w;   // only when xcd_chunk does not divide G8 / 8 (a host error)
     }
+    if (kparts > 1) {
+      const int tb = p.tiles_per_mat * p.batch;
+      kp = lw / tb;
+      lw -= kp * tb;
+    }
     mat = lw / p.tiles_per_mat;
-    const int t = lw - mat * p.tiles_per_mat;
+    t = lw - mat * p.tiles_per_mat;
     if (MODE == MODE_SYM) {
       sym_tile(t, p.tiles_m, p.sym_block, p.sym_half, &ti, &tj);
     } else {
@@ -393,10 +406,13 @@ gemm_nt(GemmParams p) {
                      __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
     return r;
   };
-  const int64_t offA = static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda;
+  // K part kp: stages kp * base .. (the last part also takes the remainder)
+  const int kbase = (p.K / BKE) / kparts;
+  const int64_t kofs = static_cast<int64_t>(kp) * kbase * BKE;
+  const int64_t offA = static_cast<int64_t>(mat) * p.sA + static_cast<int64_t>(ti) * TILE * p.lda + kofs;
   // K-major B: the panel is columns tj*TILE .. of all K rows
   const int64_t offB = static_cast<int64_t>(mat) * p.sB +
-                       (BK ? static_cast<int64_t>(tj) * TILE : static_cast<int64_t>(tj) * TILE * p.ldb);
+                       (BK ? static_cast<int64_t>(tj) * TILE : static_cast<int64_t>(tj) * TILE * p.ldb + kofs);
   i32x4 rA[PL], rB[PL];
 #pragma unroll
   for (int pl = 0; pl < PL; ++pl) {
@@ -433,6 +449,30 @@ gemm_nt(GemmParams p) {
     for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // Second pass of a K split: the accumulators start as the sum of the
+  // parts' raw accumulators, added in part order (lane-major layout: element
+  // ((wave * NBI + ib) * NBJ + jb) * 16 + r of a tile at lane offset).
+  if constexpr (KS == 2) {
+    const int64_t tile_off = (static_cast<int64_t>(mat) * p.tiles_per_mat + t) * (TILE * TILE);
+    const int64_t part_stride = static_cast<int64_t>(p.tiles_per_mat) * p.batch * (TILE * TILE);
+#pragma unroll 1
+    for (int q = 0; q < p.parts_in; ++q) {
+      const float *src = p.part_in + q * part_stride + tile_off + (threadIdx.x >> 6) * (NBI * NBJ * 16 * 64) +
+                         (threadIdx.x & 63);
+#pragma unroll
+      for (int i = 0; i < NBI; ++i)
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) {
+          // one block at a time (keeps the loads from piling up in registers)
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = __builtin_nontemporal_load(src + ((i * NBJ + j) * 16 + r) * 64);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += v[r];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  }
   using RawD = typename std::conditional<ESZ == 2, uint2, float4>::type;
   RawD draw[PL][NBI][NBJ][4];
   const bool has_d = p.DT != nullptr;
@@ -537,7 +577,11 @@ gemm_nt(GemmParams p) {
   // Main loop over K stages of 64 bytes per row in an NST-deep LDS ring.
   // The loads bypass the compiler's wait bookkeeping (inline assembly), so
   // the waits are explicit counts of this wave's outstanding loads.
-  const int nk = p.K / BKE;
+  // (wave-uniform: the loop index feeds the scalar operands of the DMA)
+  // (the summing pass has no contraction: no main loop is compiled for it)
+  const int nk = KS == 2   ? 0
+                 : KS == 0 ? p.K / BKE
+                           : __builtin_amdgcn_readfirstlane(kp < kparts - 1 ? kbase : p.K / BKE - kbase * (kparts - 1));
   if (nk > 0) {
     using Frag = typename Mma<E>::Frag;
     auto dma_stage = [&](int stage) {
@@ -715,6 +759,20 @@ gemm_nt(GemmParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else if (has_d) {
     init_from_d();
+  }
+  // First pass of a K split: this part's raw accumulators go to part_out
+  // (the second pass sums the parts and runs the epilogue).
+  if constexpr (KS == 1) {
+    const int64_t tb = static_cast<int64_t>(p.tiles_per_mat) * p.batch;
+    float *dst = p.part_out + ((kp * tb + static_cast<int64_t>(mat) * p.tiles_per_mat + t) * (TILE * TILE)) +
+                 (threadIdx.x >> 6) * (NBI * NBJ * 16 * 64) + (threadIdx.x & 63);
+#pragma unroll
+    for (int i = 0; i < NBI; ++i)
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(acc[i][j][r], dst + ((i * NBJ + j) * 16 + r) * 64);
+    return;
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -1722,8 +1780,21 @@ dion3_update(float *W, float *M, const float *O, const int64_t *S, const double 
 // ---------------------------------------------------------------------------
 template <class E, int TILE, int PL = 1>
 static hipError_t launch_gemm_t(int mode, const GemmParams &p, hipStream_t s) {
-  const int grid = p.tiles_per_mat * p.batch;
+  const bool split1 = p.part_out != nullptr, split2 = p.part_in != nullptr;
+  const int grid = p.tiles_per_mat * p.batch * (split1 ? p.k_parts : 1);
   if (grid <= 0) return hipSuccess;
+  // a K split: symmetric results on the 256-edge 16-bit kernel, one pass at a time
+  if (split1 || split2) {
+    if (mode != MODE_SYM || TILE != 256 || PL != 1 || sizeof(typename E::S) != 2 || (split1 && split2) ||
+        (split1 && (p.k_parts < 1 || p.K / 32 < p.k_parts)) || (split2 && (p.parts_in < 1 || p.K != 0)))
+      return hipErrorInvalidValue;
+    if constexpr (TILE == 256 && PL == 1 && sizeof(typename E::S) == 2) {
+      constexpr int nt = WaveLayout<TILE>::THREADS;
+      if (split1) gemm_nt<E, TILE, MODE_SYM, PL, 0, 1><<<grid, nt, 0, s>>>(p);
+      else gemm_nt<E, TILE, MODE_SYM, PL, 0, 2><<<grid, nt, 0, s>>>(p);
+      return hipGetLastError();
+    }
+  }
   constexpr int nt = WaveLayout<TILE>::THREADS;
   if constexpr (TILE == 256 && PL == 1) {
     if (p.b_kmajor && mode != MODE_SYM) {

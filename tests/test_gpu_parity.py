@@ -571,3 +571,42 @@ def test_direct_input_path(algo, restarts, io, tile):
         errs = per_matrix_rel(synth.as_f64(out), ref)
         say("  T", len(co), "rel errs", errs)
         assert max(errs) <= TOL_HALF
+
+
+@pytest.mark.parametrize("case", ["bf16", "f32", "rows", "standard"])
+def test_gram_matrix_k_split(case):
+    """Few 256-edge Gram tiles and a long contraction (8 x 1024x6144: 80 upper
+    tiles over the batch): the size rule cuts the contraction into parts and a
+    second pass sums them.  Against the oracle (matrices 0 and 7), with the
+    direct input (bf16), the normalised copy (fp32 input), a row subset, and
+    standard NS; the launch records show the two passes."""
+    gns = need_gpu()
+    B, n, m = 8, 1024, 6144
+    io = "f32" if case == "f32" else "bf16"
+    rows_n = 2048 if case == "rows" else n
+    X, X64 = _inputs(B, rows_n, m, io, seed=43)
+    kw = {}
+    rows = None
+    if case == "rows":
+        rows = np.stack([np.sort(synth.row_subset(rows_n, n, seed=43, index=b)) for b in range(B)])
+        kw = dict(row_idx=torch.from_numpy(rows).cuda(), out=torch.zeros(B, rows_n, m, dtype=X.dtype, device="cuda"))
+    say(f"k split {case}")
+    gns.timing_reset()
+    gns.timing_enable(True)
+    if case == "standard":
+        out = gns.standard_ns_batched(X.cuda(), NS5, compute_dtype=torch.bfloat16)
+    else:
+        out = gns.gram_ns_batched(X.cuda(), NS5, compute_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    recs = gns.timing_read()
+    gns.timing_enable(False)
+    grams = 5 if case == "standard" else 2          # Gram matrices formed per call
+    parts_pass = [r for r in recs if r[0] == "syrk" and r[2] > 0]
+    sum_pass = [r for r in recs if r[0] == "syrk" and r[2] == 0]
+    # each stream of the batch fan-out forms its own Gram matrices, in two passes each
+    assert len(parts_pass) == len(sum_pass) and len(parts_pass) in (grams, 2 * grams)
+    got = synth.as_f64(out)
+    for b in (0, B - 1):
+        sel = rows[b] if case == "rows" else np.arange(n)
+        ref = (oracle_standard if case == "standard" else oracle_gram)(X64[b][sel])
+        assert rel_err(got[b][sel], ref) <= TOL_HALF
