@@ -53,17 +53,21 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 def short_kernel(name):
     """rocprofv3 kernel name -> the library's short name, e.g.
-    'gns::gemm_nt<gns::EBF16, 256, 0, 1, 0>' -> 'gemm_nt<bf16,256,sym>'.  The
-    fourth template argument is the plane count (2 means split bf16,
-    'bf16x3'); a fifth argument of 1 marks the K-major-B product, 'gemm_nn'."""
+    'gns::gemm_nt<gns::EBF16, 256, 0, 1, 0, 0>' -> 'gemm_nt<bf16,256,sym>'.
+    The fourth template argument is the plane count (2 means split bf16,
+    'bf16x3'); a fifth argument of 1 marks the K-major-B product, 'gemm_nn';
+    a sixth of 1 or 2 marks the two passes of a K-split Gram matrix
+    ('sym_kpart', 'sym_ksum')."""
     import re
-    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)(?:, (\d))?(?:, (\d))?>", name)
+    m = re.search(r"gemm_nt<gns::E(\w+), (\d+), (\d)(?:, (\d))?(?:, (\d))?(?:, (\d))?>", name)
     if m:
         dt = m.group(1).lower()
         if m.group(4) == "2":
             dt = "bf16x3"
         kind = "gemm_nn" if m.group(5) == "1" else "gemm_nt"
-        return f"{kind}<{dt},{m.group(2)},{['sym', 'gen', 'final'][int(m.group(3))]}>"
+        mode = ['sym', 'gen', 'final'][int(m.group(3))]
+        mode += {"1": "_kpart", "2": "_ksum"}.get(m.group(6) or "0", "")
+        return f"{kind}<{dt},{m.group(2)},{mode}>"
     for k in ("norm_partial", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish", "row_l1",
               "select_topk", "check_rows", "momentum_l1", "row_sumsq", "normuon_factors",
               "dion3_update"):
