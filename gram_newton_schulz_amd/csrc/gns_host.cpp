@@ -929,7 +929,9 @@ bool dion3_layout(int cdt, int64_t batch, int64_t n, int64_t m, int64_t k, Dion3
 
 // ---------------------------------------------------------------- autotune
 // Shape-keyed table of measured tile choices (GNS_OPT_TILE_AUTOTUNE); the
-// value is the TILE option bit that won.
+// value is the TILE option bit that won, or kRuleChoice for the size rule's
+// own plan (which alone may also split the Gram matrix along K).
+constexpr unsigned kRuleChoice = 0x80000000u;
 struct TuneKey {
   int standard, cdt, io;
   int64_t batch, rows, m;
@@ -959,7 +961,7 @@ void keep_choice(const TuneKey &key, unsigned bit) {
 template <class Run>
 gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
   const unsigned kept = tuned_choice(key);
-  if (kept) return run(kept);
+  if (kept) return run(kept == kRuleChoice ? 0u : kept);
   if (key.cdt == GNS_F32 || key.cdt == GNS_BF16X3) {   // one tile edge only
     const gns_status st = run(GNS_OPT_TILE_128);
     if (st == GNS_OK) keep_choice(key, GNS_OPT_TILE_128);
@@ -973,15 +975,15 @@ gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
     if (ev[0]) (void)hipEventDestroy(ev[0]);
     return GNS_E_HIP;
   }
-  constexpr int kChoices = 3;
-  const unsigned bits[kChoices] = {GNS_OPT_TILE_128, GNS_OPT_TILE_256, GNS_OPT_TILE_MIXED};
-  float best[kChoices] = {INFINITY, INFINITY, INFINITY};
+  constexpr int kChoices = 4;
+  const unsigned bits[kChoices] = {GNS_OPT_TILE_128, GNS_OPT_TILE_256, GNS_OPT_TILE_MIXED, kRuleChoice};
+  float best[kChoices] = {INFINITY, INFINITY, INFINITY, INFINITY};
   gns_status st = GNS_OK;
   for (int rep = 0; rep < 2 && st == GNS_OK; ++rep)
     for (int i = 0; i < kChoices && st == GNS_OK; ++i) {
       float ms = 0.0f;
       if (hipEventRecord(ev[0], s) != hipSuccess) { st = GNS_E_HIP; break; }
-      if ((st = run(bits[i])) != GNS_OK) break;
+      if ((st = run(bits[i] == kRuleChoice ? 0u : bits[i])) != GNS_OK) break;
       if (hipEventRecord(ev[1], s) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
           hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
         st = GNS_E_HIP;
@@ -996,7 +998,7 @@ gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
   for (int i = 1; i < kChoices; ++i)
     if (best[i] < best[win]) win = i;
   // the last run used the last choice: leave the winner's result in the output
-  if (win != kChoices - 1 && (st = run(bits[win])) != GNS_OK) return st;
+  if (win != kChoices - 1 && (st = run(bits[win] == kRuleChoice ? 0u : bits[win])) != GNS_OK) return st;
   keep_choice(key, bits[win]);
   return GNS_OK;
 }
@@ -1136,8 +1138,14 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
 int gns_tuned_tile(int standard, gns_dtype cdt, gns_dtype io, int64_t batch, int64_t rows, int64_t m,
                    int *sym_edge) {
   const unsigned bit = tuned_choice(TuneKey{standard ? 1 : 0, cdt, io, batch, rows, m});
-  const int rect = bit == GNS_OPT_TILE_128 ? 128 : bit ? 256 : 0;
-  if (sym_edge) *sym_edge = bit == GNS_OPT_TILE_256 ? 256 : bit ? 128 : 0;
+  int rect = bit == GNS_OPT_TILE_128 ? 128 : bit ? 256 : 0;
+  int sym = bit == GNS_OPT_TILE_256 ? 256 : bit ? 128 : 0;
+  Plan pl;
+  if (bit == kRuleChoice && make_plan(cdt, batch, rows, m, standard ? 2 : 5, 0, &pl)) {
+    rect = pl.tile;
+    sym = pl.sym_tile;
+  }
+  if (sym_edge) *sym_edge = sym;
   return rect;
 }
 

@@ -294,8 +294,9 @@ gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, i
  * GNS_OPT_TILE_AUTOTUNE, the first call of a shape -- entry point, compute
  * and I/O dtypes, batch, rows (k with a row subset, else n) and m -- runs
  * the whole call with each tile choice (128-edge, 256-edge and mixed tiles,
- * see GNS_OPT_TILE_MIXED), twice each, on `stream` and blocks the host until
- * they end; the choice with the smallest time is kept in a process-wide
+ * see GNS_OPT_TILE_MIXED, and the size rule's own plan, which alone may also
+ * cut a small Gram matrix into parts along its contraction), twice each, on
+ * `stream` and blocks the host until they end; the choice with the smallest time is kept in a process-wide
  * table, and the caller's `out` holds the result of a run with that choice.
  * Later calls of the shape run the kept choice with no timing.  fp32 and
  * split-bf16 compute have one choice (128) and are never timed.  While

@@ -36,6 +36,8 @@ def test_autotune_keeps_an_edge_and_matches_it(algo):
     edge = gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m, standard=std)
     sym = gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m, standard=std, symmetric=True)
     assert (edge, sym) in ((128, 128), (256, 256), (256, 128))
+    # (this shape is too small for a K split, so every choice, the size rule's
+    # plan included, is one of the three forced ones)
     choice = "mixed" if (edge, sym) == (256, 128) else edge
     # the other entry point's table entry is separate
     assert gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m, standard=not std) == 0
@@ -120,4 +122,24 @@ def test_autotune_under_capture_runs_size_choice():
         torch.cuda.synchronize()
         assert torch.equal(static_out, eager), f"replay {rep}"
         _ = (static_out.float() * 2).sum().item()    # eager work between replays
+    gns.autotune_clear()
+
+
+def test_autotune_can_keep_the_size_rule_plan():
+    """On a shape where the size rule splits the Gram matrix along its
+    contraction (8 x 1024x6144), autotuning also times that plan; whatever it
+    keeps, later calls reproduce the first call's result and match the oracle."""
+    gns = need_gpu()
+    B, n, m = 8, 1024, 6144
+    X, X64 = _inputs(B, n, m, torch.bfloat16, seed=55)
+    Xd = X.cuda()
+    gns.autotune_clear()
+    say("autotune with the size rule's plan as a candidate")
+    first = gns.gram_ns_batched(Xd, NS5, tile="auto")
+    again = gns.gram_ns_batched(Xd, NS5, tile="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(first, again)
+    assert gns.tuned_tile(torch.bfloat16, torch.bfloat16, B, n, m) in (128, 256)
+    for b in (0, B - 1):
+        assert per_matrix_rel(first[b:b + 1].double().cpu().numpy(), oracle_gram(X64[b])[None])[0] < TOL_HALF
     gns.autotune_clear()
