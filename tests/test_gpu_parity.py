@@ -610,3 +610,33 @@ def test_gram_matrix_k_split(case):
         sel = rows[b] if case == "rows" else np.arange(n)
         ref = (oracle_standard if case == "standard" else oracle_gram)(X64[b][sel])
         assert rel_err(got[b][sel], ref) <= TOL_HALF
+
+
+def test_gram_matrix_k_split_graph_replay():
+    """The two passes of a K-split Gram matrix captured in a HIP graph: every
+    replay equals the eager call bit for bit (8 x 1024x6144)."""
+    gns = need_gpu()
+    B, n, m = 8, 1024, 6144
+    X, _ = _inputs(B, n, m, "bf16", seed=44)
+    Xd = X.cuda()
+    static_out = torch.empty_like(Xd)
+    ws = torch.empty(gns.gram_workspace_bytes(torch.bfloat16, B, n, m), dtype=torch.uint8, device="cuda")
+    eager = gns.gram_ns_batched(Xd, NS5)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                        # warm up on the capture stream
+        gns.gram_ns_batched(Xd, NS5, out=static_out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    say("k split graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gns.gram_ns_batched(Xd, NS5, out=static_out, workspace=ws, stream=torch.cuda.current_stream())
+    for rep in range(3):
+        static_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(static_out, eager), f"replay {rep}"
+        _ = (static_out.float() * 2).sum().item()    # eager work between replays
