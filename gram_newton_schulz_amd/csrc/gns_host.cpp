@@ -1071,7 +1071,7 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
                     });
   // Square matrices: both algorithms cost the same and standard NS needs
   // fewer launches and never forms X X^T of an ill-conditioned square
-  // matrix, so the pages fall back to it (Dion3 §4.1, last paragraph).
+  // matrix, so Dion3 falls back to it (§4.1, last paragraph).
   const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
   hipStream_t caller = static_cast<hipStream_t>(stream);
   const bool direct = direct_input(pl, X, io, cdt, row_idx);

@@ -7,7 +7,7 @@ single batch member can be regenerated on its own), normalised in float64
 where the workload says so, and rounded once to the storage dtype.  That
 rounded tensor is *the* input: the oracle upcasts the same bits.
 
-Workloads (shapes of the pages' dense-MLP and MoE-expert weights):
+Workloads (dense-MLP and MoE-expert weight shapes):
 
 1. 1 x 64x256 fp32, i.i.d. N(0,1), unit Frobenius norm.
 2. 16 x 1024x4096 bf16, U diag(s) V^T with Haar U, V and s log-uniform in
@@ -29,7 +29,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-# Coefficient schedules printed on the pages.
+# Coefficient schedules printed in the sources.
 #: Five iterations of the fixed Muon quintic (a, b, c) = (3.4445, -4.7750,
 #: 2.0315), as used by "Scaling Muon for Diffusion Transformers" (App. D.3).
 NS5_MUON = [(3.4445, -4.7750, 2.0315)] * 5

@@ -146,7 +146,7 @@ size_t gns_standard_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int6
  *              element is written.  With a row subset only the selected rows
  *              are written; the others keep what the caller put there.
  *   batch      number of matrices (>= 0).
- *   n, m       matrix shape (n, m >= 1).  The pages take rows <= m without
+ *   n, m       matrix shape (n, m >= 1).  Dion3 (§2) takes rows <= m without
  *              loss of generality; a tall problem (rows > m, rows = n or k)
  *              is orthogonalised through its transpose, polar(X) =
  *              polar(X^T)^T: the iteration runs on m x m Gram matrices of
@@ -167,7 +167,7 @@ size_t gns_standard_workspace_bytes(gns_dtype compute_dtype, int64_t batch, int6
  *   restart_after (host) n_restart iterations s, strictly increasing, each in
  *              [1, T-1]: before iteration s+1 the input is replaced by
  *              Q_s X, R is re-formed from it and Q is reset to I (Dion3
- *              §4.2; the pages' default is {2} for T = 5).  May be NULL when
+ *              §4.2; its default is {2} for T = 5).  May be NULL when
  *              n_restart == 0.
  *   row_idx    (device) [batch][k] int64 or NULL.  When given, rows
  *              row_idx[b][0..k) of X_b form one k x m matrix, normalised by
@@ -210,7 +210,7 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
  * §6, Algorithm 4, selection step): for every matrix M_b, the indices of the
  * k rows with the largest l1 norm sum_j |M_b[i][j]|, written to
  * row_idx[b][0..k) in ascending order, ready for gns_gram_batched's row
- * subset.  The pages take k = ceil(f n) for a fraction f in (0, 1].
+ * subset.  Dion3 (§6, Algorithm 4) takes k = ceil(f n) for a fraction f in (0, 1].
  *   M          (device) [batch][n][m] in dtype (GNS_F32, GNS_BF16, GNS_F16).
  *   row_idx    (device) [batch][k] int64, written.
  *   workspace  (device) >= gns_select_workspace_bytes(batch, n) bytes,

@@ -32,10 +32,10 @@ Arithmetic is float64 numpy (BLAS matmul) for float inputs.  For inputs of
 dtype ``object`` holding ``fractions.Fraction`` the very same code runs in
 exact rational arithmetic; the Frobenius norm then must be rational (the
 square root is taken exactly), which is how the tests pin the algebra
-bit-exactly.  The pages run these iterations in half precision; the oracle
+bit-exactly.  Dion3 runs these iterations in half precision; the oracle
 deliberately does not emulate any rounding.
 
-Reading of the pages taken here (each also listed in the design notes):
+Readings of the sources taken here (each also listed in the design notes):
 * normalisation is X / (||X||_F + eps) with eps = 1e-7 added to the norm;
 * "restart after iteration s" means: before computing Z_{s+1}, replace X by
   Q_s X, re-form R from it and reset Q to I (X is not renormalised);
@@ -49,7 +49,7 @@ Reading of the pages taken here (each also listed in the design notes):
 * the one stored value the selection reads, the momentum sum M + G, is
   formed as an fp32 addition, as the caller's fp32 buffer holds it; all
   later steps are fp64;
-* the pages take n <= m without loss of generality; a tall X (n > m) is
+* Dion3 (§2) takes n <= m without loss of generality; a tall X (n > m) is
   orthogonalised through its transpose: the iteration runs on X^T and the
   result is transposed back (polar(X) = polar(X^T)^T, and each odd
   polynomial step commutes with transposition).
@@ -277,7 +277,7 @@ def dion3_select(M, k: int) -> np.ndarray:
 
     A row's norm is the exact sum of |M_ij| rounded once to float64
     (math.fsum).  Rows with equal norms are taken in index order, the smaller
-    index first (the pages do not say how ties break).
+    index first (Dion3's Algorithm 4 does not say how ties break).
     """
     M = np.asarray(M, dtype=np.float64)
     n = M.shape[0]
@@ -330,7 +330,7 @@ def dion3_step(W, G, M, v, k: int, coeffs, restarts=(2,), lr=0.02, weight_decay=
     3. O = Gram Newton-Schulz of the k x m submatrix of those rows;
     4. NorMuon: v_i <- beta2 v_i + (1 - beta2) mean_j O_ij^2 for i in S,
        O_ij <- O_ij / (sqrt(v_i) + eps), then O is rescaled to the Frobenius
-       norm it had before that division (a zero O stays zero: the pages'
+       norm it had before that division (a zero O stays zero: Algorithm 4's
        ratio is 0/0 there);
     5. weight decay on every row: W <- (1 - lr * weight_decay) W;
     6. the selected rows move: W[S] <- W[S] - lr * O;

@@ -1,4 +1,4 @@
-"""Pins that tie the fp64 oracle to what the pages and the mathematics fix.
+"""Pins that tie the fp64 oracle to what the sources and the mathematics fix.
 
 Each ``pin_*`` takes the oracle module and raises AssertionError (or any
 exception) when the oracle disagrees with something independent of it:

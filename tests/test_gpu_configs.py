@@ -15,7 +15,7 @@ def test_config2_logspectrum():
     """16 x 1024x4096, singular values log-uniform in [1e-4, 1].  Forming X X^T
     squares the condition number, so plain bf16 products lose the small
     singular values; the split-bf16 compute type (hi/lo bf16 pairs, three
-    bf16 MFMAs per product) and fp16 products (the pages' default precision)
+    bf16 MFMAs per product) and fp16 products (Dion3's default precision, Algorithm 3)
     keep the error within the bound."""
     gns = need_gpu()
     X = synth.workload_batch(2)

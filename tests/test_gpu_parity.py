@@ -82,7 +82,7 @@ def test_restart_sets_fp32(restarts):
 @pytest.mark.parametrize("cdt", ["bf16", "f16"])
 @pytest.mark.parametrize("restarts", [(1,), (2,), (3,), (4,), (1, 3)])
 def test_restart_location_sweep_half(cdt, restarts):
-    """Where the restart goes (the pages sweep it in half precision): every
+    """Where the restart goes (Dion3 sweeps it in half precision): every
     location of a single restart, and two restarts, on 256-edge tiles, against
     the oracle with the same restart set."""
     gns = need_gpu()
@@ -511,10 +511,9 @@ def test_tall_mlp_down_projection():
 
 @pytest.mark.parametrize("split", [True, False])
 def test_graph_capture_replays(split):
-    """The whole call captured into a HIP graph (the pages replay the full
-    optimizer step as a graph) and replayed several times, with eager work
-    and synchronisations between replays: every replay equals the eager
-    result bit for bit.  The library enqueues no memset and no allocation,
+    """The whole call captured into a HIP graph and replayed several times,
+    with eager work and synchronisations between replays: every replay
+    equals the eager result bit for bit.  The library enqueues no memset and no allocation,
     and its two-stream fan-out is captured through its fork/join events."""
     gns = need_gpu()
     B, n, m = 4, 300, 700

@@ -48,7 +48,7 @@ def test_select_ragged_and_ties(dt):
 
 
 def test_select_then_orthogonalise():
-    """The whole Dion3 orthogonalisation of the pages' Algorithm 4 (select
+    """The whole Dion3 orthogonalisation of Algorithm 4 (select
     the top rows, orthogonalise them as one k x m matrix, write them back)
     against the oracle's selection and row update."""
     gns = need_gpu()
