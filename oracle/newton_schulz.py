@@ -27,6 +27,12 @@ Every routine follows the written description in
                        eq. (2), weight decay, update of the selected rows,
                        error feedback).
 * ``flops_*``       -- §2.2 and §4.1 FLOP models, §4.2 restart surcharge.
+* ``restart_model``, ``restart_sweep``
+                    -- Appendix B.2.1: the scalar model of Gram Newton-Schulz
+                       on every eigen-direction of R_0, with spurious negative
+                       eigenvalues and a corruption at every re-formed R, and
+                       the sweep over restart schedules that keeps the
+                       condition number of Q_t smallest.
 
 Arithmetic is float64 numpy (BLAS matmul) for float inputs.  For inputs of
 dtype ``object`` holding ``fractions.Fraction`` the very same code runs in
@@ -56,6 +62,7 @@ Readings of the sources taken here (each also listed in the design notes):
 """
 from __future__ import annotations
 
+import itertools
 import math
 from fractions import Fraction
 from typing import Iterable, Sequence
@@ -67,7 +74,7 @@ EPS = 1e-7
 __all__ = [
     "EPS", "frobenius_normalize", "standard_ns", "gram_ns", "theorem2_q",
     "composed_poly", "spectral_map", "polar", "dion3_select", "dion3_rows", "dion3_step",
-    "flops_standard", "flops_gram", "gram_ns_trace",
+    "flops_standard", "flops_gram", "gram_ns_trace", "restart_model", "restart_sweep",
 ]
 
 
@@ -373,3 +380,76 @@ def flops_gram(n: int, m: int, T: int, n_restarts: int) -> float:
     (3n^3), i.e. +3(alpha-1) n^3 (§4.2)."""
     base = T * 4.0 * n ** 3 + 3.0 * m * n * n - 3.0 * n ** 3
     return base + n_restarts * (3.0 * m * n * n - 3.0 * n ** 3)
+
+
+# --------------------------------------------------------------------------
+# Where to restart (Appendix B.2.1)
+# --------------------------------------------------------------------------
+def restart_model(coeffs, restarts: Iterable[int], r0, r_min: float = -4e-4):
+    """Gram Newton-Schulz on one eigen-direction at a time (Appendix B.2.1).
+
+    R_0, Q_t and R_t share eigenvectors in exact arithmetic (Theorem 2), so
+    each eigenvalue r_0 of R_0 evolves on its own: z_t = h_t(r_{t-1}),
+    q_t = q_{t-1} z_t, r_t = r_{t-1} z_t^2.  r0 holds eigenvalues of R_0 in
+    [r_min, 1]; a negative one is spurious (Appendix B.1.2): its direction
+    has singular value 0, so the input component is x_0 = sqrt(max(r_0, 0)).
+    A restart before iteration t (t - 1 in ``restarts``) replaces X by Q X
+    (x <- q x), re-forms R = X X^T with r_min added to every eigenvalue (the
+    pages subtract 4e-4 I to model rounding at each re-formation), and resets
+    Q to I.  The last R update is not needed and not taken.
+
+    Returns (r_trace, q_trace, x_T): r_trace lists R's eigenvalues as each
+    R is formed or updated (R_0, re-formed R's, R_1 .. R_{T-1} unless a
+    restart replaces them), q_trace lists Q_1 .. Q_T, and x_T = q_T x is the
+    output's singular value for each direction."""
+    co = [tuple(float(v) for v in row) for row in coeffs]
+    T = len(co)
+    rs = set(int(s) for s in restarts)
+    r = np.asarray(r0, dtype=np.float64).copy()
+    x = np.sqrt(np.maximum(r, 0.0))
+    q = np.ones_like(r)
+    r_trace, q_trace = [r.copy()], []
+    for t in range(1, T + 1):
+        if (t - 1) in rs:
+            x = q * x
+            r = x * x + r_min
+            q = np.ones_like(r)
+            r_trace.append(r.copy())
+        a, b, c = co[t - 1]
+        z = a + b * r + c * r * r
+        q = q * z
+        q_trace.append(q.copy())
+        if t < T and t not in rs:
+            r = r * (z * z)
+            r_trace.append(r.copy())
+    return r_trace, q_trace, q * x
+
+
+def restart_sweep(coeffs, n_restarts: int = 1, r_min: float = -4e-4, points: int = 20001):
+    """The restart-schedule sweep of Appendix B.2.1: for every set of
+    ``n_restarts`` restart iterations in [1, T-1], run :func:`restart_model`
+    on a uniform grid of R_0 eigenvalues over [r_min, 1] and record the
+    largest condition number of Q_t over t (max |q_t| / min |q_t| over the
+    grid), the largest |q_t| and the smallest eigenvalue of any R.  Returns
+    (best, rows): rows holds one dict per schedule in lexicographic order,
+    best is the schedule with the smallest largest condition number (the
+    pages' choice rule)."""
+    T = len(coeffs)
+    grid = np.linspace(r_min, 1.0, points)
+    rows = []
+    def cond(q):          # an overflowed or singular Q counts as unbounded
+        aq = np.abs(q)
+        if not np.all(np.isfinite(aq)) or np.min(aq) == 0.0:
+            return math.inf
+        return float(np.max(aq) / np.min(aq))
+
+    with np.errstate(over="ignore", invalid="ignore"):
+        for sched in itertools.combinations(range(1, T), n_restarts):
+            r_trace, q_trace, _ = restart_model(coeffs, sched, grid, r_min)
+            rows.append({"restarts": tuple(sched), "max_cond_q": max(cond(q) for q in q_trace),
+                         "max_q": max(float(np.max(np.abs(q))) if np.all(np.isfinite(q)) else math.inf
+                                      for q in q_trace),
+                         "min_r": min(float(np.min(r)) if np.all(np.isfinite(r)) else -math.inf
+                                      for r in r_trace)})
+    best = min(rows, key=lambda d: d["max_cond_q"])["restarts"]
+    return best, rows

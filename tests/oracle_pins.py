@@ -384,6 +384,74 @@ def pin_dion3_step(O):
     assert not r["M"].any()
 
 
+# ---------------------------------------------------------------------------
+# Where to restart: the scalar model and sweep of Dion3 App. B.2.1
+# ---------------------------------------------------------------------------
+def pin_restart_sweep(O):
+    sched = load_schedules()
+    ns5 = [tuple(float(v) for v in sched["muon_ns5"])] * 5
+    stab = [tuple(float(v) for v in sched["convergent"])]
+    # (a) no corruption and no spurious eigenvalue: restarts are exact, so the
+    # output singular value is phi(x_0) whatever the schedule (Theorem 2)
+    x0 = np.linspace(0.0, 1.0, 401)
+    for rs in ((), (1,), (2,), (1, 3), (4,)):
+        _, q_trace, xT = O.restart_model(ns5, rs, x0 * x0, r_min=0.0)
+        assert len(q_trace) == 5
+        assert np.max(np.abs(xT - _phi(ns5)(x0))) <= 1e-12
+    # (b) a spurious negative eigenvalue grows by at least (15/8)^2 per step
+    # under h(x) = 15/8 - 10/8 x + 3/8 x^2 (App. B.1.2), never restarted
+    r_trace, _, _ = O.restart_model(stab * 6, (), np.array([-4e-4, -1e-6]), r_min=-4e-4)
+    for r_prev, r_next in zip(r_trace[:-1], r_trace[1:]):
+        assert np.all(r_next < 0) and np.all(r_next / r_prev >= (15 / 8) ** 2)
+    # (c) the 10-step study of App. B.2 restarts after step 5 (Figs. 16-17);
+    # for a constant schedule the sweep puts one restart in the middle and
+    # two restarts of 15 steps after 5 and 10
+    assert O.restart_sweep(stab * 10, 1, points=2001)[0] == (5,)
+    assert O.restart_sweep(stab * 15, 2, points=2001)[0] == (5, 10)
+    # (d) App. B.2.1, Fig. 18: without a restart the printed quintic blows up
+    # from R_0's -4e-4; one restart after iteration 2 keeps every eigenvalue
+    # of R above -0.4 and of Q below 100, a restart after 1 or 4 does not
+    _, none = O.restart_sweep(ns5, 0)
+    assert none[0]["restarts"] == () and none[0]["max_cond_q"] > 1e6 and none[0]["min_r"] < -10
+    best, rows = O.restart_sweep(ns5, 1)
+    by = {r["restarts"]: r for r in rows}
+    assert sorted(by) == [(1,), (2,), (3,), (4,)]
+    assert by[(2,)]["min_r"] > -0.4 and by[(2,)]["max_q"] < 100
+    for bad in ((1,), (4,)):
+        assert by[bad]["min_r"] < -0.4 or by[bad]["max_q"] > 100
+    assert by[best]["max_cond_q"] == min(r["max_cond_q"] for r in rows)
+    # without corruption the condition numbers follow from Theorem 2 alone:
+    # q_t = phi_t(x_0) / x_0 on every direction, (a_1 ... a_t) at x_0 = 0
+    pts = 2001
+    _, rows0 = O.restart_sweep(ns5, 0, r_min=0.0, points=pts)
+    xs = np.sqrt(np.linspace(0.0, 1.0, pts))
+    want = 0.0
+    for t in range(1, 6):
+        with np.errstate(invalid="ignore", divide="ignore"):
+            qt = _phi(ns5[:t])(xs) / xs
+        qt[0] = np.prod([c[0] for c in ns5[:t]])
+        want = max(want, np.max(np.abs(qt)) / np.min(np.abs(qt)))
+    assert abs(rows0[0]["max_cond_q"] / want - 1.0) <= 1e-9
+    # ... and after an exact restart after 2, Q restarts from I on x_2 =
+    # phi_2(x_0): q_t = phi_t(x_0) / phi_2(x_0) for t > 2 (its smallest value
+    # lies inside the grid, where x_2^2 reaches the vertex of h)
+    _, rows2 = O.restart_sweep(ns5, 1, r_min=0.0, points=pts)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        qs = [_phi(ns5[:t])(xs) / xs for t in (1, 2)]
+        qs += [_phi(ns5[:t])(xs) / _phi(ns5[:2])(xs) for t in (3, 4, 5)]
+    qs[0][0], qs[1][0] = ns5[0][0], ns5[0][0] * ns5[1][0]
+    for i, t in enumerate((3, 4, 5)):
+        qs[2 + i][0] = np.prod([c[0] for c in ns5[2:t]])
+    want2 = max(np.max(np.abs(q)) / np.min(np.abs(q)) for q in qs)
+    assert 0 < np.argmin(np.abs(qs[2])) < pts - 1
+    assert abs([r for r in rows2 if r["restarts"] == (2,)][0]["max_cond_q"] / want2 - 1.0) <= 1e-9
+    # the re-formed R's smallest eigenvalue is the corruption itself (the
+    # zero directions of X stay zero)
+    r_trace, _, _ = O.restart_model(ns5, (2,), np.array([-4e-4, 0.25, 1.0]))
+    assert len(r_trace) == 5 and r_trace[2][0] == -4e-4 and r_trace[2][2] > 0
+
+
 FAST_PINS = [pin_exact_equivalence, pin_restart_semantics, pin_rank_one_exact, pin_theorem2, pin_spectral,
-             pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3, pin_dion3_select, pin_dion3_step]
+             pin_polar_limit, pin_flop_model, pin_invariants, pin_dion3, pin_dion3_select, pin_dion3_step,
+             pin_restart_sweep]
 ALL_PINS = FAST_PINS + [pin_exact_equivalence_t4]

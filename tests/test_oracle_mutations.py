@@ -54,6 +54,12 @@ MUTATIONS = {
                                     "W_new = W.copy()\n    W_new[S, :] *= 1.0 - lr * weight_decay\n"),
     "update sign": ("W_new[S, :] -= lr * O", "W_new[S, :] += lr * O"),
     "error feedback on every row": ("M_new[S, :] *= momentum", "M_new *= momentum"),
+    "sweep drops the corruption": ("r = x * x + r_min", "r = x * x"),
+    "sweep restart forgets Q": ("            x = q * x\n", "            x = x\n"),
+    "sweep R update not squared": ("r = r * (z * z)", "r = r * z"),
+    "sweep picks the worst": ("best = min(rows, key=", "best = max(rows, key="),
+    "sweep condition from one end": ("return float(np.max(aq) / np.min(aq))", "return float(np.max(aq) / aq[-1])"),
+    "sweep spurious direction kept": ("x = np.sqrt(np.maximum(r, 0.0))", "x = np.sqrt(np.abs(r))"),
 }
 
 
