@@ -54,6 +54,7 @@ struct Plan {
   int64_t tile_parts = 0;              // 128x128 tiles per matrix (direct input path)
   size_t off_sq[5] = {0, 0, 0, 0, 0};  // R, Z, RZ, Q0, Q1 (standard NS: A, B)
   size_t off_part = 0;                 // fp32 partial Gram tiles of a K split
+  size_t off_flag = 0;                 // int32 result of the debug checks
   size_t bytes = 0;
 };
 
@@ -175,6 +176,8 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
                      kAlign);
     }
   }
+  pl->off_flag = off;
+  off = align_up(off + sizeof(int32_t), kAlign);
   pl->bytes = off;
   return true;
 }
@@ -241,6 +244,12 @@ struct Ctx {
   // that read it apply 1/(||X||_F + eps) per matrix in their epilogues.
   bool direct = false;
   const void *xin = nullptr;           // this sub-batch's X
+  // In-place calls (out is X) on the direct path whose final product would
+  // read X: the input pass also copies X row-major into the workspace
+  // (xcopy), and every later product reads that copy, so that no product
+  // reads X while the final one writes it.  Null otherwise.
+  void *xcopy = nullptr;
+  const void *xsrc() const { return xcopy ? xcopy : xin; }
   // The rectangular products of Gram NS read X row-major (K-major B operand,
   // LDS transpose reads), so no transposed copy of X is written.
   bool nn = false;
@@ -382,7 +391,7 @@ gns_status syrk_split(const Ctx &c, void *R, bool from_input, const void *xrow) 
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int nt = static_cast<int>(N / 256);
   const bool direct = from_input && c.direct;
-  const void *Xh = direct ? c.xin : (xrow ? xrow : c.xh());
+  const void *Xh = direct ? c.xsrc() : (xrow ? xrow : c.xh());
   GemmParams p = base_params(c);
   p.A = Xh; p.lda = M; p.sA = c.rect_stride();
   p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
@@ -428,7 +437,7 @@ gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow
   const int64_t N = c.pl->Np, M = c.pl->Mp;
   const int nt = static_cast<int>(N / c.pl->sym_tile);
   const bool direct = from_input && c.direct;
-  const void *Xh = direct ? c.xin : (xrow ? xrow : c.xh());
+  const void *Xh = direct ? c.xsrc() : (xrow ? xrow : c.xh());
   if (direct) p.alpha_vec = c.inv2();
   p.A = Xh; p.lda = M; p.sA = c.rect_stride();
   p.B = Xh; p.ldb = M; p.sB = c.rect_stride();
@@ -546,9 +555,10 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
   if (c.direct) {
     {
       LaunchScope ls(c.s, "transpose_sumsq", "transpose_sumsq", 2.0 * rows * m * c.batch,
-                     c.batch * rows * m * (c.nn ? 1.0 : 2.0) * gns::dtype_size(io));
+                     c.batch * rows * m * (c.nn ? 1.0 : 2.0) * gns::dtype_size(io) +
+                         (c.xcopy ? c.batch * rows * m * gns::dtype_size(io) : 0.0));
       hipError_t e = gns::launch_transpose_sumsq(io, X, c.batch, c.pl->rows, c.pl->m,
-                                                 c.nn ? nullptr : c.xt(0), c.tile_partials(), c.s);
+                                                 c.nn ? nullptr : c.xt(0), c.xcopy, c.tile_partials(), c.s);
       ls.done();
       if (e != hipSuccess) return GNS_E_HIP;
     }
@@ -626,7 +636,7 @@ gns_status parse_restarts(const int *restart_after, int n_restart, int T, std::v
   return GNS_OK;
 }
 
-gns_status common_checks(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+gns_status common_checks(const void *X, const void *out, int64_t batch, int64_t n, int64_t m,
                          gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
                          const int64_t *row_idx, int64_t k, int64_t *rows) {
   if (!valid_dtype(io) || !valid_compute(cdt)) return GNS_E_DTYPE;
@@ -714,7 +724,7 @@ gns_status enqueue_gram(const Ctx &c, const void *X, void *out, int io, int64_t 
   // the normalised copy; restarts alternate between two row buffers (the
   // transposed-copy buffers, unused in this form, hold the second one)
   void *rows[2] = {c.xh(), c.xt(0)};
-  const void *xrow = c.direct ? c.xin : c.xh();
+  const void *xrow = c.direct ? c.xsrc() : c.xh();
   int64_t xrow_ld = c.direct ? c.pl->m : c.pl->Mp;
   int rcur = c.direct ? 0 : 1;
   // the unscaled input (row-major, or its transpose) carries the normalisation as a factor
@@ -837,23 +847,26 @@ bool direct_input(const Plan &pl, const void *X, int io, int cdt, const int64_t 
 constexpr int kSplit = 2;   // 3 and 4 parts measured slower (22.9 and 24.0 vs 22.0 ms per call)
 constexpr int kMaxDevices = 64;
 
+// The streams and events belong to one host thread and one device.  Calls
+// from different threads therefore never share them: they do not serialise
+// on each other, and a call on one thread never enqueues into streams that
+// another thread's open graph capture has joined.
 struct Fanout {
-  std::mutex mu;            // one call at a time uses the streams and events
   bool tried = false, ok = false;
   hipStream_t s[kSplit] = {};
   hipEvent_t fork = nullptr;
   hipEvent_t join[kSplit] = {};
   hipEvent_t stagger[kSplit] = {};
 };
-Fanout g_fanout[kMaxDevices];
+thread_local Fanout t_fanout[kMaxDevices];
 
-// Streams and events of the current device, created on first use (default
-// priority, non-blocking); nullptr when the device cannot provide them.
+// This thread's streams and events for the current device, created on first
+// use (default priority, non-blocking; kept until the process ends); nullptr
+// when the device cannot provide them.
 Fanout *fanout_for_current_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  Fanout *f = &g_fanout[dev];
-  std::lock_guard<std::mutex> lk(f->mu);
+  Fanout *f = &t_fanout[dev];
   if (!f->tried) {
     f->tried = true;
     bool ok = hipEventCreateWithFlags(&f->fork, hipEventDisableTiming) == hipSuccess;
@@ -875,7 +888,6 @@ gns_status run_batches(const Plan &pl, int cdt, int64_t batch, void *workspace,
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   Fanout *f = (split && batch >= 2) ? fanout_for_current_device() : nullptr;
   if (!f) return body(Ctx{&pl, cdt, batch, 0, ws, caller});
-  std::lock_guard<std::mutex> lk(f->mu);
   if (hipEventRecord(f->fork, caller) != hipSuccess) return GNS_E_HIP;
   gns_status st = GNS_OK;
   const int parts = static_cast<int>(std::min<int64_t>(kSplit, batch));
@@ -1003,6 +1015,148 @@ gns_status autotune(const TuneKey &key, hipStream_t s, Run run) {
   return GNS_OK;
 }
 
+// --------------------------------------------------------------- call plan
+// Everything a gns_gram_batched / gns_standard_batched call decides on the
+// host before it enqueues anything (also reported by gns_call_plan).
+struct CallPlan {
+  Plan pl;
+  int64_t rows = 0;
+  bool standard = false;     // runs standard NS (that entry point, or the square fallback)
+  bool naive = false;        // Algorithm 2 algebra
+  bool direct = false;       // the products read X itself (no normalised copy)
+  bool nn = false;           // Q X reads X row-major (K-major B operand)
+  bool inplace = false;      // out is X
+  bool copy_input = false;   // the input pass copies X into the workspace (Ctx::xcopy)
+  bool split = false;        // the batch may be split over the library's streams
+  bool autotune = false;     // GNS_OPT_TILE_AUTOTUNE
+  bool timed = false;        // this call would time an untuned shape
+  bool debug = false;        // GNS_OPT_DEBUG_CHECKS
+  std::vector<char> restart_at;
+};
+
+gns_status plan_call(bool standard_entry, const void *X, const void *out, int64_t batch, int64_t n, int64_t m,
+                     gns_dtype io, gns_dtype cdt, const double *coeffs, int T, const int *restart_after,
+                     int n_restart, const int64_t *row_idx, int64_t k, unsigned opts, CallPlan *cp) {
+  int64_t rows = 0;
+  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
+  if (st != GNS_OK) return st;
+  int tile_req = 0;
+  const unsigned allowed = GNS_OPT_TILE_AUTOTUNE | GNS_OPT_DEBUG_CHECKS |
+                           (standard_entry ? 0u : GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK);
+  if ((st = parse_opts(opts, allowed, &tile_req)) != GNS_OK) return st;
+  if (standard_entry) {
+    cp->restart_at.assign(T + 2, 0);
+  } else if ((st = parse_restarts(restart_after, n_restart, T, &cp->restart_at)) != GNS_OK) {
+    return st;
+  }
+  cp->rows = rows;
+  if (batch == 0) return GNS_OK;
+  // out is either X itself or a separate buffer: a partial overlap would let
+  // the output of one matrix overwrite input another still reads
+  const size_t io_bytes = static_cast<size_t>(batch) * n * m * gns::dtype_size(io);
+  cp->inplace = X == out;
+  if (!cp->inplace && ranges_overlap(X, io_bytes, out, io_bytes)) return GNS_E_ALIAS;
+  cp->autotune = (opts & GNS_OPT_TILE_AUTOTUNE) != 0;
+  cp->debug = (opts & GNS_OPT_DEBUG_CHECKS) != 0;
+  cp->split = !(opts & GNS_OPT_ONE_STREAM);
+  cp->naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
+  if (cp->autotune) {
+    // the plan of the kept choice, or of the size rule until the shape is
+    // tuned; an in-place call is never timed (every timed run would
+    // orthogonalise the previous run's output again)
+    const unsigned kept = tuned_choice(TuneKey{standard_entry ? 1 : 0, cdt, io, batch, rows, m});
+    const bool one_edge = cdt == GNS_F32 || cdt == GNS_BF16X3;
+    cp->timed = !kept && !cp->inplace && !one_edge;
+    unsigned bits = kept == kRuleChoice ? 0u : kept;
+    if (one_edge) bits = GNS_OPT_TILE_128;
+    parse_opts(bits, 0, &tile_req);
+  }
+  if (!make_plan(cdt, batch, rows, m, standard_entry ? 2 : 5, tile_req, &cp->pl)) return GNS_E_SHAPE;
+  // Square matrices: both algorithms cost the same and standard NS needs
+  // fewer launches and never forms X X^T of an ill-conditioned square
+  // matrix, so Dion3 falls back to it (§4.1, last paragraph).
+  cp->standard = standard_entry || (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK));
+  cp->direct = direct_input(cp->pl, X, io, cdt, row_idx);
+  cp->nn = !cp->standard && kmajor_products(cp->pl, cdt);
+  // In place on the direct path, the final Q X reads X (K-major form) when
+  // no restart has replaced it by a workspace buffer: the input pass then
+  // copies X, and the products read the copy.  (The transposed form and
+  // standard NS read X only in their first product, before any output is
+  // written; a row subset or a normalised copy never reads X after the
+  // input pass.)
+  const bool restarted = std::find(cp->restart_at.begin(), cp->restart_at.end(), 1) != cp->restart_at.end();
+  cp->copy_input = cp->inplace && cp->direct && cp->nn && !restarted;
+  return GNS_OK;
+}
+
+// Enqueues a planned, validated call (no autotune, no debug checks).
+gns_status enqueue_call(const CallPlan &cp, int cdt, const void *X, void *out, int64_t batch, int64_t n,
+                        int64_t m, int io, const double *coeffs, int T, const int64_t *row_idx, int64_t k,
+                        void *workspace, hipStream_t caller) {
+  const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
+  return run_batches(cp.pl, cdt, batch, workspace, caller, cp.split, [&](const Ctx &c0) {
+    const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
+    Ctx c = c0;
+    c.direct = cp.direct;
+    c.nn = cp.nn;
+    c.xin = Xs;
+    if (cp.copy_input) c.xcopy = c.xt(1);   // a region the K-major form never uses
+    const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
+    unsigned char *os = static_cast<unsigned char *>(out) + c.b0 * io_mat;
+    if (cp.standard) return enqueue_standard(c, Xs, os, io, n, coeffs, T, ri, ri, n);
+    return enqueue_gram(c, Xs, os, io, n, coeffs, T, cp.restart_at, ri, ri, n, cp.naive);
+  });
+}
+
+// Synchronous read of the debug-check flag in the workspace (4 bytes).
+gns_status read_flag(const int32_t *flag, hipStream_t s, int32_t *value) {
+  if (hipMemcpyAsync(value, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return GNS_E_HIP;
+  return GNS_OK;
+}
+
+gns_status orthogonalise(bool standard_entry, const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                         gns_dtype io, gns_dtype cdt, const double *coeffs, int T, const int *restart_after,
+                         int n_restart, const int64_t *row_idx, int64_t k, unsigned opts, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  CallPlan cp;
+  gns_status st = plan_call(standard_entry, X, out, batch, n, m, io, cdt, coeffs, T, restart_after, n_restart,
+                            row_idx, k, opts, &cp);
+  if (st != GNS_OK || batch == 0) return st;
+  if ((st = workspace_checks(X, out, batch, n, m, io, cp.pl, workspace, workspace_bytes)) != GNS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t *flag = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(workspace) + cp.pl.off_flag);
+  if (cp.debug) {
+    // the checks synchronise the stream, which a graph capture cannot do
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return GNS_E_HIP;
+    if (cs != hipStreamCaptureStatusNone) return GNS_E_FLAGS;
+    if (row_idx && n <= 65536) {
+      int32_t bad = 0;
+      if (gns::launch_check_rows(row_idx, batch, k, n, flag, s) != hipSuccess) return GNS_E_HIP;
+      if ((st = read_flag(flag, s, &bad)) != GNS_OK) return st;
+      if (bad) return GNS_E_ROWIDX;
+    }
+  }
+  if (cp.autotune) {
+    const unsigned inner = opts & ~(GNS_OPT_TILE_AUTOTUNE | GNS_OPT_DEBUG_CHECKS);
+    auto run = [&](unsigned bits) {
+      return orthogonalise(standard_entry, X, out, batch, n, m, io, cdt, coeffs, T, restart_after, n_restart,
+                           row_idx, k, inner | bits, workspace, workspace_bytes, stream);
+    };
+    const TuneKey key{standard_entry ? 1 : 0, cdt, io, batch, cp.rows, m};
+    st = cp.inplace ? run(tuned_choice(key) == kRuleChoice ? 0u : tuned_choice(key)) : autotune(key, s, run);
+  } else {
+    st = enqueue_call(cp, cdt, X, out, batch, n, m, io, coeffs, T, row_idx, k, workspace, s);
+  }
+  if (st != GNS_OK || !cp.debug) return st;
+  int32_t bad = 0;
+  if (gns::launch_check_finite(io, out, batch, n, m, row_idx, k, flag, s) != hipSuccess) return GNS_E_HIP;
+  if ((st = read_flag(flag, s, &bad)) != GNS_OK) return st;
+  return bad ? GNS_E_NONFINITE : GNS_OK;
+}
+
 }  // namespace
 
 // ==========================================================================
@@ -1021,11 +1175,12 @@ const char *gns_status_str(gns_status s) {
     case GNS_E_COEFF: return "invalid iteration count or coefficient";
     case GNS_E_RESTART: return "restart iterations must be strictly increasing in [1, T-1]";
     case GNS_E_ROWIDX: return "row index out of range or repeated";
-    case GNS_E_ALIAS: return "workspace overlaps X or out";
+    case GNS_E_ALIAS: return "buffers overlap (workspace with X or out, or out partly with X)";
     case GNS_E_WORKSPACE: return "workspace missing, misaligned or too small";
     case GNS_E_HIP: return "HIP launch failed";
     case GNS_E_FLAGS: return "unknown option bits";
     case GNS_E_PARAM: return "invalid update hyperparameter";
+    case GNS_E_NONFINITE: return "result holds Inf or NaN (debug checks)";
   }
   return "unknown status";
 }
@@ -1047,92 +1202,39 @@ gns_status gns_gram_batched(const void *X, void *out, int64_t batch, int64_t n, 
                             const int *restart_after, int n_restart, const int64_t *row_idx,
                             int64_t k, unsigned opts, void *workspace, size_t workspace_bytes,
                             void *stream) {
-  int64_t rows = 0;
-  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
-  if (st != GNS_OK) return st;
-  int tile_req = 0;
-  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK | GNS_OPT_TILE_AUTOTUNE,
-                       &tile_req)) != GNS_OK)
-    return st;
-  const bool split = !(opts & GNS_OPT_ONE_STREAM);
-  std::vector<char> restart_at;
-  if ((st = parse_restarts(restart_after, n_restart, T, &restart_at)) != GNS_OK) return st;
-  if (batch == 0) return GNS_OK;
-  Plan pl;
-  if (!make_plan(cdt, batch, rows, m, 5, tile_req, &pl)) return GNS_E_SHAPE;
-  st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
-  if (st != GNS_OK) return st;
-  if (opts & GNS_OPT_TILE_AUTOTUNE)
-    return autotune(TuneKey{0, cdt, io, batch, rows, m}, static_cast<hipStream_t>(stream),
-                    [&](unsigned bits) {
-                      return gns_gram_batched(X, out, batch, n, m, io, cdt, coeffs, T, restart_after,
-                                              n_restart, row_idx, k, (opts & ~GNS_OPT_TILE_AUTOTUNE) | bits,
-                                              workspace, workspace_bytes, stream);
-                    });
-  // Square matrices: both algorithms cost the same and standard NS needs
-  // fewer launches and never forms X X^T of an ill-conditioned square
-  // matrix, so Dion3 falls back to it (§4.1, last paragraph).
-  const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
-  hipStream_t caller = static_cast<hipStream_t>(stream);
-  const bool direct = direct_input(pl, X, io, cdt, row_idx);
-  if (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK))
-    return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c0) {
-      const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
-      Ctx c = c0;
-      c.direct = direct;
-      c.xin = Xs;
-      const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
-      return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
-                              ri, ri, n);
-    });
-  const bool naive = (opts & GNS_OPT_NAIVE_ALGEBRA) != 0;
-  const bool nn = kmajor_products(pl, cdt);
-  return run_batches(pl, cdt, batch, workspace, caller, split, [&](const Ctx &c0) {
-    const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
-    Ctx c = c0;
-    c.direct = direct;
-    c.nn = nn;
-    c.xin = Xs;
-    const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
-    return enqueue_gram(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io, n, coeffs, T,
-                        restart_at, ri, ri, n, naive);
-  });
+  return orthogonalise(false, X, out, batch, n, m, io, cdt, coeffs, T, restart_after, n_restart, row_idx, k,
+                       opts, workspace, workspace_bytes, stream);
 }
 
 gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
                                 gns_dtype io, gns_dtype cdt, const double *coeffs, int T,
                                 const int64_t *row_idx, int64_t k, unsigned opts, void *workspace,
                                 size_t workspace_bytes, void *stream) {
-  int64_t rows = 0;
-  gns_status st = common_checks(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k, &rows);
+  return orthogonalise(true, X, out, batch, n, m, io, cdt, coeffs, T, nullptr, 0, row_idx, k, opts, workspace,
+                       workspace_bytes, stream);
+}
+
+gns_status gns_call_plan(int standard, const void *X, const void *out, int64_t batch, int64_t n, int64_t m,
+                         gns_dtype io, gns_dtype cdt, const double *coeffs, int T, const int *restart_after,
+                         int n_restart, const int64_t *row_idx, int64_t k, unsigned opts, gns_plan_info *info) {
+  if (!info) return GNS_E_NULL;
+  CallPlan cp;
+  const gns_status st = plan_call(standard != 0, X, out, batch, n, m, io, cdt, coeffs, T, restart_after,
+                                  n_restart, row_idx, k, opts, &cp);
   if (st != GNS_OK) return st;
-  int tile_req = 0;
-  if ((st = parse_opts(opts, GNS_OPT_TILE_AUTOTUNE, &tile_req)) != GNS_OK) return st;
-  const bool split = !(opts & GNS_OPT_ONE_STREAM);
+  std::memset(info, 0, sizeof(*info));
   if (batch == 0) return GNS_OK;
-  Plan pl;
-  if (!make_plan(cdt, batch, rows, m, 2, tile_req, &pl)) return GNS_E_SHAPE;
-  st = workspace_checks(X, out, batch, n, m, io, pl, workspace, workspace_bytes);
-  if (st != GNS_OK) return st;
-  if (opts & GNS_OPT_TILE_AUTOTUNE)
-    return autotune(TuneKey{1, cdt, io, batch, rows, m}, static_cast<hipStream_t>(stream),
-                    [&](unsigned bits) {
-                      return gns_standard_batched(X, out, batch, n, m, io, cdt, coeffs, T, row_idx, k,
-                                                  (opts & ~GNS_OPT_TILE_AUTOTUNE) | bits, workspace,
-                                                  workspace_bytes, stream);
-                    });
-  const size_t io_mat = static_cast<size_t>(n) * m * gns::dtype_size(io);
-  const bool direct = direct_input(pl, X, io, cdt, row_idx);
-  return run_batches(pl, cdt, batch, workspace, static_cast<hipStream_t>(stream), split,
-                     [&](const Ctx &c0) {
-                       const unsigned char *Xs = static_cast<const unsigned char *>(X) + c0.b0 * io_mat;
-                       Ctx c = c0;
-                       c.direct = direct;
-                       c.xin = Xs;
-                       const int64_t *ri = row_idx ? row_idx + c.b0 * k : nullptr;
-                       return enqueue_standard(c, Xs, static_cast<unsigned char *>(out) + c.b0 * io_mat, io,
-                                               n, coeffs, T, ri, ri, n);
-                     });
+  info->standard = cp.standard ? 1 : 0;
+  info->tile = cp.pl.tile;
+  info->sym_tile = cp.pl.sym_tile;
+  info->gram_parts = cp.pl.syrk_parts;
+  info->direct_input = cp.direct ? 1 : 0;
+  info->kmajor_products = cp.nn ? 1 : 0;
+  info->input_copy = cp.copy_input ? 1 : 0;
+  info->split_streams = (cp.split && batch >= 2) ? 1 : 0;
+  info->autotune_timed = cp.timed ? 1 : 0;
+  info->workspace_bytes = cp.pl.bytes;
+  return GNS_OK;
 }
 
 int gns_tuned_tile(int standard, gns_dtype cdt, gns_dtype io, int64_t batch, int64_t rows, int64_t m,
@@ -1206,12 +1308,14 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
       !std::isfinite(eps) || (normuon && !(eps > 0.0)))
     return GNS_E_PARAM;
   int tile_req = 0;
-  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK, &tile_req)) != GNS_OK)
+  if ((st = parse_opts(opts, GNS_OPT_NAIVE_ALGEBRA | GNS_OPT_NO_SQUARE_FALLBACK | GNS_OPT_DEBUG_CHECKS,
+                       &tile_req)) != GNS_OK)
     return st;
   std::vector<char> restart_at;
   if ((st = parse_restarts(restart_after, n_restart, T, &restart_at)) != GNS_OK) return st;
   if (batch == 0) return GNS_OK;
   if (!W || !G || !M || !row_idx || (normuon && !v)) return GNS_E_NULL;
+  const bool debug = (opts & GNS_OPT_DEBUG_CHECKS) != 0;
   Plan pl;
   Dion3Layout d;
   if (!make_plan(cdt, batch, k, m, 5, tile_req, &pl) || !dion3_layout(cdt, batch, n, m, k, &d))
@@ -1231,6 +1335,11 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
         return GNS_E_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return GNS_E_HIP;
+    if (cs != hipStreamCaptureStatusNone) return GNS_E_FLAGS;
+  }
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   double *keys = reinterpret_cast<double *>(ws + d.off_keys);
   float *O = reinterpret_cast<float *>(ws + d.off_o);
@@ -1266,6 +1375,15 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
     return enqueue_gram(cg, Xs, Os, GNS_F32, n, coeffs, T, restart_at, ri, nullptr, k, naive);
   });
   if (st != GNS_OK) return st;
+  if (debug) {
+    // a non-finite update is reported before it reaches W, v or the error
+    // feedback (M then holds M + G, row_idx the selection)
+    int32_t *flag = reinterpret_cast<int32_t *>(ws + pl.off_flag);
+    int32_t bad = 0;
+    if (gns::launch_check_finite(GNS_F32, O, batch, k, m, nullptr, 0, flag, s) != hipSuccess) return GNS_E_HIP;
+    if ((st = read_flag(flag, s, &bad)) != GNS_OK) return st;
+    if (bad) return GNS_E_NONFINITE;
+  }
   // NorMuon row factors (second moment v at the selected rows), then the
   // decay, the update of the selected rows and the error feedback
   {
@@ -1294,6 +1412,36 @@ gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, i
   if (batch == 0) return GNS_OK;
   hipError_t e = gns::launch_check_rows(row_idx, batch, k, n, result, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+gns_status gns_check_finite(const void *A, gns_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
+                            const int64_t *row_idx, int64_t k, int32_t *result, void *stream) {
+  if (!valid_dtype(dtype)) return GNS_E_DTYPE;
+  if (batch < 0 || rows < 1 || cols < 1 || batch > 65535 || (row_idx && (k < 1 || k > rows))) return GNS_E_SHAPE;
+  if (!result || (batch > 0 && !A)) return GNS_E_NULL;
+  const hipError_t e = gns::launch_check_finite(dtype, A, batch, rows, cols, row_idx, k, result,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GNS_OK : GNS_E_HIP;
+}
+
+int64_t gns_select_count(int64_t n, double fraction) {
+  if (n < 1 || !(fraction > 0.0) || !(fraction <= 1.0)) return 0;
+  const double k = std::ceil(fraction * static_cast<double>(n));
+  return std::max<int64_t>(1, std::min<int64_t>(n, static_cast<int64_t>(k)));
+}
+
+gns_status gns_safety_scale(const double *coeffs, int T, double s, double *out) {
+  if (!coeffs || !out) return GNS_E_NULL;
+  if (T < 1 || T > GNS_MAX_ITERS) return GNS_E_COEFF;
+  if (!std::isfinite(s) || !(s > 0.0)) return GNS_E_PARAM;
+  const double s3 = s * s * s, s5 = s3 * s * s;
+  for (int t = 0; t < T; ++t) {
+    const double a = coeffs[3 * t], b = coeffs[3 * t + 1], c = coeffs[3 * t + 2];
+    out[3 * t] = a / s;
+    out[3 * t + 1] = b / s3;
+    out[3 * t + 2] = c / s5;
+  }
+  return GNS_OK;
 }
 
 void gns_timing_enable(int on) {

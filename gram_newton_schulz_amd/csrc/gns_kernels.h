@@ -103,11 +103,18 @@ hipError_t launch_select_rows_l1(int io_dtype, const void *M, int64_t batch, int
 // Unscaled transpose of 16-bit X (n, m multiples of 128, 16-byte aligned) into
 // XT [m][n] per matrix (skipped when XT is null), and the sum of squares of
 // every 128x128 tile into partials[b][tile] (fp64).
+// With Xcopy set, X is also copied row-major into Xcopy (same layout).
 hipError_t launch_transpose_sumsq(int dtype, const void *X, int64_t batch, int64_t n, int64_t m,
-                                  void *XT, double *partials, hipStream_t s);
+                                  void *XT, void *Xcopy, double *partials, hipStream_t s);
 // inv[b] = 1 / (sqrt(sum_i partials[b][i]) + eps) and inv2[b] = inv[b]^2 (fixed-order sums).
 hipError_t launch_norm_finish(const double *partials, int64_t batch, int64_t parts, double eps,
                               float *inv, float *inv2, hipStream_t s);
+
+// *result = 1 if any element of the [batch][rows][cols] array A (dtype DT_F32,
+// DT_BF16 or DT_F16) is Inf or NaN, else 0; with row_idx ([batch][k]) only
+// those rows are checked.
+hipError_t launch_check_finite(int dtype, const void *A, int64_t batch, int64_t rows, int64_t cols,
+                               const int64_t *row_idx, int64_t k, int32_t *result, hipStream_t s);
 
 hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, int64_t n,
                              int32_t *result, hipStream_t s);

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gns_kernels.h"
@@ -1384,6 +1385,37 @@ check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
 }
 
 // ---------------------------------------------------------------------------
+// finite check of an output: *result = 1 if any checked element is Inf or NaN
+// (plain stores of the same value from every lane that sees one; the host
+// cleared *result first).  One wave per row, rows taken through row_idx when
+// given (indices outside [0, rows) are skipped).
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ void __launch_bounds__(256)
+check_finite(const void *A, int64_t rows, int64_t cols, const int64_t *row_idx, int64_t k,
+             int32_t *result) {
+  using S = typename E::S;
+  const int64_t b = blockIdx.y;
+  const int64_t sel = row_idx ? k : rows;
+  const int lane = threadIdx.x & 63;
+  bool bad = false;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); i < sel;
+       i += static_cast<int64_t>(gridDim.x) * 4) {
+    const int64_t r = row_idx ? row_idx[b * k + i] : i;
+    if (r < 0 || r >= rows) continue;
+    const S *row = static_cast<const S *>(A) + (b * rows + r) * cols;
+    for (int64_t j = lane; j < cols; j += 64) {
+      // Inf or NaN: every exponent bit set (binary32 bits 30..23, bfloat16
+      // bits 14..7, binary16 bits 14..10)
+      if constexpr (E::code == DT_F32) bad |= (__float_as_uint(row[j]) & 0x7f800000u) == 0x7f800000u;
+      else if constexpr (E::code == DT_BF16) bad |= (row[j] & 0x7f80u) == 0x7f80u;
+      else bad |= (row[j] & 0x7c00u) == 0x7c00u;
+    }
+  }
+  if (bad) *result = 1;
+}
+
+// ---------------------------------------------------------------------------
 // Input path without a normalised copy (16-bit input in the compute type,
 // whole tiles): the products read X itself and take 1/(||X||_F + eps) as a
 // per-matrix factor in their epilogues, so only X^T is materialised.
@@ -1395,7 +1427,7 @@ check_rows(const int64_t *row_idx, int64_t k, int64_t n, int32_t *result) {
 template <class T>
 __global__ void __launch_bounds__(256)
 transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restrict__ XT,
-                double *partials) {
+                void *__restrict__ Xcopy, double *partials) {
   constexpr int TT = 128;                 // tile edge
   constexpr int PR = TT / 8;              // 16-byte pieces per tile row
   constexpr int NP = TT * PR / 256;       // pieces per thread
@@ -1411,6 +1443,16 @@ transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restri
   for (int h = 0; h < NP; ++h) {
     const int v = threadIdx.x + 256 * h;
     in[h] = *reinterpret_cast<const u32x4 *>(Xb + (r0 + v / PR) * m + c0 + (v % PR) * 8);
+  }
+  // optional row-major copy of X, same layout (read by later products in
+  // place of the caller's X when the caller's X is also the output)
+  if (Xcopy) {
+    uint16_t *Xc = static_cast<uint16_t *>(Xcopy) + static_cast<int64_t>(b) * n * m;
+#pragma unroll
+    for (int h = 0; h < NP; ++h) {
+      const int v = threadIdx.x + 256 * h;
+      *reinterpret_cast<u32x4 *>(Xc + (r0 + v / PR) * m + c0 + (v % PR) * 8) = in[h];
+    }
   }
   float sq = 0.0f;
 #pragma unroll
@@ -1901,10 +1943,24 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
 }
 
 hipError_t launch_transpose_sumsq(int dt, const void *X, int64_t batch, int64_t n, int64_t m,
-                                  void *XT, double *partials, hipStream_t s) {
+                                  void *XT, void *Xcopy, double *partials, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(m / 128), static_cast<unsigned>(n / 128), static_cast<unsigned>(batch));
-  if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, partials);
-  else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, partials);
+  if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials);
+  else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite(int dt, const void *A, int64_t batch, int64_t rows, int64_t cols,
+                               const int64_t *row_idx, int64_t k, int32_t *result, hipStream_t s) {
+  check_rows_init<<<1, 1, 0, s>>>(result);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || batch == 0) return e;
+  const int64_t sel = row_idx ? k : rows;
+  const int64_t gx = std::min<int64_t>((sel + 3) / 4, 65535);
+  dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(batch));
+  if (dt == DT_F32) check_finite<EF32><<<grid, 256, 0, s>>>(A, rows, cols, row_idx, k, result);
+  else if (dt == DT_BF16) check_finite<EBF16><<<grid, 256, 0, s>>>(A, rows, cols, row_idx, k, result);
+  else check_finite<EF16><<<grid, 256, 0, s>>>(A, rows, cols, row_idx, k, result);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@
  *   pointers read before the call returns.
  * - X and out are contiguous row-major [batch][n][m] in the I/O dtype.
  * - The caller owns every buffer, including the workspace; the library never
- *   allocates or frees device memory and never synchronises the stream.
+ *   allocates or frees device memory and never synchronises the stream
+ *   (GNS_OPT_DEBUG_CHECKS and a first GNS_OPT_TILE_AUTOTUNE call aside).
  *   The call returns once its work is enqueued; results are ready when
  *   `stream` is.  With batch >= 2 (and without GNS_OPT_ONE_STREAM) the two
  *   halves of the batch run on two streams that the library creates once per
@@ -31,15 +32,21 @@
  *   `stream` waits for both before anything enqueued on it later, so the
  *   caller sees the same ordering as if all work ran on `stream`.  The
  *   halves then fill each other's idle CUs in the last, partial wave of
- *   tiles of every launch.  Calls from several host threads on one device
- *   share those streams (they are serialised, still correct).
+ *   tiles of every launch.  Every host thread has its own two streams per
+ *   device (created on its first such call, kept until the process ends),
+ *   so calls from different threads neither serialise on shared streams nor
+ *   enter another thread's graph capture.
  * - Argument errors are detected on the host before anything is enqueued
  *   (no partial work) and reported as a status code; nothing throws across
  *   the ABI.  A failed kernel launch returns GNS_E_HIP.  Faults inside
  *   kernels surface at the caller's next synchronisation.
- * - out may be the same buffer as X (X is read completely into the
- *   workspace before out is written).  The workspace must not overlap X or
- *   out.
+ * - out may be the same buffer as X (in place): no product reads X after
+ *   the final product starts writing out.  Where the final product would
+ *   otherwise read X itself (16-bit X in the compute type, whole 256-edge
+ *   tiles, no restart), the input pass first copies X into the workspace;
+ *   results are bit-identical to the out-of-place call.  A partial overlap
+ *   of X and out returns GNS_E_ALIAS, as does any overlap of the workspace
+ *   with X or out.
  * - Results are deterministic for a fixed shape, dtype and option set (no
  *   atomics, fixed reduction order).
  * - batch == 0 is a no-op that returns GNS_OK (pointers may then be NULL).
@@ -80,12 +87,19 @@ typedef enum {
   GNS_E_COEFF = 4,     /* T < 1, T > GNS_MAX_ITERS, or a non-finite coeff.    */
   GNS_E_RESTART = 5,   /* restart list not strictly increasing in [1, T-1]    */
   GNS_E_ROWIDX = 6,    /* row index out of range or repeated (check call)     */
-  GNS_E_ALIAS = 7,     /* workspace overlaps X or out                         */
+  GNS_E_ALIAS = 7,     /* workspace overlaps X or out, or out overlaps X
+                          without being the same buffer                      */
   GNS_E_WORKSPACE = 8, /* workspace NULL or smaller than gns_*_workspace_bytes */
   GNS_E_HIP = 9,       /* a HIP launch or runtime call failed                 */
-  GNS_E_FLAGS = 10,    /* unknown option bit                                  */
-  GNS_E_PARAM = 11     /* non-finite update hyperparameter, or eps <= 0 with
-                          NorMuon (gns_dion3_step)                            */
+  GNS_E_FLAGS = 10,    /* unknown option bit, or GNS_OPT_DEBUG_CHECKS on a
+                          stream that is being captured into a graph         */
+  GNS_E_PARAM = 11,    /* non-finite update hyperparameter, or eps <= 0 with
+                          NorMuon (gns_dion3_step); bad safety factor        */
+  GNS_E_NONFINITE = 12 /* GNS_OPT_DEBUG_CHECKS only: the result holds Inf or
+                          NaN.  Half-precision Gram Newton-Schulz without
+                          restarts can blow up this way ("Dion3", Appendix
+                          B.1, Figs. 11-12); a restart, or a second one,
+                          usually cures it (Appendix B.2).                   */
 } gns_status;
 
 #define GNS_MAX_ITERS 64
@@ -112,6 +126,19 @@ typedef enum {
                                       (restart and final), 128 x 128 tiles for
                                       the symmetric ones (Gram matrix, n x n
                                       iteration)                              */
+#define GNS_OPT_DEBUG_CHECKS 0x100u /* synchronous checks (gns_gram_batched,
+                                      gns_standard_batched, gns_dion3_step):
+                                      before enqueueing, a row subset is
+                                      checked (GNS_E_ROWIDX on a repeated or
+                                      out-of-range index; rows <= 65536 only);
+                                      after the call, the output (the selected
+                                      rows of out; for gns_dion3_step the update
+                                      O, before it reaches W) is checked for Inf
+                                      and NaN (GNS_E_NONFINITE).  Both
+                                      synchronise `stream`, so the bit is
+                                      refused while `stream` is being captured
+                                      (GNS_E_FLAGS).  A debugging aid: the
+                                      default mode never synchronises. */
 /* At most one TILE bit.  Without one the library picks from the problem
    size: 256-edge tiles once the symmetric products have 64 upper 256-edge
    tiles over the batch; of those, the symmetric products run 128-edge tiles
@@ -206,6 +233,37 @@ gns_status gns_standard_batched(const void *X, void *out, int64_t batch, int64_t
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The host-side plan of a gns_gram_batched (standard = 0) or
+ * gns_standard_batched (standard = 1) call with these arguments, without
+ * enqueueing anything and without a workspace or stream: argument errors are
+ * returned exactly as the call would return them (workspace checks aside).
+ * X and out are compared and their alignment examined, never dereferenced.
+ * With GNS_OPT_TILE_AUTOTUNE the plan of the kept choice is reported, or of
+ * the size rule while the shape is untuned.  batch == 0 reports zeros.
+ */
+typedef struct {
+  int standard;         /* 1: runs standard Newton-Schulz (that entry point,
+                           or the square fallback of gns_gram_batched)        */
+  int tile;             /* edge of the rectangular products (128 or 256)      */
+  int sym_tile;         /* edge of the symmetric products                     */
+  int gram_parts;       /* parts of a Gram matrix split along its contraction
+                           (1: not split)                                     */
+  int direct_input;     /* 1: the products read X itself, scaled in their
+                           epilogues, instead of a normalised copy            */
+  int kmajor_products;  /* 1: Q X reads X row-major (no transposed copy)      */
+  int input_copy;       /* 1: in place on the direct path: the input pass
+                           copies X into the workspace first                  */
+  int split_streams;    /* 1: the batch is split over the library's streams   */
+  int autotune_timed;   /* 1: the call would time the tile choices            */
+  size_t workspace_bytes; /* workspace this plan uses                         */
+} gns_plan_info;
+
+gns_status gns_call_plan(int standard, const void *X, const void *out, int64_t batch, int64_t n,
+                         int64_t m, gns_dtype io_dtype, gns_dtype compute_dtype,
+                         const double *coeffs, int T, const int *restart_after, int n_restart,
+                         const int64_t *row_idx, int64_t k, unsigned opts, gns_plan_info *info);
+
+/*
  * Row selection of the Dion3 update ("Dion3: Full-Stack Orthogonal Updates",
  * §6, Algorithm 4, selection step): for every matrix M_b, the indices of the
  * k rows with the largest l1 norm sum_j |M_b[i][j]|, written to
@@ -288,6 +346,36 @@ gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, i
                              int32_t *result, void *stream);
 
 /*
+ * Enqueue a finite check of a [batch][rows][cols] row-major array A in
+ * dtype (GNS_F32, GNS_BF16 or GNS_F16): writes to *result (device int32) 1
+ * when an element is Inf or NaN, else 0.  With row_idx ([batch][k] int64,
+ * device) only those rows are checked (indices outside [0, rows) are
+ * skipped).  The caller reads *result after synchronising the stream.  Half
+ * precision Gram Newton-Schulz can return Infs ("Dion3", Appendix B.1); this
+ * is the enqueue-only form of the check that GNS_OPT_DEBUG_CHECKS runs
+ * synchronously.  Needs batch <= 65535.
+ */
+gns_status gns_check_finite(const void *A, gns_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
+                            const int64_t *row_idx, int64_t k, int32_t *result, void *stream);
+
+/*
+ * Rows a Dion3 update orthogonalises ("Dion3", §6, Algorithm 4): k = ceil(f
+ * n) for a fraction f in (0, 1], clamped to [1, n]; 0 for n < 1 or f outside
+ * (0, 1].
+ */
+int64_t gns_select_count(int64_t n, double fraction);
+
+/*
+ * Safety factor ("Dion3", Appendix B.2.2): the coefficients of p_t(x / s),
+ * (a_t / s, b_t / s^3, c_t / s^5), so that singular values up to s still
+ * converge (the pages use s = 1.02, or 1.05 to be conservative).
+ *   coeffs, out  (host) T x 3 doubles (may be the same array).
+ * GNS_E_NULL, GNS_E_COEFF (T outside 1..GNS_MAX_ITERS) or GNS_E_PARAM (s not
+ * finite and positive).
+ */
+gns_status gns_safety_scale(const double *coeffs, int T, double s, double *out);
+
+/*
  * Shape-keyed tile autotuning ("DMuon: Efficient Distributed Muon Training
  * with Near-Adam Overhead", §3.3: the best tile shape of the batched Gram NS
  * kernels varies by shape, so it is chosen per shape by measurement).  With
@@ -302,7 +390,10 @@ gns_status gns_check_row_idx(const int64_t *row_idx, int64_t batch, int64_t k, i
  * split-bf16 compute have one choice (128) and are never timed.  While
  * `stream` is being captured into a graph, an untuned shape runs the
  * size-based choice and stays untuned.  A failing run returns its status
- * and keeps nothing.
+ * and keeps nothing.  An in-place call (out == X) is never timed (each
+ * timed run would orthogonalise the previous run's output again): it runs
+ * the kept choice, or the size rule while the shape is untuned, and keeps
+ * nothing.
  *
  * gns_tuned_tile returns the kept tile edge of the rectangular products for
  * a shape (standard = 0 for gns_gram_batched, 1 for gns_standard_batched),

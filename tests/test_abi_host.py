@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(gns.LIB_PATH),
 
 FAKE = 0x10000000  # never dereferenced: every call below fails validation first
 E = {"OK": 0, "NULL": 1, "SHAPE": 2, "DTYPE": 3, "COEFF": 4, "RESTART": 5, "ROWIDX": 6,
-     "ALIAS": 7, "WORKSPACE": 8, "HIP": 9, "FLAGS": 10, "PARAM": 11}
+     "ALIAS": 7, "WORKSPACE": 8, "HIP": 9, "FLAGS": 10, "PARAM": 11, "NONFINITE": 12}
 
 
 def declared_functions():
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_strings():
     L = gns.lib()
     assert L.gns_abi_version() == 1
-    for code in range(0, 12):
+    for code in range(0, 13):
         assert L.gns_status_str(code)
         assert L.gns_status_str(code) != b"unknown status"
 
@@ -102,7 +102,7 @@ def test_gram_argument_errors():
     assert _gram(restarts=(5,)) == E["RESTART"]           # must be <= T-1
     assert _gram(restarts=(3, 2)) == E["RESTART"]
     assert _gram(restarts=(2, 2)) == E["RESTART"]
-    assert _gram(opts=0x100) == E["FLAGS"]
+    assert _gram(opts=0x200) == E["FLAGS"]
     assert _gram(opts=0x30) == E["FLAGS"]                 # two tile bits
     assert _gram(opts=0x50) == E["FLAGS"]                 # autotune with a tile bit
     assert _gram(opts=0x60) == E["FLAGS"]
@@ -173,6 +173,161 @@ def test_select_argument_errors():
     assert sel(batch=0, M=None, out=None, ws=None, ws_bytes=0) == E["OK"]
 
 
+def test_gram_output_overlap():
+    """out is X itself, or disjoint from it: a partial overlap would let one
+    matrix's output overwrite input that another still reads."""
+    nbytes = 1 * 4 * 8 * 2
+    assert _gram(X=FAKE, out=FAKE, ws_bytes=100) == E["WORKSPACE"]      # in place: accepted so far
+    assert _gram(X=FAKE, out=FAKE + 2) == E["ALIAS"]
+    assert _gram(X=FAKE + 2, out=FAKE) == E["ALIAS"]
+    assert _gram(X=FAKE, out=FAKE + nbytes, ws_bytes=100) == E["WORKSPACE"]   # adjacent: fine
+
+
+def _plan(standard=0, X=0x100000000, out=0x200000000, batch=3, n=512, m=1536, io=1, cdt=1,
+          coeffs=None, restarts=(), row_idx=None, k=0, opts=0x20):
+    if coeffs is None:
+        coeffs = [(3.4445, -4.7750, 2.0315)] * 5
+    return gns.call_plan(bool(standard), X, out, batch, n, m, io, cdt, coeffs, restarts,
+                         row_idx_ptr=row_idx or 0, k=k, opts=opts)
+
+
+def test_plan_in_place_copies_input_only_where_needed():
+    """The final product reads X itself only on the direct, K-major path with
+    no restart; an in-place call there copies X first (Dion3 Algorithm 3:
+    X <- Q_T X is the only write of the output)."""
+    X = 0x100000000
+    oop = _plan()                                   # whole 256-edge tiles, bf16 in bf16
+    assert oop.direct_input == 1 and oop.kmajor_products == 1 and oop.input_copy == 0
+    assert oop.tile == 256 and oop.standard == 0 and oop.split_streams == 1
+    ip = _plan(out=X)
+    assert ip.direct_input == 1 and ip.kmajor_products == 1 and ip.input_copy == 1
+    ip1 = _plan(out=X, coeffs=[(3.4445, -4.7750, 2.0315)])          # T = 1
+    assert ip1.input_copy == 1
+    # the size rule picks 256-edge tiles on its own for larger batches
+    big = _plan(out=X, batch=2, n=2048, m=4096, opts=0)
+    assert big.tile == 256 and big.sym_tile == 128 and big.input_copy == 1
+    # ... and 128-edge tiles (transposed form, X read only first) for small ones
+    small = _plan(out=X, opts=0)
+    assert small.tile == 128 and small.direct_input == 1 and small.input_copy == 0
+    # a restart replaces X by a workspace buffer before the final product
+    assert _plan(out=X, restarts=(2,)).input_copy == 0
+    # no direct path: ragged tiles, another I/O type, or a row subset
+    assert _plan(out=X, n=500).input_copy == 0 and _plan(out=X, n=500).direct_input == 0
+    assert _plan(out=X, io=0).input_copy == 0
+    assert _plan(out=X, row_idx=0x300000000, k=256).input_copy == 0
+    # transposed form (128-edge tiles) and standard NS read X only first
+    assert _plan(out=X, opts=0x10).input_copy == 0 and _plan(out=X, opts=0x10).direct_input == 1
+    assert _plan(standard=1, out=X).input_copy == 0
+    sq = _plan(out=X, n=1536)                        # square: standard NS fallback
+    assert sq.standard == 1 and sq.input_copy == 0
+    # the in-place copy lives in a region the quoted workspace already holds
+    L = gns.lib()
+    assert ip.workspace_bytes <= L.gns_gram_workspace_bytes(1, 3, 512, 1536)
+    assert oop.workspace_bytes == ip.workspace_bytes
+
+
+def test_plan_autotune_and_errors():
+    L = gns.lib()
+    L.gns_autotune_clear()
+    X = 0x100000000
+    assert _plan(opts=0x40).autotune_timed == 1
+    assert _plan(out=X, opts=0x40).autotune_timed == 0       # in place: never timed
+    assert _plan(cdt=0, io=0, opts=0x40).autotune_timed == 0  # fp32: one tile edge
+    assert _plan(opts=0x40).tile == 128                       # untuned: the size rule
+    assert _plan(batch=2, n=2048, m=4096, opts=0x40).tile == 256
+    assert _plan(batch=0).tile == 0
+    with pytest.raises(gns.GnsError):
+        _plan(out=X + 2)                                      # partial overlap
+    with pytest.raises(gns.GnsError):
+        _plan(restarts=(5,))
+    info = gns.PlanInfo()
+    carr = (ctypes.c_double * 3)(1.0, 0.0, 0.0)
+    assert L.gns_call_plan(0, X, X, 1, 4, 8, 1, 1, carr, 1, None, 0, None, 0, 0, None) == E["NULL"]
+    assert L.gns_call_plan(0, X, X, 1, 4, 8, 1, 1, carr, 1, None, 0, None, 0, 0x200,
+                           ctypes.byref(info)) == E["FLAGS"]
+    # the K split of small Gram matrices and the mixed tiles of the size rule
+    sub = _plan(batch=8, n=4096, m=16384, row_idx=0x300000000, k=1024, restarts=(2,), opts=0)
+    assert sub.tile == 256 and sub.sym_tile == 128 and sub.gram_parts == 3
+
+
+def test_debug_checks_option():
+    """GNS_OPT_DEBUG_CHECKS is a valid option of the three compute entry
+    points; validation still comes first."""
+    assert _gram(opts=0x100, ws_bytes=100) == E["WORKSPACE"]
+    assert _gram(opts=0x140, ws_bytes=100) == E["WORKSPACE"]    # with autotune
+    assert _dion3(opts=0x100, ws_bytes=64) == E["WORKSPACE"]
+    assert gns.binding.GNS_OPT_DEBUG_CHECKS == 0x100
+
+
+def test_check_finite_argument_errors():
+    L = gns.lib()
+    assert L.gns_check_finite(FAKE, 3, 1, 4, 8, None, 0, FAKE, None) == E["DTYPE"]   # split type
+    assert L.gns_check_finite(FAKE, 1, 1, 0, 8, None, 0, FAKE, None) == E["SHAPE"]
+    assert L.gns_check_finite(FAKE, 1, 1, 4, 8, FAKE, 5, FAKE, None) == E["SHAPE"]   # k > rows
+    assert L.gns_check_finite(FAKE, 1, 70000, 4, 8, None, 0, FAKE, None) == E["SHAPE"]
+    assert L.gns_check_finite(None, 1, 1, 4, 8, None, 0, FAKE, None) == E["NULL"]
+    assert L.gns_check_finite(FAKE, 1, 1, 4, 8, None, 0, None, None) == E["NULL"]
+
+
+def test_select_count_and_safety_scale_in_library():
+    """k = ceil(f n) (Dion3 Algorithm 4) and p_t(x / s) (Appendix B.2.2) are
+    computed behind the C ABI; the binding only marshals them."""
+    L = gns.lib()
+    assert L.gns_select_count(4096, 0.25) == 1024
+    assert L.gns_select_count(10, 0.01) == 1 and L.gns_select_count(10, 1.0) == 10
+    assert L.gns_select_count(7, 0.5) == 4 and L.gns_select_count(3, 1e-12) == 1
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert L.gns_select_count(10, bad) == 0
+    assert L.gns_select_count(0, 0.5) == 0
+    co = (ctypes.c_double * 6)(3.4445, -4.7750, 2.0315, 1.875, -1.25, 0.375)
+    out = (ctypes.c_double * 6)()
+    assert L.gns_safety_scale(co, 2, 2.0, out) == E["OK"]
+    assert list(out) == [3.4445 / 2, -4.7750 / 8, 2.0315 / 32, 1.875 / 2, -1.25 / 8, 0.375 / 32]
+    assert L.gns_safety_scale(co, 2, 0.0, out) == E["PARAM"]
+    assert L.gns_safety_scale(co, 2, float("inf"), out) == E["PARAM"]
+    assert L.gns_safety_scale(co, 0, 1.05, out) == E["COEFF"]
+    assert L.gns_safety_scale(None, 2, 1.05, out) == E["NULL"]
+    with pytest.raises(ValueError):
+        gns.select_count(10, 0.0)
+    with pytest.raises(ValueError):
+        gns.safety_scaled([(1, 0, 0)], -1.0)
+
+
+def test_binding_rejects_bad_buffers_before_any_launch():
+    """Every check runs on the host before the library is called: shapes,
+    dtypes and layout first, then that the tensors live on the GPU."""
+    import torch
+    X = torch.zeros(2, 4, 8, dtype=torch.bfloat16)
+    co = [(1.0, 0.0, 0.0)]
+    bad_outs = [torch.zeros(2, 4, 9, dtype=torch.bfloat16),          # shape
+                torch.zeros(2, 4, 8, dtype=torch.float32),           # dtype
+                torch.zeros(2, 8, 4, dtype=torch.bfloat16).transpose(1, 2)]   # layout
+    for fn in (gns.gram_ns_batched, gns.standard_ns_batched):
+        for o in bad_outs:
+            with pytest.raises(gns.GnsError) as e:
+                fn(X, co, out=o) if fn is gns.standard_ns_batched else fn(X, co, restarts=(), out=o)
+            assert e.value.code in (2, 3)
+        with pytest.raises(gns.GnsError) as e:                        # host memory
+            fn(X, co) if fn is gns.standard_ns_batched else fn(X, co, restarts=())
+        assert e.value.code == 1 and "GPU" in str(e.value)
+        with pytest.raises(gns.GnsError) as e:                        # row_idx dtype
+            kw = dict(row_idx=torch.zeros(2, 2, dtype=torch.int32))
+            fn(X, co, **kw) if fn is gns.standard_ns_batched else fn(X, co, restarts=(), **kw)
+        assert e.value.code == 6
+    W = torch.zeros(2, 4, 8)
+    with pytest.raises(gns.GnsError) as e:                            # row_idx shape
+        gns.dion3_step(W, W.clone(), W.clone(), None, 2, co, (), normuon=False,
+                       row_idx=torch.zeros(2, 3, dtype=torch.int64))
+    assert e.value.code == 6
+    with pytest.raises(gns.GnsError) as e:                            # host memory
+        gns.dion3_step(W, W.clone(), W.clone(), None, 2, co, (), normuon=False)
+    assert e.value.code == 1
+    with pytest.raises(gns.GnsError):
+        gns.select_rows_l1(X, 2)
+    with pytest.raises(gns.GnsError):
+        gns.check_finite(X)
+
+
 def test_safety_factor_helper():
     """p_t(x / s) has coefficients (a/s, b/s^3, c/s^5): one step of the scaled
     schedule at s*x equals one step of the original at x."""
@@ -230,7 +385,7 @@ def test_dion3_argument_errors():
     assert _dion3(lr=float("nan")) == E["PARAM"]
     assert _dion3(mu=float("inf")) == E["PARAM"]
     assert _dion3(eps=0.0) == E["PARAM"]                   # NorMuon divides by sqrt(v) + eps
-    assert _dion3(opts=0x100) == E["FLAGS"]
+    assert _dion3(opts=0x200) == E["FLAGS"]
     assert _dion3(opts=0x40) == E["FLAGS"]                 # no autotune for the whole update
     assert _dion3(opts=0x90) == E["FLAGS"]                 # two tile bits
     assert _dion3(W=None) == E["NULL"] and _dion3(rows=None) == E["NULL"]

@@ -32,7 +32,9 @@ def test_config2_logspectrum():
     say("  max rel errs", err)
     assert err["bf16x3"] <= TOL_HALF
     assert err["f16"] <= TOL_HALF
-    assert err["bf16"] < 0.5          # plain bf16 products: degraded but not diverged
+    # plain bf16 products lose the small singular values: pinned near the
+    # measured 0.110 (a CPU model of the same rounding points gives 0.111-0.114)
+    assert 0.08 <= err["bf16"] <= 0.15
 
 
 def test_config3_dense_mlp():
@@ -81,7 +83,9 @@ def test_config5_fractional_rows():
     gns = need_gpu()
     X = synth.workload_batch(5)
     rows = synth.workload_rows(5)
-    init = torch.zeros_like(X)
+    # seeded random values in every row, so that a kernel writing zeros (or
+    # anything) into an unselected row is caught bit for bit
+    init = torch.from_numpy(np.random.default_rng(555).standard_normal(X.shape, dtype=np.float32)).to(X.dtype)
     out = init.cuda()
     say("config5 gram rows")
     gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,), row_idx=rows.cuda(), out=out)
@@ -93,6 +97,6 @@ def test_config5_fractional_rows():
         e = rel_err(synth.as_f64(oc[b][sel]), ref)
         mask = torch.ones(X.shape[1], dtype=torch.bool)
         mask[rows[b]] = False
-        assert torch.count_nonzero(oc[b][mask]).item() == 0
+        assert torch.equal(oc[b][mask], init[b][mask]), f"matrix {b}: an unselected row changed"
         say(f"  matrix {b}: {e:.4g}")
         assert e <= TOL_HALF

@@ -588,7 +588,9 @@ def test_gram_matrix_k_split(case):
     rows = None
     if case == "rows":
         rows = np.stack([np.sort(synth.row_subset(rows_n, n, seed=43, index=b)) for b in range(B)])
-        kw = dict(row_idx=torch.from_numpy(rows).cuda(), out=torch.zeros(B, rows_n, m, dtype=X.dtype, device="cuda"))
+        init = torch.from_numpy(np.random.default_rng(43).standard_normal((B, rows_n, m), dtype=np.float32))
+        init = init.to(X.dtype)
+        kw = dict(row_idx=torch.from_numpy(rows).cuda(), out=init.cuda())
     say(f"k split {case}")
     gns.timing_reset()
     gns.timing_enable(True)
@@ -605,6 +607,12 @@ def test_gram_matrix_k_split(case):
     # each stream of the batch fan-out forms its own Gram matrices, in two passes each
     assert len(parts_pass) == len(sum_pass) and len(parts_pass) in (grams, 2 * grams)
     got = synth.as_f64(out)
+    if case == "rows":
+        oc = out.cpu()
+        for b in range(B):
+            mask = torch.ones(rows_n, dtype=torch.bool)
+            mask[torch.from_numpy(rows[b])] = False
+            assert torch.equal(oc[b][mask], init[b][mask]), f"matrix {b}: an unselected row changed"
     for b in (0, B - 1):
         sel = rows[b] if case == "rows" else np.arange(n)
         ref = (oracle_standard if case == "standard" else oracle_gram)(X64[b][sel])
