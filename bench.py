@@ -116,12 +116,84 @@ def _pmc_per_dispatch(dirname, counter):
     return out
 
 
+# kernels after which the next symmetric product of a call is a Gram matrix
+# (the input pass, or a restart's Q X)
+_BEFORE_GRAM = ("transpose_sumsq", "norm_finish", "norm_partial", "scale_transpose", "scale_rows_f32")
+
+
+def classify(dispatches):
+    """{dispatch id: kernel name} -> {dispatch id: short name}, with the
+    symmetric products split into ':gram' (a Gram matrix: the first symmetric
+    launch after the input pass or after a general product) and ':nxn' (the
+    n x n iteration).  Valid for one-stream runs, where dispatch order is call
+    order."""
+    out, prev = {}, ""
+    for i in sorted(dispatches):
+        name = short_kernel(dispatches[i])
+        if name.startswith("gemm_nt<") and name.endswith(",sym>"):
+            name += ":gram" if (prev in _BEFORE_GRAM or prev.endswith(",gen>")) else ":nxn"
+        out[i] = name
+        prev = name.split(":")[0]
+    return out
+
+
+def summarize_mfma(dirname, workload):
+    """MFMA utilisation and clock per kernel kind from a rocprofv3 --pmc run of
+    SQ_INSTS_VALU_MFMA_MOPS_<dtype>, SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE with --kernel-trace (one-stream bench run).
+    - utilisation = busy cycles summed over the 1024 SIMDs / (cycles x 1024);
+    - clock = GRBM_GUI_ACTIVE summed over the 8 XCDs / 8 / kernel duration (the
+      GPU-active count also covers a few microseconds of dispatch, so short
+      kernels read high);
+    - executed TFLOP/s = MOPS x 512 FLOP / duration."""
+    rows = _csv(_find(dirname, "counter_collection.csv"))
+    trace = {int(r["Dispatch_Id"]): r for r in _csv(_find(dirname, "kernel_trace.csv"))}
+    cnt, names = {}, {}
+    for r in rows:
+        i = int(r["Dispatch_Id"])
+        names[i] = r["Kernel_Name"]
+        c = cnt.setdefault(i, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    kinds = classify(names)
+    agg = {}
+    for i, c in cnt.items():
+        t = trace.get(i)
+        if t is None or "MOPS" not in " ".join(c):
+            continue
+        dur = (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) * 1e-9
+        mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
+        if dur <= 0 or mops == 0:
+            continue
+        # a symmetric launch counts toward its kernel and its kind
+        for nm in {kinds[i], kinds[i].split(":")[0]}:
+            a = agg.setdefault(nm, {"n": 0, "dur": 0.0, "busy": 0.0, "cycles": 0.0, "flops": 0.0})
+            a["n"] += 1
+            a["dur"] += dur
+            a["busy"] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            a["cycles"] += c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+            a["flops"] += mops * 512.0
+    print(f"{'kernel':36s} {'launches':>8s} {'avg_us':>9s} {'mfma_util':>9s} {'clock_GHz':>9s} {'exec_TFLOPs':>11s}")
+    for name, a in sorted(agg.items()):
+        util = a["busy"] / (a["cycles"] * 1024.0)
+        clock = a["cycles"] / a["dur"] / 1e9
+        tf = a["flops"] / a["dur"] / 1e12
+        print(f"{name:36s} {a['n']:8d} {a['dur'] / a['n'] * 1e6:9.1f} {util:9.3f} {clock:9.3f} {tf:11.1f}")
+        print("MFMA " + json.dumps({"kernel": name, "launches": a["n"], "avg_launch_ms": a["dur"] / a["n"] * 1e3,
+                                    "mfma_util": util, "clock_ghz": clock, "exec_tflops": tf,
+                                    "exec_flops_per_launch": a["flops"] / a["n"], "workload": workload,
+                                    "source_sha256_16": kernel_source_hash()}))
+
+
 def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
     """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scaled by the
     reading of the calibration copy (a device copy of calib_mib MiB, which
     reads and writes exactly that many bytes)."""
     fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    for src in (fetch, write):
+        kinds = classify({i: d["kernel"] for i, d in src.items()})
+        for i, d in src.items():
+            d["kind"] = kinds[i]
     def first(d, pred):
         for k in sorted(d):
             if pred(d[k]["kernel"]):
@@ -140,8 +212,10 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
             name = short_kernel(d["kernel"])
             if not (name.startswith("gemm_n") or name in HBM_KERNELS):
                 continue
-            a = agg.setdefault(name, {"fetch": [], "write": []})
-            a[key].append(d["v"] * 1024.0 * scale)
+            # every symmetric launch counts toward its kernel and its kind
+            for nm in {name, d["kind"]}:
+                a = agg.setdefault(nm, {"fetch": [], "write": []})
+                a[key].append(d["v"] * 1024.0 * scale)
     print(f"{'kernel':34s} {'launches':>8s} {'fetch_MiB/launch':>17s} {'write_MiB/launch':>17s}")
     for name, a in sorted(agg.items()):
         nf = max(len(a["fetch"]), 1)
@@ -157,6 +231,26 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
 
 HBM_KERNELS = ("norm_partial", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish", "momentum_l1",
                "row_sumsq", "normuon_factors", "dion3_update", "select_topk")
+
+
+def mfma_from_profile(kernel, workload):
+    """The MFMA record of `kernel` on `workload` written by --summarize-mfma
+    into profiles/, or None when absent or taken on a different kernel
+    source."""
+    try:
+        names = [n for n in os.listdir(PROFILES) if n.endswith(".txt")]
+    except FileNotFoundError:
+        return None
+    h = kernel_source_hash()
+    for n in names:
+        with open(os.path.join(PROFILES, n)) as f:
+            for line in f:
+                if line.startswith("MFMA "):
+                    rec = json.loads(line[len("MFMA "):])
+                    if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                            and rec.get("source_sha256_16") == h):
+                        return rec
+    return None
 
 
 def traffic_from_profile(kernel, workload):
@@ -223,6 +317,15 @@ def bench_dion3_step(gns, synth, torch, w, coeffs, restarts, stream, steps=10):
             "hbm_kernels": kernels}
 
 
+def desc_of(cfg):
+    return {
+        2: "16 x 1024x4096 bf16, log-uniform spectrum [1e-4,1]",
+        3: "8 x 4096x16384 bf16 dense-MLP momentum, N(0,0.02^2) normalised",
+        4: "64 x 2048x7168 bf16 MoE expert stack, Student-t nu=3 normalised",
+        5: "8 x 4096x16384 bf16 N(0,1), 1024 seeded rows per matrix gathered/scattered",
+    }[cfg]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,9 +350,17 @@ def main():
                     help="print a summary of a rocprofv3 --kernel-trace --stats csv directory and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM traffic from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="print MFMA utilisation and clock per kernel from a rocprofv3 --pmc run and exit")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the timing of the other workloads (16 x 1024x4096 in bf16x3 and fp16, "
+                         "64 x 2048x7168, 8 x 4096x16384 with 1024 selected rows)")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.workload)
         return
     if args.summarize_pmc:
         # records of the Dion3 update are tagged apart from the workload's own call
@@ -314,21 +425,32 @@ def main():
         gns.standard_ns_batched(Xd, coeffs, row_idx=rows_d, out=out, compute_dtype=cdt,
                                 workspace=ws, stream=stream, split_batch=split)
 
-    def timed(fn, steps, warmup, per_launch=False):
+    def timed(fn, steps, warmup, per_launch=False, per_step=None):
+        """Mean ms per step over `steps` calls between two events on the
+        caller's stream (the library's streams join it after every call).
+        per_step, when a list, receives each call's ms from an event recorded
+        before every call."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         if per_launch:
             gns.timing_reset()
             gns.timing_enable(True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if per_step is not None else None
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(stream)
-        for _ in range(steps):
+        for i in range(steps):
+            if ev:
+                ev[i].record(stream)
             fn()
+        if ev:
+            ev[steps].record(stream)
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if ev:
+            per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
         recs = []
         if per_launch:
             gns.timing_enable(False)
@@ -340,7 +462,10 @@ def main():
     # every launch has the GPU to itself and its duration measures the kernel.
     ms, wall, recs = timed(step_one_stream, args.steps, args.warmup, per_launch=True)
     # the headline number: no per-launch events, batch split over two streams
-    ms_clean, wall_clean, _ = timed(step, args.steps, 1, per_launch=False)
+    # (one event per call gives the median and the interquartile range)
+    step_ms = []
+    ms_clean, wall_clean, _ = timed(step, args.steps, 1, per_launch=False, per_step=step_ms)
+    q1, med, q3 = (float(v) for v in np.percentile(step_ms, [25, 50, 75]))
     ms_one, _, _ = timed(step_one_stream, args.steps, 1, per_launch=False) if split else (ms_clean, 0, 0)
 
     alg_flops = w.batch * flops_gram(rows, w.m, T, len(restarts))
@@ -377,6 +502,18 @@ def main():
         "launches_per_step": dom["launches"] / args.steps,
         "share_of_step": round(dom["ms"] / args.steps / ms, 4),
     }
+    # MFMA counters of the same kernel (rocprofv3 --pmc, summarised into
+    # profiles/ by --summarize-mfma): busy fraction of the matrix cores and
+    # the sustained clock, with the peak at that clock (256 CUs x 4096 dense
+    # bf16 FLOP per clock)
+    mf = mfma_from_profile(dom_name, args.workload)
+    if mf:
+        roofline["mfma_util"] = round(mf["mfma_util"], 4)
+        roofline["clock_ghz"] = round(mf["clock_ghz"], 3)
+        roofline["peak_at_clock"] = round(256 * 4096 * mf["clock_ghz"] * 1e9 / 1e12, 1)
+        roofline["frac_at_clock"] = round(dom_tflops / roofline["peak_at_clock"], 4)
+    else:
+        roofline["mfma_util"] = roofline["clock_ghz"] = None
     kernels = {k: {"ms_per_step": round(v["ms"] / args.steps, 4),
                    "avg_launch_ms": round(v["ms"] / v["launches"], 4),
                    "tflops": round(v["flops"] / (v["ms"] / 1e3) / 1e12, 2) if v["ms"] > 0 else None,
@@ -421,6 +558,56 @@ def main():
     if not args.one_stream and not args.no_dion3:
         dion3 = bench_dion3_step(gns, synth, torch, w, coeffs, restarts, stream)
 
+    # the other workloads, each timed as one call per step like the headline
+    # (median and interquartile range over the steps); the row subset also
+    # reports the HBM rate of its gather (the norm pass and the scaled copy of
+    # the selected rows, from the library's per-launch events)
+    others = None
+    if not args.one_stream and not args.no_other_workloads and args.workload == 3:
+        del Xd, out, ws
+        torch.cuda.empty_cache()
+        others = {}
+        for cfg, computes in ((2, ("bf16x3", "f16", "bf16")), (4, ("bf16",)), (5, ("bf16",))):
+            wo = synth.WORKLOADS[cfg]
+            log(f"generating workload {cfg}: {wo.batch} x {wo.n}x{wo.m}")
+            Xo = synth.workload_batch(cfg).cuda()
+            ro = synth.workload_rows(cfg)
+            ro = ro.cuda() if ro is not None else None
+            rows_o = wo.k or wo.n
+            oo = torch.zeros_like(Xo)
+            entry = {"workload": desc_of(cfg), "batch": wo.batch, "n": rows_o, "m": wo.m}
+            for comp in computes:
+                cd = {"bf16": torch.bfloat16, "f16": torch.float16, "bf16x3": "bf16x3"}[comp]
+                wso = torch.empty(gns.gram_workspace_bytes(cd, wo.batch, rows_o, wo.m), dtype=torch.uint8,
+                                  device="cuda")
+
+                def call(split_batch=True):
+                    gns.gram_ns_batched(Xo, coeffs, restarts, row_idx=ro, out=oo, compute_dtype=cd,
+                                        workspace=wso, stream=stream, split_batch=split_batch)
+                per = []
+                mo, _, _ = timed(call, 10, 2, per_step=per)
+                fl = wo.batch * flops_gram(rows_o, wo.m, T, len(restarts))
+                med_o = float(np.median(per))
+                e = {"ms_per_step": round(mo, 4), "median_ms": round(med_o, 4),
+                     "iqr_ms": [round(float(v), 4) for v in np.percentile(per, [25, 75])],
+                     "matrices_per_s": round(wo.batch / (mo / 1e3), 1),
+                     "alg_tflops": round(fl / (mo / 1e3) / 1e12, 1),
+                     "pct_peak": round(100 * fl / (mo / 1e3) / 1e12 / PEAK_TFLOPS[comp], 2)}
+                if cfg == 5:
+                    _, _, rec5 = timed(lambda: call(False), 3, 1, per_launch=True)
+                    g = [(by, kms) for name, kern, fl_, by, kms in rec5
+                         if name in ("norm_partial", "scale_transpose")]
+                    gb, gms = sum(b for b, _ in g), sum(t for _, t in g)
+                    e["gather"] = {"kernels": "norm_partial + scale_transpose (selected rows)",
+                                   "ms_per_step": round(gms / 3, 4),
+                                   "gbs": round(gb / (gms / 1e3) / 1e9, 1) if gms > 0 else None,
+                                   "frac_hbm": round(gb / (gms / 1e3) / 1e9 / HBM_PEAK_GBS, 3) if gms > 0 else None}
+                entry[comp] = e
+                del wso
+            others[str(cfg)] = entry
+            del Xo, oo
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -440,12 +627,7 @@ def main():
         cpu = {"value": round(1.0 / dt, 5), "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
                "sample": f"1 of the {w.batch} matrices ({rows}x{w.m}), fp64 numpy Gram NS, {dt:.1f} s"}
 
-    desc = {
-        2: "16 x 1024x4096 bf16, log-uniform spectrum [1e-4,1]",
-        3: "8 x 4096x16384 bf16 dense-MLP momentum, N(0,0.02^2) normalised",
-        4: "64 x 2048x7168 bf16 MoE expert stack, Student-t nu=3 normalised",
-        5: "8 x 4096x16384 bf16 N(0,1), 1024 seeded rows per matrix gathered/scattered",
-    }[args.workload]
+    desc = desc_of(args.workload)
     line = {
         "metric": "orthogonalized matrices/s + bf16 MFMA TFLOP/s (% peak), 4096x16384 Gram-NS T=5",
         "value": round(value, 3),
@@ -463,6 +645,8 @@ def main():
                    "batch": w.batch, "n": rows, "m": w.m, "parallelism": "single GPU"},
         "alg_tflops": round(tflops, 2),
         "pct_peak": round(100 * tflops / peak, 2),
+        "median_ms": round(med, 4),
+        "iqr_ms": [round(q1, 4), round(q3, 4)],
         "ms_per_step_with_launch_events": round(ms, 4),
         "ms_per_step_one_stream": round(ms_one, 4),
         "batch_split_over_streams": split,
@@ -471,6 +655,7 @@ def main():
         "standard_ns5": std,
         "dion3_select_l1": sel,
         "dion3_step": dion3,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
 

@@ -128,8 +128,21 @@ def _fill(out: torch.Tensor, make) -> torch.Tensor:
     depend on the pool size."""
     def one(b):
         out[b] = make(b)
-    with ThreadPoolExecutor(_workers(out.shape[0])) as ex:
-        list(ex.map(one, range(out.shape[0])))
+    workers = _workers(out.shape[0])
+    # one BLAS thread per worker: the pool already uses every core, and
+    # nested BLAS threads oversubscribe them (16 Haar-spectrum matrices of
+    # 1024 x 4096: 112 s with 8 x 8 threads, a few seconds with 8 x 1)
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas") if workers > 1 else None
+    except ImportError:  # pragma: no cover
+        limit = None
+    try:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(out.shape[0])))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
     return out
 
 
