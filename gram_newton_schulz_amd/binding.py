@@ -42,6 +42,7 @@ EXPORTS = [
     "gns_select_workspace_bytes", "gns_select_rows_l1",
     "gns_dion3_workspace_bytes", "gns_dion3_step", "gns_tuned_tile", "gns_autotune_clear",
     "gns_call_plan", "gns_check_finite", "gns_select_count", "gns_safety_scale",
+    "gns_gram_batched_noalloc",
 ]
 
 
@@ -114,6 +115,11 @@ def lib() -> ctypes.CDLL:
     L.gns_autotune_clear.argtypes = []
     L.gns_check_row_idx.restype = ctypes.c_int
     L.gns_check_row_idx.argtypes = [vp, i64, i64, i64, vp, vp]
+    L.gns_gram_batched_noalloc.restype = ctypes.c_int
+    L.gns_gram_batched_noalloc.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_double), ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_int), ctypes.c_int, vp, i64,
+                                           ctypes.c_uint, vp]
     L.gns_call_plan.restype = ctypes.c_int
     L.gns_call_plan.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                 ctypes.POINTER(ctypes.c_double), ctypes.c_int,
@@ -299,6 +305,32 @@ def standard_ns_batched(X: torch.Tensor, coeffs: Sequence, *,
         | (GNS_OPT_DEBUG_CHECKS if debug_checks else 0),
         _ptr(ws), ws.numel(), _stream(stream)))
     return out.squeeze(0) if squeeze else out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def gram_ns_batched_noalloc(X: torch.Tensor, out: torch.Tensor, coeffs: Sequence,
+                            restarts: Sequence[int] = (2,), *, row_idx: Optional[torch.Tensor] = None,
+                            compute_dtype=None, naive_algebra: bool = False,
+                            square_fallback: bool = True, tile=None, stream=None) -> torch.Tensor:
+    """gns_gram_batched_noalloc: Gram Newton-Schulz with the library's own
+    fixed device array (NOALLOC_SCRATCH_BYTES per GPU) as the workspace; the
+    call itself allocates nothing.  ``out`` is required (allocate it
+    beforehand); everything runs on ``stream``."""
+    Xb, row_idx, outb, squeeze, k = _prepare(X, row_idx, out)
+    B, n, m = Xb.shape
+    cdt = _dtype_code(Xb.dtype if compute_dtype is None else compute_dtype)
+    carr, T = _coeff_array(coeffs)
+    rs = list(restarts)
+    rarr = (ctypes.c_int * max(len(rs), 1))(*rs)
+    _check(lib().gns_gram_batched_noalloc(
+        _ptr(Xb), _ptr(outb), B, n, m, _dtype_code(Xb.dtype), cdt, carr, T, rarr, len(rs),
+        _ptr(row_idx), k,
+        (GNS_OPT_NAIVE_ALGEBRA if naive_algebra else 0)
+        | (0 if square_fallback else GNS_OPT_NO_SQUARE_FALLBACK) | _tile_opts(tile),
+        _stream(stream)))
+    return out
 
 
 def call_plan(standard: bool, X_ptr: int, out_ptr: int, batch: int, n: int, m: int, io_dtype,

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgns.so")
-SOURCES = ["gns_kernels.hip", "gns_host.cpp"]
+SOURCES = ["gns_kernels.hip", "gns_host.cpp", "gns_noalloc.cpp"]
 ARCH = "gfx950"
 
 

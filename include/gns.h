@@ -264,6 +264,32 @@ gns_status gns_call_plan(int standard, const void *X, const void *out, int64_t b
                          const int64_t *row_idx, int64_t k, unsigned opts, gns_plan_info *info);
 
 /*
+ * gns_gram_batched for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The workspace is a device array inside the library of
+ * GNS_NOALLOC_SCRATCH_BYTES (128 MiB), one per GPU, held from the library's
+ * first use of it on that GPU until the process ends; its device address is
+ * looked up once per device.  Arguments as for gns_gram_batched, without
+ * the workspace.  The call allocates nothing and creates no streams or
+ * events: it always runs on `stream` (GNS_OPT_ONE_STREAM is implied) with
+ * the size rule's tiles.
+ *   - A problem whose gns_gram_workspace_bytes exceeds the array returns
+ *     GNS_E_WORKSPACE before anything is enqueued (for example 4 x 1024x4096
+ *     bf16 needs 156 MiB; 2 x 1024x4096, 78 MiB, fits).
+ *   - GNS_OPT_TILE_AUTOTUNE and GNS_OPT_DEBUG_CHECKS return GNS_E_FLAGS.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind; nothing in it needs to start at zero.  Calls that overlap in
+ *     time on one GPU (two streams, or two host threads) race on the array
+ *     and give wrong results: order them on one stream.
+ */
+#define GNS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gns_status gns_gram_batched_noalloc(const void *X, void *out, int64_t batch, int64_t n, int64_t m,
+                                    gns_dtype io_dtype, gns_dtype compute_dtype,
+                                    const double *coeffs, int T, const int *restart_after,
+                                    int n_restart, const int64_t *row_idx, int64_t k, unsigned opts,
+                                    void *stream);
+
+/*
  * Row selection of the Dion3 update ("Dion3: Full-Stack Orthogonal Updates",
  * §6, Algorithm 4, selection step): for every matrix M_b, the indices of the
  * k rows with the largest l1 norm sum_j |M_b[i][j]|, written to
