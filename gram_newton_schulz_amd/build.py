@@ -38,14 +38,39 @@ def build(verbose: bool = False) -> str:
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", tmp,
     ]
+    # the compiler's resource report of every kernel (checked below)
+    cmd.insert(-2, "-Rpass-analysis=kernel-resource-usage")
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    spills = scratch_users(res.stderr)
+    if spills:
+        raise RuntimeError("GEMM kernels that use scratch memory: " + ", ".join(spills))
     os.replace(tmp, LIB)
     return LIB
+
+
+def scratch_users(report: str) -> list:
+    """Names of GEMM kernels whose resource report shows scratch memory.
+
+    The GEMM main loop waits on explicit counts of its own outstanding
+    LDS-DMA loads and sets m0 inside inline assembly; both assume that the
+    compiler adds no memory traffic and keeps nothing of its own in m0,
+    which spilling to scratch would break.  A build in which any GEMM kernel
+    spills is therefore refused."""
+    out, name = [], None
+    for line in report.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif name and "gemm_nt" in name and ("ScratchSize [bytes/lane]:" in line or "VGPRs Spill:" in line
+                                               or "SGPRs Spill:" in line):
+            val = int(line.split(":")[-1].split("[")[0].strip())
+            if val > 0 and name not in out:
+                out.append(name)
+    return out
 
 
 if __name__ == "__main__":

@@ -418,3 +418,20 @@ def test_binding_tile_option():
     assert binding._tile_opts("mixed") == binding.GNS_OPT_TILE_MIXED
     with pytest.raises(gns.GnsError):
         binding._tile_opts(64)
+
+
+def test_build_refuses_spilling_gemm_kernels():
+    """The GEMM kernels' hand-counted DMA waits and m0 use assume no spills:
+    the build parses the compiler's resource report and names any GEMM
+    kernel that uses scratch."""
+    from gram_newton_schulz_amd.build import scratch_users
+    ok = ("remark: Function Name: _ZN3gns7gemm_ntINS_5EBF16ELi256E [-Rpass-analysis]\n"
+          "remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis]\n"
+          "remark:     VGPRs Spill: 0 [-Rpass-analysis]\n"
+          "remark: Function Name: _ZN3gns9norm_partialI [-Rpass-analysis]\n"
+          "remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis]\n")
+    assert scratch_users(ok) == []
+    bad = ok + ("remark: Function Name: _ZN3gns7gemm_ntINS_4EF32ELi256E [-Rpass-analysis]\n"
+                "remark:     ScratchSize [bytes/lane]: 720 [-Rpass-analysis]\n"
+                "remark:     VGPRs Spill: 180 [-Rpass-analysis]\n")
+    assert scratch_users(bad) == ["_ZN3gns7gemm_ntINS_4EF32ELi256E"]
