@@ -48,12 +48,18 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-// Round to nearest even; NaN stays NaN.
+// Round to nearest even; NaN stays NaN.  gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction): checked against the
+// integer rounding (u + 0x7fff + lsb) >> 16 on every fp32 bit pattern, in
+// both halves, on the GPU.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(f32x2_to_bf16x2(f, 0.0f));
 }
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
@@ -61,18 +67,24 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), f16x2_t));
+}
 
 struct EBF16 {
   using S = uint16_t;
   static constexpr int code = DT_BF16;
   __device__ static float ld(S v) { return bf16_to_f32(v); }
   __device__ static S st(float f) { return f32_to_bf16(f); }
+  // two values rounded into one packed pair (lo in bits 0-15)
+  __device__ static uint32_t st2(float lo, float hi) { return f32x2_to_bf16x2(lo, hi); }
 };
 struct EF16 {
   using S = uint16_t;
   static constexpr int code = DT_F16;
   __device__ static float ld(S v) { return f16_to_f32(v); }
   __device__ static S st(float f) { return f32_to_f16(f); }
+  __device__ static uint32_t st2(float lo, float hi) { return f32x2_to_f16x2(lo, hi); }
 };
 struct EF32 {
   using S = float;
@@ -614,8 +626,8 @@ gemm_nt(GemmParams p) {
   if (nk > 0) {
     using Frag = typename Mma<E>::Frag;
     auto dma_stage = [&](int stage) {
-      const int st = stage < nk ? stage : nk - 1;   // past the end: harmless reload
       const uint32_t buf_lds = lds_base + static_cast<uint32_t>((stage % NST) * STB);
+      const int st = stage < nk ? stage : nk - 1;   // past the end: harmless reload
 #pragma unroll
       for (int q = 0; q < BPW; ++q) {
         const int blk = wave_u + q * NW;
@@ -848,9 +860,7 @@ gemm_nt(GemmParams p) {
           dv[ib] = alpha * v;
         }
 #pragma unroll
-        for (int h = 0; h < 8; ++h)
-          pk[ib][jb][h] = static_cast<uint32_t>(T::st(alpha * acc[ib][jb][2 * h])) |
-                          (static_cast<uint32_t>(T::st(alpha * acc[ib][jb][2 * h + 1])) << 16);
+        for (int h = 0; h < 8; ++h) pk[ib][jb][h] = T::st2(alpha * acc[ib][jb][2 * h], alpha * acc[ib][jb][2 * h + 1]);
       }
     }
   };
