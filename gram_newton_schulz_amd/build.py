@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgns.so")
+# measurement build: every GEMM workgroup records timestamps (GNS_TIMELINE in
+# gns_kernels.hip); read by gram_newton_schulz_amd.timeline
+TIMELINE_LIB = os.path.join(HERE, "libgns_timeline.so")
 SOURCES = ["gns_kernels.hip", "gns_host.cpp", "gns_noalloc.cpp"]
 ARCH = "gfx950"
 
@@ -25,8 +28,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm required to build the HIP library)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    target = TIMELINE_LIB if timeline else LIB
+    tmp = target + ".tmp"
     cmd = [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 instructions are kept out of all generated code
@@ -35,6 +39,7 @@ def build(verbose: bool = False) -> str:
         # counters; a larger budget keeps them fully unrolled (in registers)
         "-mllvm", "-pragma-unroll-threshold=200000",
         "-I", INCLUDE, "-I", CSRC,
+        *(["-DGNS_TIMELINE"] if timeline else []),
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", tmp,
     ]
@@ -49,8 +54,8 @@ def build(verbose: bool = False) -> str:
     spills = scratch_users(res.stderr)
     if spills:
         raise RuntimeError("GEMM kernels that use scratch memory: " + ", ".join(spills))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 def scratch_users(report: str) -> list:
@@ -74,4 +79,4 @@ def scratch_users(report: str) -> list:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

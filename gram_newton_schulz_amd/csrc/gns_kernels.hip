@@ -290,6 +290,63 @@ __device__ __forceinline__ void sym_tile(int t, int nt, int bb, int hh, int *ti,
   *ti = J * bb + r - bj * (bj + 1) / 2;
 }
 
+// Timeline build (compiled with GNS_TIMELINE; the build script's --timeline
+// option makes libgns_timeline.so): every GEMM workgroup records the
+// constant 100 MHz clock (s_memrealtime) at entry, when its prologue is done,
+// when its main loop is done and when its last store has completed, the
+// shader-clock cycles in between (s_memtime), its tile, and the CU and queue
+// it ran on.  The work itself is unchanged; in the library build the marks
+// compile to nothing.
+#ifdef GNS_TIMELINE
+constexpr unsigned kTimelineMax = 1u << 18;   // records (64 bytes each)
+__device__ unsigned long long g_timeline[kTimelineMax][8];
+__device__ unsigned int g_timeline_n;
+struct Timeline {
+  unsigned long long t0, t1, t2, c0, tile;
+  int mode, K;
+  __device__ __forceinline__ Timeline(int mode_, int K_) : tile(0), mode(mode_), K(K_) {
+    t0 = t1 = t2 = __builtin_amdgcn_s_memrealtime();
+    c0 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void prologue_done() { t1 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ __forceinline__ void loop_done() { t2 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ __forceinline__ void set_tile(int ti, int tj, int mat) {
+    tile = static_cast<unsigned long long>(ti) | (static_cast<unsigned long long>(tj) << 16) |
+           (static_cast<unsigned long long>(mat) << 32);
+  }
+  // at every exit of the kernel: every wave's stores have completed
+  __device__ __forceinline__ ~Timeline() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const unsigned long long t3 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long c3 = __builtin_amdgcn_s_memtime();
+    unsigned hw = 0, xcc = 0;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if (threadIdx.x == 0) {
+      const unsigned slot = atomicAdd(&g_timeline_n, 1u);
+      if (slot < kTimelineMax) {
+        unsigned long long *r = g_timeline[slot];
+        r[0] = t0; r[1] = t1; r[2] = t2; r[3] = t3;
+        r[4] = c3 - c0;
+        r[5] = tile;
+        r[6] = static_cast<unsigned long long>(static_cast<unsigned>(K)) |
+               (static_cast<unsigned long long>(gridDim.x & 0xffffffu) << 32) |
+               (static_cast<unsigned long long>(mode) << 56);
+        r[7] = static_cast<unsigned long long>(hw) | (static_cast<unsigned long long>(xcc) << 32);
+      }
+    }
+  }
+};
+#else
+struct Timeline {
+  __device__ __forceinline__ Timeline(int, int) {}
+  __device__ __forceinline__ void prologue_done() {}
+  __device__ __forceinline__ void loop_done() {}
+  __device__ __forceinline__ void set_tile(int, int, int) {}
+};
+#endif
+
 // BK = 0: both operands row-major along K (C = A B^T).  BK = 1: B is stored
 // K-major, B[k][n] row-major with n contiguous (C = A B), read with the LDS
 // transpose load; 256-edge 16-bit tiles, general results only.
@@ -298,6 +355,7 @@ __device__ __forceinline__ void sym_tile(int t, int nt, int bb, int hh, int *ti,
 template <class E, int TILE, int MODE, int PL, int BK = 0, int KS = 0>
 __global__ void __launch_bounds__(WaveLayout<TILE>::THREADS)
 gemm_nt(GemmParams p) {
+  Timeline tl(MODE | (BK << 2) | (KS << 3) | ((TILE == 256) << 5), p.K);
   using S = typename E::S;
   using St = Store<E, PL>;
   constexpr int ESZ = sizeof(S);
@@ -372,6 +430,7 @@ gemm_nt(GemmParams p) {
     }
   }
 
+  tl.set_tile(ti, tj, mat);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -725,6 +784,7 @@ gemm_nt(GemmParams p) {
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
       __syncthreads();
       if (g1) __syncthreads();
+      tl.prologue_done();
       // the same barrier sequence in both versions of the loop: the half
       // waves of a diagonal tile run the one that skips column blocks 2, 3
       auto loop = [&](auto nj) {
@@ -763,6 +823,7 @@ gemm_nt(GemmParams p) {
       static_assert(LPS * (NST - 2) < 64, "wait count out of range");
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 2)) : "memory");
       __syncthreads();
+      tl.prologue_done();
       fload(0, 0, 0, std::integral_constant<int, NBJ>{});
 
       int buf = 0;                            // buffer of stage i
@@ -798,6 +859,7 @@ gemm_nt(GemmParams p) {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    tl.loop_done();
   } else if (has_d) {
     load_d();
     init_from_d();
@@ -2073,3 +2135,23 @@ hipError_t launch_dion3_update(float *W, float *M, const float *O, const int64_t
 }
 
 }  // namespace gns
+
+#ifdef GNS_TIMELINE
+// Timeline build only: copies up to max_rec records (8 x uint64 each, see
+// Timeline) to host memory dst, stores the number recorded since the last
+// reset in *n_out, and with reset != 0 starts a new recording.  Returns 0, or
+// the step that failed (1-3).
+extern "C" int gns_timeline_read(void *dst, unsigned max_rec, unsigned *n_out, int reset) {
+  unsigned n = 0;
+  if (hipMemcpyFromSymbol(&n, HIP_SYMBOL(gns::g_timeline_n), sizeof(n)) != hipSuccess) return 1;
+  *n_out = n;
+  unsigned c = n < max_rec ? n : max_rec;
+  if (c > gns::kTimelineMax) c = gns::kTimelineMax;
+  if (c && dst && hipMemcpyFromSymbol(dst, HIP_SYMBOL(gns::g_timeline), size_t(c) * 64) != hipSuccess) return 2;
+  if (reset) {
+    const unsigned z = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(gns::g_timeline_n), &z, sizeof(z)) != hipSuccess) return 3;
+  }
+  return 0;
+}
+#endif
