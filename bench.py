@@ -184,6 +184,45 @@ def summarize_mfma(dirname, workload):
                                     "source_sha256_16": kernel_source_hash()}))
 
 
+def summarize_counters(dirname, workload):
+    """Every counter of a rocprofv3 --pmc --kernel-trace run (one stream),
+    per kernel kind: the sum per launch and, for SQ cycle counts, the share
+    of CU cycles (sum / (GRBM_GUI_ACTIVE / 8 x 256 CUs); SQ counters are
+    summed over the CUs of each shader engine, GRBM_GUI_ACTIVE over the 8
+    XCDs)."""
+    rows = _csv(_find(dirname, "counter_collection.csv"))
+    trace = {int(r["Dispatch_Id"]): r for r in _csv(_find(dirname, "kernel_trace.csv"))}
+    cnt, names = {}, {}
+    for r in rows:
+        i = int(r["Dispatch_Id"])
+        names[i] = r["Kernel_Name"]
+        c = cnt.setdefault(i, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    kinds = classify(names)
+    agg = {}
+    for i, c in cnt.items():
+        t = trace.get(i)
+        if t is None:
+            continue
+        a = agg.setdefault(kinds[i], {"n": 0, "dur": 0.0, "c": {}})
+        a["n"] += 1
+        a["dur"] += (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) * 1e-9
+        for k, v in c.items():
+            a["c"][k] = a["c"].get(k, 0.0) + v
+    for name, a in sorted(agg.items()):
+        cyc = a["c"].get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        rec = {"kernel": name, "launches": a["n"], "avg_launch_us": round(a["dur"] / a["n"] * 1e6, 1),
+               "workload": workload, "source_sha256_16": kernel_source_hash()}
+        if cyc > 0:
+            rec["clock_ghz"] = round(cyc / a["dur"] / 1e9, 3)
+        rec["per_launch"] = {k: v / a["n"] for k, v in sorted(a["c"].items())}
+        if cyc > 0:
+            rec["per_cu_cycle"] = {k: round(v / (cyc * 256.0), 4) for k, v in sorted(a["c"].items())
+                                   if k.startswith("SQ_") and ("CYCLES" in k or "ACTIVE" in k or "CONFLICT" in k
+                                                               or "WAIT" in k)}
+        print("COUNTERS " + json.dumps(rec))
+
+
 def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
     """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scaled by the
     reading of the calibration copy (a device copy of calib_mib MiB, which
@@ -352,12 +391,17 @@ def main():
                     help="print per-kernel HBM traffic from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="print MFMA utilisation and clock per kernel from a rocprofv3 --pmc run and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print every counter per kernel kind from a rocprofv3 --pmc --kernel-trace run and exit")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the timing of the other workloads (16 x 1024x4096 in bf16x3 and fp16, "
                          "64 x 2048x7168, 8 x 4096x16384 with 1024 selected rows)")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, args.workload)
