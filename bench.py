@@ -312,6 +312,129 @@ def traffic_from_profile(kernel, workload):
     return None
 
 
+class SmiSampler:
+    """Socket power, gfx clocks and package-power throttling while the GPU
+    runs a workload, from the driver's GPU metrics table (amdsmi).  The
+    table refreshes about once a second, so the window must last a few
+    seconds; a thread polls it every `period` seconds and keeps each new
+    table.  Between the first and the last table of the window:
+    - power: energy accumulator difference (units of 15.259 uJ, 2^-16 J)
+      over the firmware timestamp difference (10 ns units);
+    - ppt_residency_frac: share of the accumulation ticks spent limited by
+      package power tracking;
+    - gfxclk: per-XCD clocks of the tables after the first.
+    Every field is None where the metrics cannot be read; the benchmark never
+    depends on them."""
+
+    ENERGY_J = 2.0 ** -16
+    FW_TICK_S = 1e-8
+
+    def __init__(self, period=0.05):
+        import threading
+        self.period, self.tables, self.h, self.smi = period, [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) == 1:        # one GPU per box here: no index mapping to get wrong
+                self.smi, self.h = amdsmi, hs[0]
+        except Exception:
+            self.smi = None
+
+    @staticmethod
+    def _num(v):
+        return float(v) if isinstance(v, (int, float)) and not isinstance(v, bool) else None
+
+    def _metrics(self):
+        try:
+            return self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        except Exception:
+            return None
+
+    def _keep(self, m):
+        if m is None:
+            return
+        ts = self._num(m.get("firmware_timestamp"))
+        if ts is None or (self.tables and self._num(self.tables[-1].get("firmware_timestamp")) == ts):
+            return
+        self.tables.append(m)
+
+    def _run(self):
+        import time as _t
+        while not self._stop.is_set():
+            self._keep(self._metrics())
+            _t.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.smi is not None:
+            self._keep(self._metrics())          # the table current at the start (pre-window)
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        """None without metrics or with fewer than two tables refreshed inside
+        the window (the table current at the start may predate the load)."""
+        if self.smi is None or len(self.tables) < 3:
+            return None
+        win = self.tables[1:]
+        first, last = win[0], win[-1]
+        out = {"tables": len(win), "socket_power_w": None, "ppt_residency_frac": None, "power_cap_w": None,
+               "gfxclk_mhz_mean": None, "gfxclk_mhz_min": None, "gfxclk_mhz_max": None}
+        try:
+            dE = self._num(last.get("energy_accumulator")) - self._num(first.get("energy_accumulator"))
+            dt = (self._num(last.get("firmware_timestamp")) - self._num(first.get("firmware_timestamp"))) * self.FW_TICK_S
+            if dt > 0:
+                out["socket_power_w"] = round(dE * self.ENERGY_J / dt, 1)
+        except Exception:
+            pass
+        try:
+            d_ppt = self._num(last.get("ppt_residency_acc")) - self._num(first.get("ppt_residency_acc"))
+            d_acc = self._num(last.get("accumulation_counter")) - self._num(first.get("accumulation_counter"))
+            if d_acc > 0:
+                out["ppt_residency_frac"] = round(d_ppt / d_acc, 4)
+        except Exception:
+            pass
+        clks = []
+        for m in win[1:] or win:
+            c = [self._num(v) for v in (m.get("current_gfxclks") or [])]
+            clks.extend(v for v in c if v and v < 10000)
+        if clks:
+            out["gfxclk_mhz_mean"] = round(sum(clks) / len(clks), 1)
+            out["gfxclk_mhz_min"], out["gfxclk_mhz_max"] = min(clks), max(clks)
+        try:
+            cap = self._num(self.smi.amdsmi_get_power_cap_info(self.h).get("power_cap"))
+            if cap:
+                out["power_cap_w"] = cap / 1e6 if cap > 1e5 else cap      # reported in microwatts
+        except Exception:
+            pass
+        return out
+
+
+def power_window(fn, torch, seconds=3.0):
+    """Run fn (one call) back to back for `seconds` under an SmiSampler and
+    return its summary; None (and no time spent) without GPU metrics."""
+    smi = SmiSampler()
+    if smi.smi is None:
+        return None
+    with smi:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+    return smi.summary()
+
+
 def bench_dion3_step(gns, synth, torch, w, coeffs, restarts, stream, steps=10):
     """One whole Dion3 update (Algorithm 4: momentum sum, l1 selection of
     k = n/4 rows, Gram NS of those rows, NorMuon, decay, row update, error
@@ -511,6 +634,15 @@ def main():
     ms_clean, wall_clean, _ = timed(step, args.steps, 1, per_launch=False, per_step=step_ms)
     q1, med, q3 = (float(v) for v in np.percentile(step_ms, [25, 50, 75]))
     ms_one, _, _ = timed(step_one_stream, args.steps, 1, per_launch=False) if split else (ms_clean, 0, 0)
+    # the same call back to back for a few seconds: socket power, package
+    # power throttling and gfx clocks from the driver's metrics, and the
+    # dense bf16 peak at that clock
+    log("power and clock window (3 s of the same call)")
+    power = power_window(step, torch)
+    if power and power.get("gfxclk_mhz_mean"):
+        power["peak_tflops_at_clock"] = round(256 * 4096 * power["gfxclk_mhz_mean"] * 1e6 / 1e12, 1)
+        power["pct_of_peak_at_clock"] = round(100 * w.batch * flops_gram(rows, w.m, T, len(restarts)) /
+                                              (ms_clean / 1e3) / 1e12 / power["peak_tflops_at_clock"], 2)
 
     alg_flops = w.batch * flops_gram(rows, w.m, T, len(restarts))
     value = w.batch / (ms_clean / 1e3)
@@ -695,6 +827,9 @@ def main():
         "ms_per_step_one_stream": round(ms_one, 4),
         "batch_split_over_streams": split,
         "roofline": roofline,
+        # socket power, package-power throttling and gfx clocks over 3 s of
+        # the headline call (driver GPU metrics; null where unavailable)
+        "gpu_power_clock": power,
         "cpu_baseline": cpu,
         "standard_ns5": std,
         "dion3_select_l1": sel,
