@@ -119,6 +119,11 @@ __device__ __forceinline__ uint2 ld_once(const uint2 *p) {
 }
 
 
+// Streaming passes keep kUnroll 16-byte pieces per lane in flight: all their
+// loads are issued before the first use, which one piece at a time (a single
+// load round trip per wave) left at about two thirds of HBM bandwidth.
+constexpr int kUnroll = 4;
+
 // One lane's share of a 16-deep slice of the contraction: 8 consecutive
 // elements (one 16-byte chunk for 16-bit types, two for fp32).  A and B
 // fragments use the same element -> k mapping, so the products pair up
@@ -1749,9 +1754,8 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
   double acc = 0.0;
   if (vec) {
     // four elements per piece: 16 bytes of M, 16 (fp32) or 8 (16-bit) of G
-    for (int64_t v = lane; v < m / 4; v += 64) {
-      float4 mv = ld_once(reinterpret_cast<const float4 *>(mr) + v);
-      float g[4];
+    auto load = [&](int64_t v, float4 &mv, float *g) {
+      mv = ld_once(reinterpret_cast<const float4 *>(mr) + v);
       if constexpr (sizeof(SG) == 4) {
         const float4 gv = ld_once(reinterpret_cast<const float4 *>(gr) + v);
         g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
@@ -1762,6 +1766,8 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
         g[2] = TG::ld(static_cast<SG>(gv.y & 0xffffu));
         g[3] = TG::ld(static_cast<SG>(gv.y >> 16));
       }
+    };
+    auto finish = [&](int64_t v, float4 mv, const float *g) {
       mv.x += g[0];
       mv.y += g[1];
       mv.z += g[2];
@@ -1771,6 +1777,24 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
       acc += fabs(static_cast<double>(mv.y));
       acc += fabs(static_cast<double>(mv.z));
       acc += fabs(static_cast<double>(mv.w));
+    };
+    // kUnroll pieces per lane in flight: all their loads are issued before
+    // the first store (the lane's pieces are summed in the same order)
+    const int64_t nv = m / 4;
+    int64_t v = lane;
+    for (; v + 64 * (kUnroll - 1) < nv; v += 64 * kUnroll) {
+      float4 mv[kUnroll];
+      float g[kUnroll][4];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) load(v + 64 * u, mv[u], g[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) finish(v + 64 * u, mv[u], g[u]);
+    }
+    for (; v < nv; v += 64) {
+      float4 mv;
+      float g[4];
+      load(v, mv, g);
+      finish(v, mv, g);
     }
   } else {
     for (int64_t c = lane; c < m; c += 64) {
@@ -1795,13 +1819,23 @@ row_sumsq(const float *O, int64_t k, int64_t m, bool vec, double *rowsq) {
   const float *orow = O + (static_cast<int64_t>(b) * k + row) * m;
   double acc = 0.0;
   if (vec) {
-    for (int64_t v = lane; v < m / 4; v += 64) {
-      const float4 o = ld_once(reinterpret_cast<const float4 *>(orow) + v);
+    auto add = [&](const float4 &o) {
       acc += static_cast<double>(o.x) * o.x;
       acc += static_cast<double>(o.y) * o.y;
       acc += static_cast<double>(o.z) * o.z;
       acc += static_cast<double>(o.w) * o.w;
+    };
+    // kUnroll pieces per lane in flight, summed in the same order
+    const int64_t nv = m / 4;
+    int64_t v = lane;
+    for (; v + 64 * (kUnroll - 1) < nv; v += 64 * kUnroll) {
+      float4 o[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) o[u] = ld_once(reinterpret_cast<const float4 *>(orow) + v + 64 * u);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) add(o[u]);
     }
+    for (; v < nv; v += 64) add(ld_once(reinterpret_cast<const float4 *>(orow) + v));
   } else {
     for (int64_t c = lane; c < m; c += 64) acc += static_cast<double>(orow[c]) * orow[c];
   }
@@ -1882,13 +1916,24 @@ dion3_update(float *W, float *M, const float *O, const int64_t *S, const double 
   const int64_t slot = (lo < k && Sb[lo] == row) ? lo : -1;
   if (slot < 0 && decay == 1.0f) return;
   float *wr = W + (static_cast<int64_t>(b) * n + row) * m;
+  const int64_t nv = m / 4;
+  const int64_t step = blockDim.x;
   if (slot < 0) {
     if (vec) {
-      for (int64_t v = threadIdx.x; v < m / 4; v += blockDim.x) {
-        float4 w = ld_once(reinterpret_cast<const float4 *>(wr) + v);
+      auto scale = [&](int64_t v, float4 w) {
         w.x *= decay; w.y *= decay; w.z *= decay; w.w *= decay;
         st_once(reinterpret_cast<float4 *>(wr) + v, w);
+      };
+      // kUnroll pieces per thread in flight: loads first, then the stores
+      int64_t v = threadIdx.x;
+      for (; v + step * (kUnroll - 1) < nv; v += step * kUnroll) {
+        float4 w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) w[u] = ld_once(reinterpret_cast<const float4 *>(wr) + v + step * u);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) scale(v + step * u, w[u]);
       }
+      for (; v < nv; v += step) scale(v, ld_once(reinterpret_cast<const float4 *>(wr) + v));
     } else {
       for (int64_t c = threadIdx.x; c < m; c += blockDim.x) wr[c] *= decay;
     }
@@ -1898,10 +1943,7 @@ dion3_update(float *W, float *M, const float *O, const int64_t *S, const double 
   const float *orow = O + (static_cast<int64_t>(b) * k + slot) * m;
   float *mr = M + (static_cast<int64_t>(b) * n + row) * m;
   if (vec) {
-    for (int64_t v = threadIdx.x; v < m / 4; v += blockDim.x) {
-      float4 w = ld_once(reinterpret_cast<const float4 *>(wr) + v);
-      const float4 o = ld_once(reinterpret_cast<const float4 *>(orow) + v);
-      float4 mm = ld_once(reinterpret_cast<const float4 *>(mr) + v);
+    auto update = [&](int64_t v, float4 w, const float4 &o, float4 mm) {
       w.x = fmaf(-c, o.x, decay * w.x);
       w.y = fmaf(-c, o.y, decay * w.y);
       w.z = fmaf(-c, o.z, decay * w.z);
@@ -1909,7 +1951,22 @@ dion3_update(float *W, float *M, const float *O, const int64_t *S, const double 
       mm.x *= mu; mm.y *= mu; mm.z *= mu; mm.w *= mu;
       st_once(reinterpret_cast<float4 *>(wr) + v, w);
       st_once(reinterpret_cast<float4 *>(mr) + v, mm);
+    };
+    int64_t v = threadIdx.x;
+    for (; v + step * (kUnroll - 1) < nv; v += step * kUnroll) {
+      float4 w[kUnroll], o[kUnroll], mm[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        w[u] = ld_once(reinterpret_cast<const float4 *>(wr) + v + step * u);
+        o[u] = ld_once(reinterpret_cast<const float4 *>(orow) + v + step * u);
+        mm[u] = ld_once(reinterpret_cast<const float4 *>(mr) + v + step * u);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) update(v + step * u, w[u], o[u], mm[u]);
     }
+    for (; v < nv; v += step)
+      update(v, ld_once(reinterpret_cast<const float4 *>(wr) + v), ld_once(reinterpret_cast<const float4 *>(orow) + v),
+             ld_once(reinterpret_cast<const float4 *>(mr) + v));
   } else {
     for (int64_t j = threadIdx.x; j < m; j += blockDim.x) {
       wr[j] = fmaf(-c, orow[j], decay * wr[j]);
