@@ -516,6 +516,8 @@ def main():
                     help="print MFMA utilisation and clock per kernel from a rocprofv3 --pmc run and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print every counter per kernel kind from a rocprofv3 --pmc --kernel-trace run and exit")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the 3 s power and clock window (for profiled runs)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the timing of the other workloads (16 x 1024x4096 in bf16x3 and fp16, "
                          "64 x 2048x7168, 8 x 4096x16384 with 1024 selected rows)")
@@ -637,8 +639,10 @@ def main():
     # the same call back to back for a few seconds: socket power, package
     # power throttling and gfx clocks from the driver's metrics, and the
     # dense bf16 peak at that clock
-    log("power and clock window (3 s of the same call)")
-    power = power_window(step, torch)
+    power = None
+    if not args.no_power:
+        log("power and clock window (3 s of the same call)")
+        power = power_window(step, torch)
     if power and power.get("gfxclk_mhz_mean"):
         power["peak_tflops_at_clock"] = round(256 * 4096 * power["gfxclk_mhz_mean"] * 1e6 / 1e12, 1)
         power["pct_of_peak_at_clock"] = round(100 * w.batch * flops_gram(rows, w.m, T, len(restarts)) /
