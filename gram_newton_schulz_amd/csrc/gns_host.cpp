@@ -354,6 +354,14 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np;
   const int nt = static_cast<int>(N / c.pl->sym_tile);
+  // The 256-edge kernels add beta D from the operand stream when D is the B
+  // operand (D = B, a symmetric iterate: each wave takes its D entries from
+  // the B panel's stages as they pass through LDS).  A product whose D is its
+  // A operand (R Z with D = R, Q Z with D = Q) therefore runs as B A^T: A and
+  // B are polynomials in the same R, so both orders give the same product up
+  // to rounding, and the stored result (upper tiles, mirrored) is exactly
+  // symmetric either way.
+  if (D && D == A && D != B) std::swap(A, B);
   p.A = A; p.lda = N; p.sA = c.sq_stride();
   p.B = B; p.ldb = N; p.sB = c.sq_stride();
   p.K = static_cast<int>(N);

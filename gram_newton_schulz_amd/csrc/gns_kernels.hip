@@ -515,7 +515,8 @@ gemm_nt(GemmParams p) {
   const int tr_half = 8 * (lane & 1);
 
   // Accumulators start at (beta/alpha) * D so that the epilogue is a plain
-  // scale-and-store.  D is read through its transposed copy DT (D itself
+  // scale-and-store (except where D comes from the operand stream, see
+  // op_d below).  D is read through its transposed copy DT (D itself
   // for symmetric D), where the four rows held by a lane are contiguous.
   // The D loads are issued right after the main loop's first DMA stages, so
   // that those stages do not queue behind the D requests and the two
@@ -620,12 +621,14 @@ gemm_nt(GemmParams p) {
         }
       }
   };
-  auto init_from_d = [&]() {
+  // d1 = false: the D term itself comes from the operand stream (below) and
+  // only a second term is loaded here
+  auto init_from_d = [&](bool d1) {
 #pragma unroll
     for (int i = 0; i < NBI; ++i)
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) {
-        if (half && j >= 2) continue;
+        if (!d1 || (half && j >= 2)) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -687,6 +690,22 @@ gemm_nt(GemmParams p) {
   const int nk = KS == 2   ? 0
                  : KS == 0 ? p.K / BKE
                            : __builtin_amdgcn_readfirstlane(kp < kparts - 1 ? kbase : p.K / BKE - kbase * (kparts - 1));
+  // beta * D from the operand stream.  When D is the B operand of a
+  // symmetric product (D = B: the same exactly symmetric iterate), the lane's
+  // D entries D(e + q, j), e = wr + 32 ib + 8 g + 4 lh, j = wc + 32 jb + lr,
+  // equal B(tj TILE + j, ti TILE + e + q): 8 contiguous bytes of row j of the
+  // B panel in the stage holding K = ti TILE + wr + 32 ib.  That stage passes
+  // through LDS anyway, so the wave adds them to its accumulators there (two
+  // stages per wave, one per row block ib): D costs no memory traffic and no
+  // wait before the first stage.  The D loads of the prologue took 12.8 of a
+  // tile's 118 us on 8 x 4096x16384 bf16; n x n products with short K gain
+  // most (64 x 2048x7168: 20.10 -> 19.80 ms per call).  The stage index is
+  // made wave-uniform (readfirstlane): taken as divergent, the tests on it
+  // turned the K loop into an exec-masked loop with its indices on the VALU.
+  constexpr bool kOpD = (TILE == 256 && ESZ == 2 && PL == 1 && NW == 8 && BK == 0 && KS == 0 && MODE == MODE_SYM);
+  const bool op_d = kOpD && has_d && p.DT == p.B && p.lddt == p.ldb && p.sDT == p.sB && !p.d_rows &&
+                    nk >= (ti + 1) * (TILE / BKE);
+  const int ds0 = __builtin_amdgcn_readfirstlane((ti * TILE + wr) / BKE);   // this wave's first D stage
   if (nk > 0) {
     using Frag = typename Mma<E>::Frag;
     auto dma_stage = [&](int stage) {
@@ -767,6 +786,26 @@ gemm_nt(GemmParams p) {
         }
     };
 
+    // D entries of row block IB from the B plane of the stage in buffer buf
+    // (chunk g of a row holds K elements 8 g .. 8 g + 7, swizzled like the
+    // fragments)
+    auto add_d = [&](int buf, auto ibc, auto nj) {
+      constexpr int IB = decltype(ibc)::value;
+      constexpr int NJ = decltype(nj)::value;
+      const unsigned char *lb = lds + buf * STB + OPB;
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        const unsigned char *rowp = lb + (wc + jb * 32 + lr) * SB + 8 * lh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint2 v = *reinterpret_cast<const uint2 *>(rowp + ((g ^ fsw) << 4));
+          acc[IB][jb][4 * g + 0] += p.init_scale * E::ld(static_cast<S>(v.x & 0xffffu));
+          acc[IB][jb][4 * g + 1] += p.init_scale * E::ld(static_cast<S>(v.x >> 16));
+          acc[IB][jb][4 * g + 2] += p.init_scale * E::ld(static_cast<S>(v.y & 0xffffu));
+          acc[IB][jb][4 * g + 3] += p.init_scale * E::ld(static_cast<S>(v.y >> 16));
+        }
+      }
+    };
     if constexpr (NW == 8) {
       // Ping-pong over the two waves of every SIMD.  Every wave runs the same
       // stream per stage i -- L(i): read its fragments of stage i, then issue
@@ -785,7 +824,8 @@ gemm_nt(GemmParams p) {
       static_assert(kWait < 64, "wait count out of range");
 #pragma unroll
       for (int j = 0; j < NST - 1; ++j) dma_stage(j);
-      if (has_d) { load_d(); init_from_d(); }
+      if (has_d && !op_d) { load_d(); init_from_d(true); }
+      else if (op_d && p.DT2) init_from_d(false);
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
       __syncthreads();
       if (g1) __syncthreads();
@@ -794,9 +834,10 @@ gemm_nt(GemmParams p) {
       // waves of a diagonal tile run the one that skips column blocks 2, 3
       auto loop = [&](auto nj) {
         int buf = 0;                        // buffer of stage i
-        for (int i = 0; i < nk; ++i) {
+        auto stage_body = [&](int i, auto dk) {
           static_for<0, SUB>([&](auto sc) { fload(decltype(sc)::value, buf, decltype(sc)::value, nj); });
           dma_stage(i + NST - 1);           // into the buffer of stage i-1
+          if constexpr (decltype(dk)::value >= 0) add_d(buf, dk, nj);
           asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
           __syncthreads();
           __builtin_amdgcn_s_setprio(1);
@@ -804,7 +845,17 @@ gemm_nt(GemmParams p) {
           __builtin_amdgcn_s_setprio(0);
           __syncthreads();
           buf = buf == NST - 1 ? 0 : buf + 1;
+        };
+        // the two stages that carry this wave's D rows run outside the main
+        // loop, so that the loop itself keeps the code of a product without D
+        const int lo = op_d ? ds0 : nk;
+        int i = 0;
+        for (; i < lo; ++i) stage_body(i, std::integral_constant<int, -1>{});
+        if (op_d) {
+          stage_body(i++, std::integral_constant<int, 0>{});
+          stage_body(i++, std::integral_constant<int, 1>{});
         }
+        for (; i < nk; ++i) stage_body(i, std::integral_constant<int, -1>{});
       };
       if constexpr (kHalfDiag) {
         if (half) loop(std::integral_constant<int, 2>{});
@@ -824,7 +875,7 @@ gemm_nt(GemmParams p) {
       // prologue: all NST stages in flight; wait for stages 0 and 1
 #pragma unroll
       for (int j = 0; j < NST; ++j) dma_stage(j);
-      if (has_d) { load_d(); init_from_d(); }
+      if (has_d) { load_d(); init_from_d(true); }
       static_assert(LPS * (NST - 2) < 64, "wait count out of range");
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 2)) : "memory");
       __syncthreads();
@@ -867,7 +918,7 @@ gemm_nt(GemmParams p) {
     tl.loop_done();
   } else if (has_d) {
     load_d();
-    init_from_d();
+    init_from_d(true);
   }
   // First pass of a K split: this part's raw accumulators go to part_out
   // (the second pass sums the parts and runs the epilogue).
