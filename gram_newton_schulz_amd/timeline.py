@@ -47,11 +47,9 @@ def _fields(r: np.ndarray) -> dict:
     }
 
 
-def record(workload: int = 3, split: bool = False, calls: int = 1) -> np.ndarray:
-    """Run `calls` calls of the workload through the timeline library (after
-    three untimed ones) and return their records, one row per workgroup."""
-    import torch
-    from . import synth
+def timeline_lib():
+    """The timeline build, loaded through the binding (which then serves every
+    call of this process); raises if the library build is already loaded."""
     if binding._lib is not None and binding.LIB_PATH != build.TIMELINE_LIB:
         raise RuntimeError("the library build is already loaded in this process")
     if not os.path.exists(build.TIMELINE_LIB):
@@ -60,6 +58,34 @@ def record(workload: int = 3, split: bool = False, calls: int = 1) -> np.ndarray
     L = binding.lib()
     L.gns_timeline_read.restype = ctypes.c_int
     L.gns_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_uint, ctypes.POINTER(ctypes.c_uint), ctypes.c_int]
+    return L
+
+
+def reset_records(L) -> int:
+    """Start a new recording; returns the number of records dropped."""
+    n = ctypes.c_uint(0)
+    if L.gns_timeline_read(None, 0, ctypes.byref(n), 1) != 0:
+        raise RuntimeError("gns_timeline_read failed")
+    return n.value
+
+
+def read_records(L, reset: bool = True, cap: int = 1 << 18) -> np.ndarray:
+    """The records since the last reset (one row per workgroup)."""
+    n = ctypes.c_uint(0)
+    buf = np.zeros((cap, 8), dtype=np.uint64)
+    if L.gns_timeline_read(buf.ctypes.data, cap, ctypes.byref(n), int(reset)) != 0:
+        raise RuntimeError("gns_timeline_read failed")
+    if n.value > cap:
+        raise RuntimeError(f"{n.value} workgroups recorded, room for {cap}")
+    return buf[: n.value].copy()
+
+
+def record(workload: int = 3, split: bool = False, calls: int = 1) -> np.ndarray:
+    """Run `calls` calls of the workload through the timeline library (after
+    three untimed ones) and return their records, one row per workgroup."""
+    import torch
+    from . import synth
+    L = timeline_lib()
     w = synth.WORKLOADS[workload]
     X = synth.workload_batch(workload).cuda()
     rows = synth.workload_rows(workload)
@@ -73,21 +99,14 @@ def record(workload: int = 3, split: bool = False, calls: int = 1) -> np.ndarray
         binding.gram_ns_batched(X, synth.NS5_MUON, (2,), row_idx=rows, out=out, workspace=ws, stream=s,
                                 split_batch=split)
 
-    n = ctypes.c_uint(0)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
-    if L.gns_timeline_read(None, 0, ctypes.byref(n), 1) != 0:
-        raise RuntimeError("gns_timeline_read failed")
+    reset_records(L)
     for _ in range(calls):
         call()
     torch.cuda.synchronize()
-    buf = np.zeros((1 << 18, 8), dtype=np.uint64)
-    if L.gns_timeline_read(buf.ctypes.data, buf.shape[0], ctypes.byref(n), 1) != 0:
-        raise RuntimeError("gns_timeline_read failed")
-    if n.value > buf.shape[0]:
-        raise RuntimeError(f"{n.value} workgroups recorded, room for {buf.shape[0]}")
-    return buf[: n.value].copy()
+    return read_records(L)
 
 
 def launches(f: dict) -> list:
