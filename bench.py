@@ -435,6 +435,43 @@ def power_window(fn, torch, seconds=3.0):
     return smi.summary()
 
 
+def vendor_gemm(torch, w, steps=20):
+    """The vendor library's batched GEMM (torch.bmm, hipBLASLt on ROCm) on the
+    products of Gram NS at the workload's shape, for comparison: Q X
+    (n x n by n x m), the full X X^T (n x m by m x n, the transpose copied to
+    a contiguous operand) and a full n x n product.  bf16 in and out,
+    contiguous operands; median ms of `steps` calls, TFLOP/s, and the GPU's
+    power and clock over 3 s of back-to-back calls."""
+    B, n, m = w.batch, w.n, w.m
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = []
+    for name, (mm, kk, nn) in (("QX", (n, n, m)), ("XXt_full", (n, m, n)), ("nxn_full", (n, n, n))):
+        A = (torch.randn(B, mm, kk, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        Bm = (torch.randn(B, kk, nn, device="cuda", generator=g) * 0.02).to(torch.bfloat16).contiguous()
+        C = torch.empty(B, mm, nn, device="cuda", dtype=torch.bfloat16)
+
+        def fn():
+            torch.bmm(A, Bm, out=C)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(steps):
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        out.append({"product": name, "shape": [B, mm, kk, nn], "median_ms": round(ms, 4),
+                    "tflops": round(2.0 * B * mm * kk * nn / (ms * 1e-3) / 1e12, 1),
+                    "power": power_window(fn, torch, 3.0)})
+        del A, Bm, C
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_dion3_step(gns, synth, torch, w, coeffs, restarts, stream, steps=10):
     """One whole Dion3 update (Algorithm 4: momentum sum, l1 selection of
     k = n/4 rows, Gram NS of those rows, NorMuon, decay, row update, error
@@ -516,6 +553,9 @@ def main():
                     help="print MFMA utilisation and clock per kernel from a rocprofv3 --pmc run and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print every counter per kernel kind from a rocprofv3 --pmc --kernel-trace run and exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor library's bf16 GEMM (torch.bmm) on the workload's products "
+                         "(Q X, full X X^T, full n x n) with power and clock, print VENDOR lines and exit")
     ap.add_argument("--no-power", action="store_true",
                     help="skip the 3 s power and clock window (for profiled runs)")
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -559,6 +599,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.workload]
+    if args.vendor_gemm:
+        for rec in vendor_gemm(torch, w):
+            print("VENDOR " + json.dumps({"workload": args.workload, **rec}), flush=True)
+        return
     coeffs = synth.NS5_MUON
     T, restarts = 5, (2,)
     cdt = {"bf16": torch.bfloat16, "f16": torch.float16, "bf16x3": "bf16x3"}[args.compute]
