@@ -250,6 +250,22 @@ def test_plan_autotune_and_errors():
     assert sub.tile == 256 and sub.sym_tile == 128 and sub.gram_parts == 3
 
 
+def test_plan_size_limits():
+    """A 256-row panel must stay within the 32-bit offsets of the buffer
+    loads, and a padded matrix within 2^31 elements: 256 x 4194048 bf16 (a
+    panel of 2^31 - 2^17 bytes) is accepted, on 256-edge tiles with X read
+    row-major as one operand; a row one tile longer is refused, tall or wide."""
+    ok = _plan(batch=1, n=256, m=4194048, opts=0)
+    assert ok.direct_input == 1 and ok.tile == 128
+    ok256 = _plan(batch=1, n=256, m=4194048, opts=0x20)
+    assert ok256.tile == 256 and ok256.kmajor_products == 1 and ok256.gram_parts == 1
+    assert _plan(batch=1, n=4194048, m=256, opts=0x20).tile == 256          # tall: the same panels
+    for n, m in ((256, 4194304), (4194304, 256), (32768, 65792)):
+        with pytest.raises(gns.GnsError):
+            _plan(batch=1, n=n, m=m, opts=0x20)
+    assert _plan(batch=1, n=32768, m=65536, opts=0x10).tile == 128          # 2^31 elements
+
+
 def test_debug_checks_option():
     """GNS_OPT_DEBUG_CHECKS is a valid option of the three compute entry
     points; validation still comes first."""

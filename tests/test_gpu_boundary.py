@@ -24,6 +24,50 @@ def _bf16(B, n, m, seed, dist="normal"):
     return X, synth.as_f64(X)
 
 
+def test_longest_rows_at_the_addressing_limit():
+    """The longest rows the library accepts: a 256-row panel of 4194048 bf16
+    columns spans 2^31 - 2^17 bytes, just under the 32-bit offsets of the
+    buffer loads (a longer row is refused; see the host tests).  1 x 256 x
+    4194048 bf16 with the size rule (128-edge tiles, X transposed) and with
+    256-edge tiles (one workgroup contracting the whole rows for the Gram
+    matrix, Q X reading X row-major as one 2 GiB operand), against the fp64
+    oracle."""
+    gns = need_gpu()
+    n, m = 256, 4194048
+    say(f"longest rows 1 x {n} x {m}: inputs")
+    X = synth.batch(1, n, m, seed=43, dtype=torch.bfloat16)
+    Xd = X.cuda()
+    got = {}
+    for tile in (None, 256):
+        say(f"longest rows: tile {tile}")
+        got[tile] = gns.gram_ns_batched(Xd, NS5, restarts=(2,), tile=tile).cpu()
+        torch.cuda.synchronize()
+    del Xd
+    say("longest rows: oracle")
+    ref = oracle_gram(synth.as_f64(X)[0])
+    for tile, o in got.items():
+        assert rel_err(synth.as_f64(o)[0], ref) <= TOL_HALF, tile
+
+
+def test_batch_beyond_one_grid_dimension():
+    """70000 matrices, more than 65535 (the batch is a grid dimension of the
+    input pass): 70000 x 8 x 24 bf16 in one call; the members around 65535
+    and a seeded sample of the rest against the fp64 oracle."""
+    gns = need_gpu()
+    B, n, m = 70000, 8, 24
+    say(f"batch {B} x {n} x {m}")
+    g = torch.Generator().manual_seed(44)
+    X = (torch.randn(B, n, m, generator=g) * 0.1).to(torch.bfloat16)
+    out = gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,)).cpu()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(44)
+    picks = sorted({0, 1, 65534, 65535, 65536, B - 1, *rng.choice(B, 24, replace=False).tolist()})
+    X64 = synth.as_f64(X[picks])
+    got = synth.as_f64(out[picks])
+    for i, b in enumerate(picks):
+        assert rel_err(got[i], oracle_gram(X64[i])) <= TOL_HALF, b
+
+
 @pytest.mark.parametrize("tile,shape", [(256, (3, 512, 1536)), (None, (3, 512, 1536)),
                                         (None, (2, 2048, 4096))])
 @pytest.mark.parametrize("T", [5, 1])
