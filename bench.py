@@ -832,7 +832,7 @@ def main():
             del Xo, oo
             torch.cuda.empty_cache()
 
-    cpu = None
+    cpu = cpu_std = None
     if not args.no_cpu:
         import oracle
         try:
@@ -850,6 +850,12 @@ def main():
         dt = time.perf_counter() - t0
         cpu = {"value": round(1.0 / dt, 5), "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
                "sample": f"1 of the {w.batch} matrices ({rows}x{w.m}), fp64 numpy Gram NS, {dt:.1f} s"}
+        # the standard NS oracle on the same matrix, beside it
+        t0 = time.perf_counter()
+        oracle.standard_ns(x64, coeffs)
+        dts = time.perf_counter() - t0
+        cpu_std = {"value": round(1.0 / dts, 5), "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
+                   "sample": f"the same matrix, fp64 numpy standard NS, {dts:.1f} s"}
 
     desc = desc_of(args.workload)
     line = {
@@ -879,6 +885,7 @@ def main():
         # the headline call (driver GPU metrics; null where unavailable)
         "gpu_power_clock": power,
         "cpu_baseline": cpu,
+        "cpu_baseline_standard_ns": cpu_std,
         "standard_ns5": std,
         "dion3_select_l1": sel,
         "dion3_step": dion3,
