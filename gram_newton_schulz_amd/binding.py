@@ -59,7 +59,7 @@ class PlanInfo(ctypes.Structure):
                 ("gram_parts", ctypes.c_int), ("direct_input", ctypes.c_int),
                 ("kmajor_products", ctypes.c_int), ("input_copy", ctypes.c_int),
                 ("split_streams", ctypes.c_int), ("autotune_timed", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("gram_tile", ctypes.c_int)]
 
 
 class LaunchRecord(ctypes.Structure):

@@ -41,6 +41,7 @@ bool valid_compute(int dt) { return valid_dtype(dt) || dt == GNS_BF16X3; }
 struct Plan {
   int tile = 128;                      // tile edge of the rectangular products
   int sym_tile = 128;                  // and of the symmetric ones
+  int gram_tile = 128;                 // and of the Gram matrix (gram_tile_edge)
   int syrk_parts = 1;                  // K parts of the Gram matrix (256-edge tiles)
   int syrk_parts_room = 1;             // parts the workspace has room for
   int64_t batch = 0, rows = 0, m = 0;  // the caller's (selected) rows and columns
@@ -109,6 +110,18 @@ int choose_syrk_parts(int cdt, int64_t batch, int64_t Np256, int64_t Mp256) {
   return parts >= 2 ? static_cast<int>(parts) : 1;
 }
 
+// Under the size rule the Gram matrix keeps 256-edge tiles where the n x n
+// products take 128 but its own 128-edge grid would not fit one round of two
+// workgroups per compute unit: 16 x 1024x4096 has 576 upper 128-edge tiles
+// for 512 slots, and its 160 256-edge tiles run in one round instead (1.14 ->
+// 1.10-1.11 ms per call, 1.26 -> 1.20 on one stream; outputs identical, as
+// the tile edge changes no sum).  Forced tile requests keep their edges.
+int gram_tile_edge(int tile_request, int tile, int sym_tile, int64_t batch, int64_t r) {
+  if (tile_request != 0 || tile != 256 || sym_tile != 128) return sym_tile;
+  const int64_t t128 = round_up(r, 256) / 128;
+  return t128 * (t128 + 1) / 2 * batch > 2 * 256 ? 256 : 128;
+}
+
 // tile_request: see kTileMixed.  Workspace sizes are quoted
 // for 256-padded buffers so that any tile choice fits.
 bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, int tile_request,
@@ -128,6 +141,7 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
   }
   // the fp32 and split-plane kernels exist for 128-edge tiles only
   if (cdt == GNS_F32 || cdt == GNS_BF16X3) pl->tile = pl->sym_tile = 128;
+  pl->gram_tile = gram_tile_edge(tile_request, pl->tile, pl->sym_tile, batch, pl->r);
   pl->batch = batch;
   pl->rows = rows;
   pl->m = m;
@@ -168,6 +182,7 @@ bool make_plan(int cdt, int64_t batch, int64_t rows, int64_t m, int n_square, in
     const int64_t Np256 = round_up(pl->r, 256), Mp256 = round_up(pl->c, 256);
     pl->syrk_parts_room = pl->tall ? 1 : choose_syrk_parts(cdt, batch, Np256, Mp256);
     pl->syrk_parts = (tile_request == 0 && pl->tile == 256) ? pl->syrk_parts_room : 1;
+    if (pl->syrk_parts > 1) pl->gram_tile = 256;   // the K split runs 256-edge tiles
     pl->off_part = off;
     if (pl->syrk_parts_room > 1) {
       const int64_t t = Np256 / 256;
@@ -443,7 +458,7 @@ gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow
   if (c.pl->syrk_parts > 1) return syrk_split(c, R, from_input, xrow);
   GemmParams p = base_params(c);
   const int64_t N = c.pl->Np, M = c.pl->Mp;
-  const int nt = static_cast<int>(N / c.pl->sym_tile);
+  const int nt = static_cast<int>(N / c.pl->gram_tile);
   const bool direct = from_input && c.direct;
   const void *Xh = direct ? c.xsrc() : (xrow ? xrow : c.xh());
   if (direct) p.alpha_vec = c.inv2();
@@ -455,9 +470,9 @@ gns_status syrk(const Ctx &c, void *R, bool from_input = false, const void *xrow
   p.pA = p.pB = c.plane_rect();
   p.pC = c.plane_sq();
   const double n = static_cast<double>(c.pl->r), m = static_cast<double>(c.pl->c);
-  LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->sym_tile, gns::MODE_SYM), n * n * m * c.batch,
+  LaunchScope ls(c.s, "syrk", gns::gemm_kernel_name(c.cdt, c.pl->gram_tile, gns::MODE_SYM), n * n * m * c.batch,
                  c.batch * (n * m + n * n) * c.pl->esz);
-  hipError_t e = gns::launch_gemm(c.cdt, c.pl->sym_tile, gns::MODE_SYM, p, c.s);
+  hipError_t e = gns::launch_gemm(c.cdt, c.pl->gram_tile, gns::MODE_SYM, p, c.s);
   ls.done();
   return e == hipSuccess ? GNS_OK : GNS_E_HIP;
 }
@@ -1235,6 +1250,7 @@ gns_status gns_call_plan(int standard, const void *X, const void *out, int64_t b
   info->standard = cp.standard ? 1 : 0;
   info->tile = cp.pl.tile;
   info->sym_tile = cp.pl.sym_tile;
+  info->gram_tile = cp.pl.gram_tile;
   info->gram_parts = cp.pl.syrk_parts;
   info->direct_input = cp.direct ? 1 : 0;
   info->kmajor_products = cp.nn ? 1 : 0;

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GNS_ABI_VERSION 1
+#define GNS_ABI_VERSION 2   /* 2: gns_plan_info gained gram_tile */
 
 typedef enum {
   GNS_F32 = 0,   /* IEEE binary32                          */
@@ -256,6 +256,9 @@ typedef struct {
   int split_streams;    /* 1: the batch is split over the library's streams   */
   int autotune_timed;   /* 1: the call would time the tile choices            */
   size_t workspace_bytes; /* workspace this plan uses                         */
+  int gram_tile;        /* edge of the Gram matrix's tiles (the size rule
+                           keeps 256 where a 128-edge grid would overflow one
+                           round of the GPU; else sym_tile)                   */
 } gns_plan_info;
 
 gns_status gns_call_plan(int standard, const void *X, const void *out, int64_t batch, int64_t n,

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = gns.lib()
-    assert L.gns_abi_version() == 1
+    assert L.gns_abi_version() == 2
     for code in range(0, 13):
         assert L.gns_status_str(code)
         assert L.gns_status_str(code) != b"unknown status"
@@ -247,7 +247,22 @@ def test_plan_autotune_and_errors():
                            ctypes.byref(info)) == E["FLAGS"]
     # the K split of small Gram matrices and the mixed tiles of the size rule
     sub = _plan(batch=8, n=4096, m=16384, row_idx=0x300000000, k=1024, restarts=(2,), opts=0)
-    assert sub.tile == 256 and sub.sym_tile == 128 and sub.gram_parts == 3
+    assert sub.tile == 256 and sub.sym_tile == 128 and sub.gram_parts == 3 and sub.gram_tile == 256
+
+
+def test_plan_gram_tile_edge():
+    """Under the size rule the Gram matrix keeps 256-edge tiles where the n x n
+    products take 128 but its 128-edge grid would overflow one round of two
+    workgroups per compute unit (more than 512 upper tiles over the batch)."""
+    w2 = _plan(batch=16, n=1024, m=4096, opts=0)               # 16 x 36 = 576 128-edge tiles
+    assert (w2.tile, w2.sym_tile, w2.gram_tile, w2.gram_parts) == (256, 128, 256, 1)
+    fits = _plan(batch=14, n=1024, m=4096, opts=0)             # 14 x 36 = 504: one round
+    assert (fits.tile, fits.sym_tile, fits.gram_tile) == (256, 128, 128)
+    assert _plan(batch=16, n=1024, m=4096, opts=0x80).gram_tile == 128   # forced mixed tiles
+    assert _plan(batch=16, n=1024, m=4096, opts=0x10).gram_tile == 128   # forced 128
+    big = _plan(batch=8, n=4096, m=16384, opts=0)
+    assert (big.sym_tile, big.gram_tile) == (256, 256)
+    assert _plan(batch=16, n=1024, m=4096, io=0, cdt=0, opts=0).gram_tile == 128   # fp32: 128 only
 
 
 def test_plan_size_limits():
