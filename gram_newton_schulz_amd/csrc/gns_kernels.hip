@@ -715,9 +715,22 @@ gemm_nt(GemmParams p) {
   const int ds0 = __builtin_amdgcn_readfirstlane((ti * TILE + wr) / BKE);   // this wave's first D stage
   if (nk > 0) {
     using Frag = typename Mma<E>::Frag;
+    // The loop issues NST - 1 stages past the last one, so that every stage
+    // waits on the same count of loads.  Those go through descriptors with an
+    // empty range: out-of-range loads complete without fetching anything, and
+    // the ring slots they fill are never read.
+    i32x4 rAz[PL], rBz[PL];
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+      rAz[pl] = rA[pl];
+      rAz[pl][2] = 0;
+      rBz[pl] = rB[pl];
+      rBz[pl][2] = 0;
+    }
     auto dma_stage = [&](int stage) {
       const uint32_t buf_lds = lds_base + static_cast<uint32_t>((stage % NST) * STB);
-      const int st = stage < nk ? stage : nk - 1;   // past the end: harmless reload
+      const bool live = stage < nk;
+      const int st = live ? stage : nk - 1;
 #pragma unroll
       for (int q = 0; q < BPW; ++q) {
         const int blk = wave_u + q * NW;
@@ -728,11 +741,13 @@ gemm_nt(GemmParams p) {
           asm volatile(
               "s_mov_b32 m0, %0\n\t"
               "buffer_load_dwordx4 %1, %2, %3 offen lds"
-              :: "s"(buf_lds + pl * OPB + blk * 1024), "v"(vA), "s"(rA[pl]), "s"(soA) : "memory", "m0");
+              :: "s"(buf_lds + pl * OPB + blk * 1024), "v"(vA), "s"(live ? rA[pl] : rAz[pl]), "s"(soA)
+              : "memory", "m0");
           asm volatile(
               "s_mov_b32 m0, %0\n\t"
               "buffer_load_dwordx4 %1, %2, %3 offen lds"
-              :: "s"(buf_lds + (PL + pl) * OPB + blk * 1024), "v"(vB), "s"(rB[pl]), "s"(soB) : "memory", "m0");
+              :: "s"(buf_lds + (PL + pl) * OPB + blk * 1024), "v"(vB), "s"(live ? rB[pl] : rBz[pl]), "s"(soB)
+              : "memory", "m0");
         }
       }
     };
