@@ -709,7 +709,9 @@ gemm_nt(GemmParams p) {
   // most (64 x 2048x7168: 20.10 -> 19.80 ms per call).  The stage index is
   // made wave-uniform (readfirstlane): taken as divergent, the tests on it
   // turned the K loop into an exec-masked loop with its indices on the VALU.
-  constexpr bool kOpD = (TILE == 256 && ESZ == 2 && PL == 1 && NW == 8 && BK == 0 && KS == 0 && MODE == MODE_SYM);
+  // (both the 8-wave 256-edge and the 4-wave 128-edge symmetric kernels)
+  constexpr bool kOpD = (ESZ == 2 && PL == 1 && BK == 0 && KS == 0 && MODE == MODE_SYM &&
+                         ((TILE == 256 && NW == 8) || (TILE == 128 && NW == 4)));
   const bool op_d = kOpD && has_d && p.DT == p.B && p.lddt == p.ldb && p.sDT == p.sB && !p.d_rows &&
                     nk >= (ti + 1) * (TILE / BKE);
   const int ds0 = __builtin_amdgcn_readfirstlane((ti * TILE + wr) / BKE);   // this wave's first D stage
@@ -897,7 +899,8 @@ gemm_nt(GemmParams p) {
       // prologue: all NST stages in flight; wait for stages 0 and 1
 #pragma unroll
       for (int j = 0; j < NST; ++j) dma_stage(j);
-      if (has_d) { load_d(); init_from_d(true); }
+      if (has_d && !op_d) { load_d(); init_from_d(true); }
+      else if (op_d && p.DT2) init_from_d(false);
       static_assert(LPS * (NST - 2) < 64, "wait count out of range");
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 2)) : "memory");
       __syncthreads();
@@ -905,7 +908,7 @@ gemm_nt(GemmParams p) {
       fload(0, 0, 0, std::integral_constant<int, NBJ>{});
 
       int buf = 0;                            // buffer of stage i
-      for (int i = 0; i < nk; ++i) {
+      auto stage_body = [&](int i, auto dk) {
         const int bnext = buf == NST - 1 ? 0 : buf + 1;
         static_for<0, SUB>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
@@ -928,13 +931,27 @@ gemm_nt(GemmParams p) {
             for (int b = 0; b < NBJ; ++b) fb[0][pl][b] = fb[1][pl][b];
           }
         }
+        // this wave's D rows of row block dk from stage i (still in its buffer)
+        if constexpr (decltype(dk)::value >= 0) add_d(buf, dk, std::integral_constant<int, NBJ>{});
         // stage i+2 must be complete before the barrier; stages i+3 .. i+NST-1
         // may still be in flight
         asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS * (NST - 3)) : "memory");
         __syncthreads();
         dma_stage(i + NST);
         buf = bnext;
+      };
+      // as in the 8-wave loop, the two stages that carry this wave's D rows
+      // run outside the main loop
+      const int lo = op_d ? ds0 : nk;
+      int i = 0;
+      for (; i < lo; ++i) stage_body(i, std::integral_constant<int, -1>{});
+      if constexpr (kOpD) {
+        if (op_d) {
+          stage_body(i++, std::integral_constant<int, 0>{});
+          stage_body(i++, std::integral_constant<int, 1>{});
+        }
       }
+      for (; i < nk; ++i) stage_body(i, std::integral_constant<int, -1>{});
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     tl.loop_done();
