@@ -1224,6 +1224,18 @@ gemm_nt(GemmParams p) {
       constexpr bool kToBf16 = std::is_same<E, EF16>::value;
       if ((p.out_dtype == E::code || (kToBf16 && p.out_dtype == DT_BF16)) && (p.out_cols & 7) == 0 &&
           (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
+        constexpr int CPR = TILE / 8;                      // 16-byte pieces per row
+        constexpr int NPC = TILE * CPR / NT;               // pieces per thread
+        static_assert(TILE * CPR % NT == 0, "whole pieces per thread");
+        // the destination rows of this thread's pieces, loaded before the
+        // tile is rounded and staged so that their latency overlaps that work
+        // (-1: not a row of the output)
+        int64_t dest[NPC];
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+          const int64_t i = tr0 + (tid + j * NT) / CPR;
+          dest[j] = i < p.rows_eff ? (ridx ? ridx[i] : i) : -1;
+        }
         if constexpr (kToBf16) {
           if (p.out_dtype == DT_BF16) pack(false, Tag<EBF16>{});
           else pack(false, Tag<E>{});
@@ -1232,15 +1244,13 @@ gemm_nt(GemmParams p) {
         }
         stage_direct();
         S *O = static_cast<S *>(p.out) + obase;
-        constexpr int CPR = TILE / 8;                      // 16-byte pieces per row
-#pragma unroll 4
-        for (int k = tid; k < TILE * CPR; k += NT) {
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+          const int k = tid + j * NT;
           const int rr = k / CPR;
           const int cc = (k % CPR) * 8;
-          const int64_t i = tr0 + rr;
-          if (i >= p.rows_eff || tc0 + cc >= p.out_cols) continue;
-          const int64_t row = ridx ? ridx[i] : i;
-          if (row < 0 || row >= p.out_rows) continue;
+          const int64_t row = dest[j];
+          if (row < 0 || row >= p.out_rows || tc0 + cc >= p.out_cols) continue;
           const u32x4 v = *reinterpret_cast<const u32x4 *>(Ts + rr * TP + cc);
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(O + row * p.out_cols + tc0 + cc));
         }
