@@ -312,13 +312,16 @@ void set_scale(GemmParams *p, float alpha, float beta) {
   }
 }
 
-// Runs of tiles dealt to one XCD (the kernel's xcd_chunk): one matrix per
-// run with xpm = 1, else 1/xpm of a matrix so that xpm XCDs share each
-// matrix.  Falls back to one contiguous run per XCD when the sizes do not
-// divide.  Every product uses xpm = 4 (a quarter matrix per run): measured
-// on 8 x 4096x16384 bf16 against 1, 2 and 8 per product kind, it keeps the
+// Runs of tiles dealt to one XCD (the kernel's xcd_chunk): 1/xpm of a matrix
+// per run so that xpm XCDs share each matrix, or with xpm = 1 (and whenever
+// the sizes do not divide) one contiguous run per XCD, which holds whole
+// matrices when the batch is a multiple of 8.  Products use xpm = 4 (a quarter matrix per run): measured on
+// 8 x 4096x16384 bf16 against 1, 2 and 8 per product kind, it keeps the
 // matrices in flight within the shared last-level cache while each XCD's L2
-// still sees a compact block of tiles.
+// still sees a compact block of tiles.  The n x n products of matrices of at
+// most 2 MiB (half an XCD's L2) use xpm = 1 instead, so that one XCD's L2
+// holds every operand of its matrix (16 x 1024x4096 bf16: 1.08 -> 1.06 ms
+// a call; 64 x 2048x7168 unchanged).
 int xcd_chunk(int64_t tiles_per_mat, int64_t batch, int xpm) {
   const int64_t S = ((tiles_per_mat * batch) & ~int64_t(7)) / 8;
   if (S == 0) return 1;
@@ -380,7 +383,8 @@ gns_status symm(const Ctx &c, const void *A, const void *B, float alpha, float b
   p.A = A; p.lda = N; p.sA = c.sq_stride();
   p.B = B; p.ldb = N; p.sB = c.sq_stride();
   p.K = static_cast<int>(N);
-  sym_layout(&p, c, nt, 4, kSymmBlock, kSymmBand);
+  const int xpm = N * N * c.pl->esz * c.pl->planes <= (int64_t(2) << 20) ? 1 : 4;
+  sym_layout(&p, c, nt, xpm, kSymmBlock, kSymmBand);
   set_scale(&p, alpha, beta);
   if (D) { p.DT = D; p.lddt = N; p.sDT = c.sq_stride(); }   // D is symmetric
   if (D && D2) {
