@@ -784,8 +784,10 @@ def main():
 
     # the other workloads, each timed as one call per step like the headline
     # (median and interquartile range over the steps); the row subset also
-    # reports the HBM rate of its gather (the norm pass and the scaled copy of
-    # the selected rows, from the library's per-launch events)
+    # reports the HBM rate of its gather (the input pass over the selected
+    # rows: their gathered copy with per-tile sums of squares on the direct
+    # path, else the norm pass and the scaled copy; from the library's
+    # per-launch events)
     others = None
     if not args.one_stream and not args.no_other_workloads and args.workload == 3:
         del Xd, out, ws
@@ -819,10 +821,11 @@ def main():
                      "pct_peak": round(100 * fl / (mo / 1e3) / 1e12 / PEAK_TFLOPS[comp], 2)}
                 if cfg == 5:
                     _, _, rec5 = timed(lambda: call(False), 3, 1, per_launch=True)
-                    g = [(by, kms) for name, kern, fl_, by, kms in rec5
-                         if name in ("norm_partial", "scale_transpose")]
-                    gb, gms = sum(b for b, _ in g), sum(t for _, t in g)
-                    e["gather"] = {"kernels": "norm_partial + scale_transpose (selected rows)",
+                    gather_kernels = ("transpose_sumsq", "norm_partial", "scale_transpose")
+                    g = [(name, by, kms) for name, kern, fl_, by, kms in rec5 if name in gather_kernels]
+                    gb, gms = sum(b for _, b, _ in g), sum(t for _, _, t in g)
+                    ran = [k for k in gather_kernels if any(name == k for name, _, _ in g)]
+                    e["gather"] = {"kernels": " + ".join(ran) + " (selected rows)",
                                    "ms_per_step": round(gms / 3, 4),
                                    "gbs": round(gb / (gms / 1e3) / 1e9, 1) if gms > 0 else None,
                                    "frac_hbm": round(gb / (gms / 1e3) / 1e9 / HBM_PEAK_GBS, 3) if gms > 0 else None}

@@ -254,15 +254,16 @@ struct Ctx {
   int64_t b0;
   unsigned char *ws;
   hipStream_t s;
-  // Direct input path: X (already in the compute type, whole tiles, no row
-  // subset) is read in place instead of through a normalised copy; products
-  // that read it apply 1/(||X||_F + eps) per matrix in their epilogues.
+  // Direct input path: X (already in the compute type, whole tiles) is read
+  // as it is instead of through a normalised copy; products that read it
+  // apply 1/(||X||_F + eps) per matrix in their epilogues.
   bool direct = false;
   const void *xin = nullptr;           // this sub-batch's X
-  // In-place calls (out is X) on the direct path whose final product would
-  // read X: the input pass also copies X row-major into the workspace
-  // (xcopy), and every later product reads that copy, so that no product
-  // reads X while the final one writes it.  Null otherwise.
+  // The input pass also copies X row-major into the workspace (xcopy), and
+  // every later product reads that copy, for a row subset (the copy holds the
+  // selected rows, unscaled) and for in-place calls whose final product would
+  // read X (so that no product reads X while the final one writes it).  Null
+  // otherwise.
   void *xcopy = nullptr;
   const void *xsrc() const { return xcopy ? xcopy : xin; }
   // The rectangular products of Gram NS read X row-major (K-major B operand,
@@ -585,7 +586,8 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
                      c.batch * rows * m * (c.nn ? 1.0 : 2.0) * gns::dtype_size(io) +
                          (c.xcopy ? c.batch * rows * m * gns::dtype_size(io) : 0.0));
       hipError_t e = gns::launch_transpose_sumsq(io, X, c.batch, c.pl->rows, c.pl->m,
-                                                 c.nn ? nullptr : c.xt(0), c.xcopy, c.tile_partials(), c.s);
+                                                 c.nn ? nullptr : c.xt(0), c.xcopy, c.tile_partials(), row_idx,
+                                                 n_total, c.s);
       ls.done();
       if (e != hipSuccess) return GNS_E_HIP;
     }
@@ -849,10 +851,10 @@ bool kmajor_products(const Plan &pl, int cdt) {
 }
 
 // The direct input path applies when X can stand in for its normalised copy:
-// X is already in the (16-bit, unsplit) compute type, every matrix is used
-// whole and fills whole tiles, and X is 16-byte aligned.
-bool direct_input(const Plan &pl, const void *X, int io, int cdt, const int64_t *row_idx) {
-  return io == cdt && (cdt == GNS_BF16 || cdt == GNS_F16) && pl.planes == 1 && !row_idx &&
+// X is already in the (16-bit, unsplit) compute type, the matrices (or their
+// row subsets) fill whole tiles, and X is 16-byte aligned.
+bool direct_input(const Plan &pl, const void *X, int io, int cdt) {
+  return io == cdt && (cdt == GNS_BF16 || cdt == GNS_F16) && pl.planes == 1 &&
          !pl.tall && pl.rows % pl.tile == 0 && pl.m % pl.tile == 0 &&
          (reinterpret_cast<uintptr_t>(X) & 15) == 0;
 }
@@ -1103,16 +1105,19 @@ gns_status plan_call(bool standard_entry, const void *X, const void *out, int64_
   // fewer launches and never forms X X^T of an ill-conditioned square
   // matrix, so Dion3 falls back to it (§4.1, last paragraph).
   cp->standard = standard_entry || (rows == m && !(opts & GNS_OPT_NO_SQUARE_FALLBACK));
-  cp->direct = direct_input(cp->pl, X, io, cdt, row_idx);
   cp->nn = !cp->standard && kmajor_products(cp->pl, cdt);
+  // A row subset takes the direct path in the K-major form only: its input
+  // pass gathers the rows, unscaled, into a workspace region that form never
+  // uses (elsewhere that region holds the second transposed copy).
+  cp->direct = direct_input(cp->pl, X, io, cdt) && (!row_idx || cp->nn);
   // In place on the direct path, the final Q X reads X (K-major form) when
   // no restart has replaced it by a workspace buffer: the input pass then
   // copies X, and the products read the copy.  (The transposed form and
   // standard NS read X only in their first product, before any output is
-  // written; a row subset or a normalised copy never reads X after the
-  // input pass.)
+  // written; a normalised copy is never X.)  A row subset always reads its
+  // gathered copy.
   const bool restarted = std::find(cp->restart_at.begin(), cp->restart_at.end(), 1) != cp->restart_at.end();
-  cp->copy_input = cp->inplace && cp->direct && cp->nn && !restarted;
+  cp->copy_input = cp->direct && cp->nn && ((cp->inplace && !restarted) || row_idx != nullptr);
   return GNS_OK;
 }
 

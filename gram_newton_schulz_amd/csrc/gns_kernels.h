@@ -103,9 +103,13 @@ hipError_t launch_select_rows_l1(int io_dtype, const void *M, int64_t batch, int
 // Unscaled transpose of 16-bit X (n, m multiples of 128, 16-byte aligned) into
 // XT [m][n] per matrix (skipped when XT is null), and the sum of squares of
 // every 128x128 tile into partials[b][tile] (fp64).
-// With Xcopy set, X is also copied row-major into Xcopy (same layout).
+// With Xcopy set, X is also copied row-major into Xcopy ([b][n][m]).
+// With row_idx ([batch][n]), the n x m matrix of batch entry b is rows
+// row_idx[b][0..n) of the n_src x m matrix X_b (an index outside [0, n_src)
+// reads as a zero row).
 hipError_t launch_transpose_sumsq(int dtype, const void *X, int64_t batch, int64_t n, int64_t m,
-                                  void *XT, void *Xcopy, double *partials, hipStream_t s);
+                                  void *XT, void *Xcopy, double *partials, const int64_t *row_idx,
+                                  int64_t n_src, hipStream_t s);
 // inv[b] = 1 / (sqrt(sum_i partials[b][i]) + eps) and inv2[b] = inv[b]^2 (fixed-order sums).
 hipError_t launch_norm_finish(const double *partials, int64_t batch, int64_t parts, double eps,
                               float *inv, float *inv2, hipStream_t s);

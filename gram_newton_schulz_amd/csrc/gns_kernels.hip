@@ -1629,11 +1629,14 @@ check_finite(const void *A, int64_t rows, int64_t cols, const int64_t *row_idx, 
 // One 128x128 tile per workgroup: X^T tile through a padded LDS tile (16-byte
 // loads and stores, all eight loads of a thread in flight together), and the
 // tile's sum of squares (fp32 per thread over 64 elements, then a fixed-order
-// fp64 combination).
+// fp64 combination).  The n x m matrix is either X_b itself (n_src = n) or,
+// with row_idx, rows row_idx[b][0..n) of the n_src x m matrix X_b (a row
+// outside X_b reads as zeros).
 template <class T>
 __global__ void __launch_bounds__(256)
 transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restrict__ XT,
-                void *__restrict__ Xcopy, double *partials) {
+                void *__restrict__ Xcopy, double *partials, const int64_t *__restrict__ row_idx,
+                int64_t n_src) {
   constexpr int TT = 128;                 // tile edge
   constexpr int PR = TT / 8;              // 16-byte pieces per tile row
   constexpr int NP = TT * PR / 256;       // pieces per thread
@@ -1642,16 +1645,21 @@ transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restri
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * TT;
   __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
   __shared__ double wsum[4];
-  const uint16_t *Xb = static_cast<const uint16_t *>(X) + static_cast<int64_t>(b) * n * m;
+  const uint16_t *Xb = static_cast<const uint16_t *>(X) + static_cast<int64_t>(b) * n_src * m;
+  const int64_t *rib = row_idx ? row_idx + static_cast<int64_t>(b) * n : nullptr;
   uint16_t *XTb = static_cast<uint16_t *>(XT) + static_cast<int64_t>(b) * m * n;
   u32x4 in[NP];
 #pragma unroll
   for (int h = 0; h < NP; ++h) {
     const int v = threadIdx.x + 256 * h;
-    in[h] = *reinterpret_cast<const u32x4 *>(Xb + (r0 + v / PR) * m + c0 + (v % PR) * 8);
+    const int64_t r = r0 + v / PR;
+    const int64_t src = rib ? rib[r] : r;
+    // a row index outside X_b reads as zeros (no access)
+    in[h] = (src >= 0 && src < n_src) ? *reinterpret_cast<const u32x4 *>(Xb + src * m + c0 + (v % PR) * 8)
+                                      : u32x4{0u, 0u, 0u, 0u};
   }
-  // optional row-major copy of X, same layout (read by later products in
-  // place of the caller's X when the caller's X is also the output)
+  // optional row-major copy of the n x m matrix (read by later products in
+  // place of the caller's X: a row subset, or X when it is also the output)
   if (Xcopy) {
     uint16_t *Xc = static_cast<uint16_t *>(Xcopy) + static_cast<int64_t>(b) * n * m;
 #pragma unroll
@@ -2201,10 +2209,12 @@ hipError_t launch_scale_transpose(int io, int cdt, const void *X, int64_t batch,
 }
 
 hipError_t launch_transpose_sumsq(int dt, const void *X, int64_t batch, int64_t n, int64_t m,
-                                  void *XT, void *Xcopy, double *partials, hipStream_t s) {
+                                  void *XT, void *Xcopy, double *partials, const int64_t *row_idx,
+                                  int64_t n_src, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(m / 128), static_cast<unsigned>(n / 128), static_cast<unsigned>(batch));
-  if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials);
-  else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials);
+  if (!row_idx) n_src = n;
+  if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, row_idx, n_src);
+  else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, row_idx, n_src);
   return hipGetLastError();
 }
 

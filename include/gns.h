@@ -251,8 +251,11 @@ typedef struct {
   int direct_input;     /* 1: the products read X itself, scaled in their
                            epilogues, instead of a normalised copy            */
   int kmajor_products;  /* 1: Q X reads X row-major (no transposed copy)      */
-  int input_copy;       /* 1: in place on the direct path: the input pass
-                           copies X into the workspace first                  */
+  int input_copy;       /* 1: on the direct path, the input pass copies X
+                           (a row subset: its selected rows) into the
+                           workspace and the products read the copy: for a
+                           row subset, and in place when the final product
+                           would read X                                       */
   int split_streams;    /* 1: the batch is split over the library's streams   */
   int autotune_timed;   /* 1: the call would time the tile choices            */
   size_t workspace_bytes; /* workspace this plan uses                         */

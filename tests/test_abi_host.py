@@ -211,10 +211,9 @@ def test_plan_in_place_copies_input_only_where_needed():
     assert small.tile == 128 and small.direct_input == 1 and small.input_copy == 0
     # a restart replaces X by a workspace buffer before the final product
     assert _plan(out=X, restarts=(2,)).input_copy == 0
-    # no direct path: ragged tiles, another I/O type, or a row subset
+    # no direct path: ragged tiles or another I/O type
     assert _plan(out=X, n=500).input_copy == 0 and _plan(out=X, n=500).direct_input == 0
     assert _plan(out=X, io=0).input_copy == 0
-    assert _plan(out=X, row_idx=0x300000000, k=256).input_copy == 0
     # transposed form (128-edge tiles) and standard NS read X only first
     assert _plan(out=X, opts=0x10).input_copy == 0 and _plan(out=X, opts=0x10).direct_input == 1
     assert _plan(standard=1, out=X).input_copy == 0
@@ -224,6 +223,27 @@ def test_plan_in_place_copies_input_only_where_needed():
     L = gns.lib()
     assert ip.workspace_bytes <= L.gns_gram_workspace_bytes(1, 3, 512, 1536)
     assert oop.workspace_bytes == ip.workspace_bytes
+
+
+def test_plan_row_subset_reads_a_gathered_copy():
+    """A row subset that fills whole tiles in the compute type takes the
+    direct path in the K-major form: the input pass gathers the selected rows,
+    unscaled, into the workspace, and the products read that copy (scaled in
+    their epilogues) in place of a normalised copy.  Elsewhere a row subset
+    keeps the normalised copy (Dion3 Algorithm 4: only the selected rows are
+    orthogonalised)."""
+    R = 0x300000000
+    sub = _plan(row_idx=R, k=256)                   # 256 of 512 rows, 256-edge tiles
+    assert sub.direct_input == 1 and sub.kmajor_products == 1 and sub.input_copy == 1
+    assert _plan(out=0x100000000, row_idx=R, k=256).input_copy == 1      # in place too
+    assert _plan(row_idx=R, k=256, restarts=(2,)).input_copy == 1
+    # ragged subset, transposed form (128-edge tiles), another I/O type,
+    # standard NS: the normalised copy
+    for p in (_plan(row_idx=R, k=200), _plan(row_idx=R, k=256, opts=0x10),
+              _plan(row_idx=R, k=256, io=0), _plan(standard=1, row_idx=R, k=256)):
+        assert p.direct_input == 0 and p.input_copy == 0
+    # the copy lives in a region the quoted workspace already holds
+    assert sub.workspace_bytes <= gns.lib().gns_gram_workspace_bytes(1, 3, 256, 1536)
 
 
 def test_plan_autotune_and_errors():

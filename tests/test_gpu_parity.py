@@ -572,6 +572,45 @@ def test_direct_input_path(algo, restarts, io, tile):
         assert max(errs) <= TOL_HALF
 
 
+@pytest.mark.parametrize("restarts", [(2,), ()])
+@pytest.mark.parametrize("tile", [256, "mixed"])
+def test_row_subset_on_direct_path(restarts, tile):
+    """A row subset that fills whole tiles in the compute type: the input pass
+    gathers the selected rows, unscaled, into the workspace and the products
+    read that copy with the normalisation in their epilogues.  Bit-identical
+    to the same call on the gathered rows as a dense batch, out of place and
+    in place, with every other row untouched; against the oracle (Dion3 §6,
+    Algorithm 4: only the selected rows are orthogonalised and written)."""
+    gns = need_gpu()
+    B, n, m, k = 3, 768, 1536, 512
+    X, X64 = _inputs(B, n, m, "bf16", seed=37)
+    rows = np.stack([synth.row_subset(n, k, seed=37, index=b) for b in range(B)])
+    say(f"row subset direct restarts={restarts} tile={tile}")
+    plan = gns.call_plan(False, 1 << 32, 2 << 32, B, n, m, torch.bfloat16, torch.bfloat16, NS5, restarts,
+                         row_idx_ptr=3 << 32, k=k, opts=0x20 if tile == 256 else 0x80)
+    assert plan.direct_input == 1 and plan.input_copy == 1
+    ri = torch.from_numpy(rows).cuda()
+    Xd = X.cuda()
+    init = synth.batch(B, n, m, seed=38, dtype=torch.bfloat16).cuda()
+    out = gns.gram_ns_batched(Xd, NS5, restarts=restarts, row_idx=ri, out=init.clone(), tile=tile)
+    dense_in = torch.stack([Xd[b, ri[b]] for b in range(B)]).contiguous()
+    dense = gns.gram_ns_batched(dense_in, NS5, restarts=restarts, tile=tile)
+    inplace = Xd.clone()
+    gns.gram_ns_batched(inplace, NS5, restarts=restarts, row_idx=ri, out=inplace, tile=tile)
+    torch.cuda.synchronize()
+    mask = torch.ones(B, n, dtype=torch.bool)
+    for b in range(B):
+        mask[b, rows[b]] = False
+        assert torch.equal(out[b, ri[b]], dense[b]), b
+        assert torch.equal(inplace[b, ri[b]], dense[b]), b
+    assert torch.equal(out.cpu()[mask], init.cpu()[mask])
+    assert torch.equal(inplace.cpu()[mask], X[mask])
+    ref = np.stack([oracle.gram_ns(X64[b][rows[b]], NS5, restarts=restarts) for b in range(B)])
+    errs = per_matrix_rel(synth.as_f64(dense), ref)
+    say("  rel errs", errs)
+    assert max(errs) <= TOL_HALF
+
+
 @pytest.mark.parametrize("case", ["bf16", "f32", "rows", "standard"])
 def test_gram_matrix_k_split(case):
     """Few 256-edge Gram tiles and a long contraction (8 x 1024x6144: 80 upper
