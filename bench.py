@@ -68,7 +68,8 @@ def short_kernel(name):
         mode = ['sym', 'gen', 'final'][int(m.group(3))]
         mode += {"1": "_kpart", "2": "_ksum"}.get(m.group(6) or "0", "")
         return f"{kind}<{dt},{m.group(2)},{mode}>"
-    for k in ("norm_partial", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish", "row_l1",
+    for k in ("norm_partial", "row_partials", "scale_transpose", "scale_rows_f32", "transpose_sumsq",
+              "norm_finish", "row_l1",
               "select_topk", "check_rows", "momentum_l1", "row_sumsq", "normuon_factors",
               "dion3_update"):
         if k in name:
@@ -118,7 +119,8 @@ def _pmc_per_dispatch(dirname, counter):
 
 # kernels after which the next symmetric product of a call is a Gram matrix
 # (the input pass, or a restart's Q X)
-_BEFORE_GRAM = ("transpose_sumsq", "norm_finish", "norm_partial", "scale_transpose", "scale_rows_f32")
+_BEFORE_GRAM = ("transpose_sumsq", "norm_finish", "norm_partial", "row_partials", "scale_transpose",
+                "scale_rows_f32")
 
 
 def classify(dispatches):
@@ -268,7 +270,8 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib, workload):
                                         "source_sha256_16": kernel_source_hash()}))
 
 
-HBM_KERNELS = ("norm_partial", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish", "momentum_l1",
+HBM_KERNELS = ("norm_partial", "row_partials", "scale_transpose", "scale_rows_f32", "transpose_sumsq", "norm_finish",
+               "momentum_l1",
                "row_sumsq", "normuon_factors", "dion3_update", "select_topk")
 
 

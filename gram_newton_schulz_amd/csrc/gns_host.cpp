@@ -269,6 +269,10 @@ struct Ctx {
   // The rectangular products of Gram NS read X row-major (K-major B operand,
   // LDS transpose reads), so no transposed copy of X is written.
   bool nn = false;
+  // Per-row sums of squares of this sub-batch's X ([batch][n], fp64), known
+  // before the call (the Dion3 update's momentum pass forms them): a row
+  // subset's norm then adds those of its rows instead of reading the rows.
+  const double *row_sumsq = nullptr;
   // Fan-out stagger: recorded on `s` once the input is normalised; the next
   // part's stream waits for it (see run_batches).  Null when unused.
   hipEvent_t stagger = nullptr;
@@ -598,7 +602,13 @@ gns_status normalize(const Ctx &c, const void *X, int io, int64_t n_total, const
     ls.done();
     return e == hipSuccess ? GNS_OK : GNS_E_HIP;
   }
-  {
+  if (c.row_sumsq && row_idx) {
+    LaunchScope ls(c.s, "row_partials", "row_partials", rows * c.batch, 16.0 * rows * c.batch);
+    hipError_t e = gns::launch_row_partials(c.row_sumsq, row_idx, c.batch, n_total, c.pl->rows, c.pl->parts,
+                                            partials, c.s);
+    ls.done();
+    if (e != hipSuccess) return GNS_E_HIP;
+  } else {
     LaunchScope ls(c.s, "norm_partial", "norm_partial", 2.0 * rows * m * c.batch,
                    c.batch * rows * m * gns::dtype_size(io));
     hipError_t e = gns::launch_norm_partial(io, X, c.batch, n_total, c.pl->m, c.pl->rows, row_idx,
@@ -947,7 +957,7 @@ gns_status run_batches(const Plan &pl, int cdt, int64_t batch, void *workspace,
 // Dion3 update: workspace layout after the orthogonalisation's own workspace
 // --------------------------------------------------------------------------
 struct Dion3Layout {
-  size_t off_keys = 0, off_o = 0, off_rowsq = 0, off_factor = 0, bytes = 0;
+  size_t off_keys = 0, off_msq = 0, off_o = 0, off_rowsq = 0, off_factor = 0, bytes = 0;
 };
 
 // The orthogonalisation's region is sized for 256-padded buffers (any tile
@@ -957,6 +967,8 @@ bool dion3_layout(int cdt, int64_t batch, int64_t n, int64_t m, int64_t k, Dion3
   if (batch <= 0 || n < 1 || k < 1 || k > n || !make_plan(cdt, batch, k, m, 5, 256, &pl)) return false;
   size_t off = align_up(pl.bytes, kAlign);
   d->off_keys = off;                                  // fp64 row keys [batch][n]
+  off = align_up(off + sizeof(double) * batch * n, kAlign);
+  d->off_msq = off;                                   // fp64 row sums of M^2 [batch][n]
   off = align_up(off + sizeof(double) * batch * n, kAlign);
   d->off_o = off;                                     // fp32 update O [batch][k][m]
   off = align_up(off + sizeof(float) * batch * k * m, kAlign);
@@ -1375,15 +1387,18 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
   }
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   double *keys = reinterpret_cast<double *>(ws + d.off_keys);
+  double *msq = reinterpret_cast<double *>(ws + d.off_msq);
   float *O = reinterpret_cast<float *>(ws + d.off_o);
   double *rowsq = reinterpret_cast<double *>(ws + d.off_rowsq);
   double *factor = reinterpret_cast<double *>(ws + d.off_factor);
   const double bn = static_cast<double>(batch) * n, bk = static_cast<double>(batch) * k;
   const double gsz = gns::dtype_size(grad_dtype);
-  // Algorithm 4, first two steps: M <- M + G, then the k rows of largest l1 norm
+  // Algorithm 4, first two steps: M <- M + G, then the k rows of largest l1
+  // norm (the same pass keeps every row's sum of squares for the norm of the
+  // selected rows)
   {
-    LaunchScope ls(s, "momentum_l1", "momentum_l1", 2.0 * bn * m, bn * m * (8.0 + gsz));
-    hipError_t e = gns::launch_momentum_l1(grad_dtype, M, G, batch, n, m, keys, s);
+    LaunchScope ls(s, "momentum_l1", "momentum_l1", 4.0 * bn * m, bn * m * (8.0 + gsz));
+    hipError_t e = gns::launch_momentum_l1(grad_dtype, M, G, batch, n, m, keys, msq, s);
     ls.done();
     if (e != hipSuccess) return GNS_E_HIP;
   }
@@ -1402,8 +1417,9 @@ gns_status gns_dion3_step(float *W, const void *G, float *M, float *v, int64_t b
     const float *Xs = M + c.b0 * in_mat;
     float *Os = O + c.b0 * o_mat;
     const int64_t *ri = row_idx + c.b0 * k;
-    if (square) return enqueue_standard(c, Xs, Os, GNS_F32, n, coeffs, T, ri, nullptr, k);
     Ctx cg = c;
+    cg.row_sumsq = msq + c.b0 * n;
+    if (square) return enqueue_standard(cg, Xs, Os, GNS_F32, n, coeffs, T, ri, nullptr, k);
     cg.nn = kmajor_products(pl, cdt);
     return enqueue_gram(cg, Xs, Os, GNS_F32, n, coeffs, T, restart_at, ri, nullptr, k, naive);
   });

@@ -124,9 +124,15 @@ hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, i
                              int32_t *result, hipStream_t s);
 
 // Dion3 update (Algorithm 4 around the orthogonalisation).
-// M <- M + G (fp32) and keys[b][i] = sum_j |M_b[i][j]| (fp64).
+// M <- M + G (fp32) and keys[b][i] = sum_j |M_b[i][j]| (fp64); with sumsq
+// also sumsq[b][i] = sum_j M_b[i][j]^2 (fp64).
 hipError_t launch_momentum_l1(int grad_dtype, float *M, const void *G, int64_t batch, int64_t n,
-                              int64_t m, double *keys, hipStream_t s);
+                              int64_t m, double *keys, double *sumsq, hipStream_t s);
+// partials[b][p] (p < parts) = sum over the rows r of part p (ceil(k / parts)
+// consecutive entries of row_idx[b], in order) of rowsq[b][row_idx[b][r]]:
+// the norm partials of a row subset whose per-row sums of squares are known.
+hipError_t launch_row_partials(const double *rowsq, const int64_t *row_idx, int64_t batch, int64_t n,
+                               int64_t k, int parts, double *partials, hipStream_t s);
 // out[b][0..k) = indices of the k largest keys, ascending (ties: smaller index).
 hipError_t launch_select_topk(const double *keys, int64_t batch, int64_t n, int64_t k, int64_t *out,
                               hipStream_t s);

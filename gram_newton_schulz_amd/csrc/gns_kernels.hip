@@ -1846,11 +1846,12 @@ select_topk(const double *keys, int64_t n, int64_t k, int64_t *out) {
 // ---------------------------------------------------------------------------
 // The momentum takes the gradient, M <- M + G (one fp32 addition per
 // element, stored), and every row of the sum gets its l1 key sum_j |M_ij|
-// (fp64; lane-strided 16-byte pieces, then the wave tree: a fixed order for
-// a given shape).  One wave per row.
+// and, when sumsq is given, its sum of squares sum_j M_ij^2 (both fp64;
+// lane-strided 16-byte pieces, then the wave tree: a fixed order for a given
+// shape).  One wave per row.
 template <class TG>
 __global__ void __launch_bounds__(256)
-momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *keys) {
+momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *keys, double *sumsq) {
   using SG = typename TG::S;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -1859,7 +1860,7 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
   const int64_t base = (static_cast<int64_t>(b) * n + row) * m;
   float *mr = M + base;
   const SG *gr = static_cast<const SG *>(G) + base;
-  double acc = 0.0;
+  double acc = 0.0, sq = 0.0;
   if (vec) {
     // four elements per piece: 16 bytes of M, 16 (fp32) or 8 (16-bit) of G
     auto load = [&](int64_t v, float4 &mv, float *g) {
@@ -1885,6 +1886,10 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
       acc += fabs(static_cast<double>(mv.y));
       acc += fabs(static_cast<double>(mv.z));
       acc += fabs(static_cast<double>(mv.w));
+      sq += static_cast<double>(mv.x) * mv.x;
+      sq += static_cast<double>(mv.y) * mv.y;
+      sq += static_cast<double>(mv.z) * mv.z;
+      sq += static_cast<double>(mv.w) * mv.w;
     };
     // kUnroll pieces per lane in flight: all their loads are issued before
     // the first store (the lane's pieces are summed in the same order)
@@ -1909,10 +1914,41 @@ momentum_l1(float *M, const void *G, int64_t n, int64_t m, bool vec, double *key
       const float s = mr[c] + TG::ld(gr[c]);
       mr[c] = s;
       acc += fabs(static_cast<double>(s));
+      sq += static_cast<double>(s) * s;
     }
   }
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
-  if (lane == 0) keys[static_cast<int64_t>(b) * n + row] = acc;
+  for (int off = 32; off > 0; off >>= 1) {
+    acc += __shfl_down(acc, off, 64);
+    sq += __shfl_down(sq, off, 64);
+  }
+  if (lane == 0) {
+    keys[static_cast<int64_t>(b) * n + row] = acc;
+    if (sumsq) sumsq[static_cast<int64_t>(b) * n + row] = sq;
+  }
+}
+
+// Norm partials of a row subset from known per-row sums of squares:
+// partial p of matrix b adds rowsq[b][row_idx[b][r]] over the rows r in
+// [p rpp, min((p + 1) rpp, k)), rpp = ceil(k / parts), in order (an index
+// outside [0, n) adds nothing).  The scaled copy then sums the partials
+// exactly as it sums those of a pass over the rows themselves.
+__global__ void __launch_bounds__(256)
+row_partials(const double *rowsq, const int64_t *row_idx, int64_t n, int64_t k, int parts,
+             double *partials) {
+  const int b = blockIdx.y;
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= parts) return;
+  const int64_t rpp = (k + parts - 1) / parts;
+  const int64_t r0 = p * rpp;
+  const int64_t r1 = r0 + rpp < k ? r0 + rpp : k;
+  const int64_t *ri = row_idx + static_cast<int64_t>(b) * k;
+  const double *rs = rowsq + static_cast<int64_t>(b) * n;
+  double acc = 0.0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int64_t row = ri[r];
+    if (row >= 0 && row < n) acc += rs[row];
+  }
+  partials[static_cast<int64_t>(b) * parts + p] = acc;
 }
 
 // Sum of squares of every row of the k x m update O (fp32 values, fp64
@@ -2260,13 +2296,21 @@ hipError_t launch_check_rows(const int64_t *row_idx, int64_t batch, int64_t k, i
 }
 
 hipError_t launch_momentum_l1(int grad_dtype, float *M, const void *G, int64_t batch, int64_t n,
-                              int64_t m, double *keys, hipStream_t s) {
+                              int64_t m, double *keys, double *sumsq, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(batch));
   const bool vec = (m % 4) == 0 && (reinterpret_cast<uintptr_t>(M) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(G) & (grad_dtype == DT_F32 ? 15 : 7)) == 0;
-  if (grad_dtype == DT_BF16) momentum_l1<EBF16><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys);
-  else if (grad_dtype == DT_F16) momentum_l1<EF16><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys);
-  else momentum_l1<EF32><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys);
+  if (grad_dtype == DT_BF16) momentum_l1<EBF16><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys, sumsq);
+  else if (grad_dtype == DT_F16) momentum_l1<EF16><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys, sumsq);
+  else momentum_l1<EF32><<<grid, 256, 0, s>>>(M, G, n, m, vec, keys, sumsq);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_partials(const double *rowsq, const int64_t *row_idx, int64_t batch, int64_t n,
+                               int64_t k, int parts, double *partials, hipStream_t s) {
+  if (batch == 0 || parts < 1) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((parts + 255) / 256), static_cast<unsigned>(batch));
+  row_partials<<<grid, 256, 0, s>>>(rowsq, row_idx, n, k, parts, partials);
   return hipGetLastError();
 }
 
