@@ -1632,7 +1632,7 @@ check_finite(const void *A, int64_t rows, int64_t cols, const int64_t *row_idx, 
 // fp64 combination).  The n x m matrix is either X_b itself (n_src = n) or,
 // with row_idx, rows row_idx[b][0..n) of the n_src x m matrix X_b (a row
 // outside X_b reads as zeros).
-template <class T>
+template <class T, bool GATHER>
 __global__ void __launch_bounds__(256)
 transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restrict__ XT,
                 void *__restrict__ Xcopy, double *partials, const int64_t *__restrict__ row_idx,
@@ -1646,17 +1646,23 @@ transpose_sumsq(const void *__restrict__ X, int64_t n, int64_t m, void *__restri
   __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
   __shared__ double wsum[4];
   const uint16_t *Xb = static_cast<const uint16_t *>(X) + static_cast<int64_t>(b) * n_src * m;
-  const int64_t *rib = row_idx ? row_idx + static_cast<int64_t>(b) * n : nullptr;
+  const int64_t *rib = GATHER ? row_idx + static_cast<int64_t>(b) * n : nullptr;
   uint16_t *XTb = static_cast<uint16_t *>(XT) + static_cast<int64_t>(b) * m * n;
   u32x4 in[NP];
 #pragma unroll
   for (int h = 0; h < NP; ++h) {
     const int v = threadIdx.x + 256 * h;
     const int64_t r = r0 + v / PR;
-    const int64_t src = rib ? rib[r] : r;
-    // a row index outside X_b reads as zeros (no access)
-    in[h] = (src >= 0 && src < n_src) ? *reinterpret_cast<const u32x4 *>(Xb + src * m + c0 + (v % PR) * 8)
-                                      : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (!GATHER) {
+      in[h] = *reinterpret_cast<const u32x4 *>(Xb + r * m + c0 + (v % PR) * 8);
+    } else {
+      // a row index outside X_b reads as zeros: row 0 is loaded instead and
+      // the value dropped, which keeps every load unconditional
+      const int64_t src = rib[r];
+      const bool ok = src >= 0 && src < n_src;
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(Xb + (ok ? src : 0) * m + c0 + (v % PR) * 8);
+      in[h] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   // optional row-major copy of the n x m matrix (read by later products in
   // place of the caller's X: a row subset, or X when it is also the output)
@@ -2248,9 +2254,13 @@ hipError_t launch_transpose_sumsq(int dt, const void *X, int64_t batch, int64_t 
                                   void *XT, void *Xcopy, double *partials, const int64_t *row_idx,
                                   int64_t n_src, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(m / 128), static_cast<unsigned>(n / 128), static_cast<unsigned>(batch));
-  if (!row_idx) n_src = n;
-  if (dt == DT_BF16) transpose_sumsq<EBF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, row_idx, n_src);
-  else transpose_sumsq<EF16><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, row_idx, n_src);
+  if (!row_idx) {
+    if (dt == DT_BF16) transpose_sumsq<EBF16, false><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, nullptr, n);
+    else transpose_sumsq<EF16, false><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, nullptr, n);
+  } else {
+    if (dt == DT_BF16) transpose_sumsq<EBF16, true><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, row_idx, n_src);
+    else transpose_sumsq<EF16, true><<<grid, 256, 0, s>>>(X, n, m, XT, Xcopy, partials, row_idx, n_src);
+  }
   return hipGetLastError();
 }
 
