@@ -1813,15 +1813,20 @@ select_topk(const double *keys, int64_t n, int64_t k, int64_t *out) {
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int64_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= need) break;
-        above += hist[d];
+    // the digit d of the k-th largest key: the keys in buckets above d
+    // number fewer than `need`, and with bucket d at least `need` (an
+    // exclusive scan over the buckets from 255 down gives every thread its
+    // bucket's count above; the one thread whose bucket qualifies writes;
+    // bucket 0 takes the rest)
+    {
+      const int d = 255 - static_cast<int>(threadIdx.x);
+      const int h = threadIdx.x < 256 ? static_cast<int>(hist[d]) : 0;
+      int total = 0;
+      const int64_t above = block_scan_excl(h, &total, wsum);
+      if (threadIdx.x < 256 && (d == 0 || above + h >= need) && above < need) {
+        s_prefix = prefix | (static_cast<uint64_t>(d) << shift);
+        s_need = need - above;
       }
-      s_prefix = prefix | (static_cast<uint64_t>(d) << shift);
-      s_need = need - above;
     }
     __syncthreads();
     prefix = s_prefix;
