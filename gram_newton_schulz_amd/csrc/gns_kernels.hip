@@ -981,13 +981,13 @@ gemm_nt(GemmParams p) {
   const int64_t col_base = static_cast<int64_t>(tj) * TILE + wc;
   const float alpha = p.alpha_vec ? p.alpha * p.alpha_vec[mat] : p.alpha;
 
-  // Outputs of 256-edge tiles in 16-bit types go through LDS: the
-  // accumulator layout gives each lane scattered 2-byte elements (direct
-  // layout) or 8-byte pieces of 32 different rows (transposed layout), so
-  // the tile is first written into LDS (rows of 528 bytes, either layout) and
-  // the whole workgroup then stores it as full 512-byte rows, 16 bytes per
-  // lane.  Both layouts of every output are stored this way.
-  constexpr bool kStage = (TILE == 256 && PL == 1 && ESZ == 2);
+  // Outputs of unsplit 16-bit tiles go through LDS: the accumulator layout
+  // gives each lane scattered 2-byte elements (direct layout) or 8-byte
+  // pieces of 32 different rows (transposed layout), so the tile is first
+  // written into LDS (rows of TILE + 8 elements, either layout) and the whole
+  // workgroup then stores it as full rows, 16 bytes per lane.  Both layouts
+  // of every output are stored this way.
+  constexpr bool kStage = ((TILE == 256 || TILE == 128) && PL == 1 && ESZ == 2);
   constexpr int TP = TILE + 8;                         // staged row pitch (elements)
   static_assert(!kStage || TILE * TP * 2 <= NST * STB, "staging tile fits the ring");
   S *const Ts = reinterpret_cast<S *>(lds);
