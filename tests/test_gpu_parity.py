@@ -367,6 +367,35 @@ def test_out_of_range_rows_touch_nothing():
     assert torch.isfinite(out).all()
 
 
+def test_out_of_range_rows_on_direct_path():
+    """The direct path's gather (bf16 rows that fill whole 256-edge tiles)
+    also reads a bad index as a zero row and writes nothing for it: the other
+    selected rows match the oracle on the gathered matrix with that row zero,
+    and every unselected row keeps its value."""
+    gns = need_gpu()
+    B, n, m, k = 2, 512, 512, 256
+    X, X64 = _inputs(B, n, m, "bf16", seed=23)
+    rows = np.stack([np.sort(synth.row_subset(n, k, seed=23, index=b)) for b in range(B)])
+    rows[0, 5] = n + 90                        # outside X_0
+    rows[1, 0] = -1                            # outside X_1
+    plan = gns.call_plan(False, 1 << 32, 2 << 32, B, n, m, torch.bfloat16, torch.bfloat16, NS5, (2,),
+                         row_idx_ptr=3 << 32, k=k, opts=0x20)
+    assert plan.direct_input == 1 and plan.input_copy == 1
+    init = synth.batch(B, n, m, seed=24, dtype=torch.bfloat16)
+    say("direct path, out-of-range rows")
+    out = gns.gram_ns_batched(X.cuda(), NS5, restarts=(2,), row_idx=torch.from_numpy(rows).cuda(),
+                              out=init.clone().cuda(), tile=256).cpu()
+    assert torch.isfinite(out.float()).all()
+    for b in range(B):
+        valid = (rows[b] >= 0) & (rows[b] < n)
+        G = np.zeros((k, m))
+        G[valid] = X64[b][rows[b][valid]]
+        ref = oracle.gram_ns(G, NS5, restarts=(2,))
+        assert rel_err(synth.as_f64(out[b])[rows[b][valid]], ref[valid]) <= TOL_HALF
+        keep = np.setdiff1d(np.arange(n), rows[b][valid])
+        assert torch.equal(out[b][keep], init[b][keep])
+
+
 @pytest.mark.parametrize("algo", ["gram", "standard"])
 def test_batch_split_matches_one_stream(algo):
     """Splitting a batch over the library's two streams gives bit-identical
