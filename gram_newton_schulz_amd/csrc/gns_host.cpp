@@ -320,10 +320,11 @@ void set_scale(GemmParams *p, float alpha, float beta) {
 // Runs of tiles dealt to one XCD (the kernel's xcd_chunk): 1/xpm of a matrix
 // per run so that xpm XCDs share each matrix, or with xpm = 1 (and whenever
 // the sizes do not divide) one contiguous run per XCD, which holds whole
-// matrices when the batch is a multiple of 8.  Products use xpm = 4 (a quarter matrix per run): measured on
-// 8 x 4096x16384 bf16 against 1, 2 and 8 per product kind, it keeps the
-// matrices in flight within the shared last-level cache while each XCD's L2
-// still sees a compact block of tiles.  The n x n products of matrices of at
+// matrices when the batch is a multiple of 8.  Products use xpm = 4 (a
+// quarter matrix per run): measured on 8 x 4096x16384 bf16 against 1, 2 and 8
+// per product kind, it keeps the matrices in flight within the shared
+// last-level cache while each XCD's L2 still sees a compact block of tiles.
+// The n x n products of matrices of at
 // most 2 MiB (half an XCD's L2) use xpm = 1 instead, so that one XCD's L2
 // holds every operand of its matrix (16 x 1024x4096 bf16: 1.08 -> 1.06 ms
 // a call; 64 x 2048x7168 unchanged).
